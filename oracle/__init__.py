@@ -1,0 +1,191 @@
+"""Oracle for the FPS tokenizer -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, single-threaded C implementation (``fpstok_oracle.c``) of what
+the tokenizer computes, wrapped with ctypes for numpy arrays.  It decides the
+correct answer in the parity tests.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it; the GPU library and
+its Python binding never do, and the two share no code.
+
+Parity pins: every function here is pinned in ``tests/test_oracle_pins.py``
+against brute force on tiny events, hand-derived closed forms and invariants
+(see that module's docstring).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fpstok_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_fpstok.so")
+
+# -ffp-contract=off: no fused multiply-add, every float32 operation rounded on
+# its own; no -ffast-math; x86-64 computes float in SSE (no excess precision).
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc; returns the path of the shared library."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        i32 = ctypes.c_int32
+        lib.oracle_sample.argtypes = [P, P, i64, i32, P, P, P, P, P]
+        lib.oracle_assign.argtypes = [P, P, i64, i32, P, P, P]
+        lib.oracle_knn.argtypes = [P, P, i64, i32, i32, P, P, P]
+        lib.oracle_lloyd.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P]
+        lib.oracle_pool.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_tokenize.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, i32, i32, P,
+                                        P, P, P, P, P, P, P]
+        for f in ("oracle_sample", "oracle_assign", "oracle_knn", "oracle_lloyd",
+                  "oracle_pool", "oracle_tokenize"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a, cols):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.ndim != 2 or a.shape[1] != cols:
+        raise ValueError("expected [N,%d] float32" % cols)
+    return a
+
+
+def _offs(offsets):
+    o = np.ascontiguousarray(offsets, dtype=np.int64)
+    if o.ndim != 1 or o.size < 1 or o[0] != 0 or np.any(np.diff(o) < 0):
+        raise ValueError("offsets must be non-decreasing, start at 0")
+    return o
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError("oracle %s failed with code %d" % (what, rc))
+
+
+def sample(coords, offsets, P, start_idx=None, with_assign=True):
+    """FPS / pass-through for every event.  Returns (centroid_idx [B,P] i32,
+    centroids [B,P,4] f32, token_count [B] i32, assign [N] i32 or None)."""
+    x = _f32(coords, 4)
+    o = _offs(offsets)
+    B = o.size - 1
+    if o[-1] != x.shape[0]:
+        raise ValueError("offsets[-1] != N")
+    sel = np.empty((B, P), np.int32)
+    cen = np.empty((B, P, 4), np.float32)
+    tc = np.empty(B, np.int32)
+    asg = np.empty(x.shape[0], np.int32) if with_assign else None
+    st = None if start_idx is None else np.ascontiguousarray(start_idx, dtype=np.int32)
+    _check(_load().oracle_sample(_ptr(x), _ptr(o), B, P, _ptr(st), _ptr(sel), _ptr(cen),
+                                 _ptr(tc), _ptr(asg)), "sample")
+    return sel, cen, tc, asg
+
+
+def assign(coords, offsets, P, centroids, token_count):
+    """Nearest-centroid slot of every pulse ([N] int32)."""
+    x = _f32(coords, 4)
+    o = _offs(offsets)
+    B = o.size - 1
+    cen = np.ascontiguousarray(centroids, dtype=np.float32).reshape(B, P, 4)
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    out = np.empty(x.shape[0], np.int32)
+    _check(_load().oracle_assign(_ptr(x), _ptr(o), B, P, _ptr(cen), _ptr(tc), _ptr(out)),
+           "assign")
+    return out
+
+
+def knn(coords, offsets, P, k, centroids, token_count):
+    """k nearest pulses of each token ([B,P,k] int32, -1 padded)."""
+    x = _f32(coords, 4)
+    o = _offs(offsets)
+    B = o.size - 1
+    cen = np.ascontiguousarray(centroids, dtype=np.float32).reshape(B, P, 4)
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    out = np.empty((B, P, k), np.int32)
+    _check(_load().oracle_knn(_ptr(x), _ptr(o), B, P, k, _ptr(cen), _ptr(tc), _ptr(out)),
+           "knn")
+    return out
+
+
+def lloyd(coords, features, offsets, P, L, centroids, token_count, assign_in, charge_col):
+    """L Lloyd rounds; returns new (centroids, assign) (inputs are not modified)."""
+    x = _f32(coords, 4)
+    o = _offs(offsets)
+    B = o.size - 1
+    f = np.ascontiguousarray(features, dtype=np.float32)
+    C = f.shape[1] if f.ndim == 2 else 0
+    cen = np.array(centroids, dtype=np.float32, copy=True).reshape(B, P, 4)
+    asg = np.array(assign_in, dtype=np.int32, copy=True)
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    _check(_load().oracle_lloyd(_ptr(x), _ptr(f), _ptr(o), B, C, charge_col, P, L, _ptr(cen),
+                                _ptr(tc), _ptr(asg)), "lloyd")
+    return cen, asg
+
+
+def pool(features, offsets, P, token_count, mode=0, assign=None, knn_idx=None, k=1,
+         weighted=True, charge_col=-1):
+    """Per-token (weighted) mean of the features; returns (pooled [B,P,C] f32,
+    cell_count [B,P] i32)."""
+    f = np.ascontiguousarray(features, dtype=np.float32)
+    o = _offs(offsets)
+    B = o.size - 1
+    C = f.shape[1]
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    a = None if assign is None else np.ascontiguousarray(assign, dtype=np.int32)
+    kn = None if knn_idx is None else np.ascontiguousarray(knn_idx, dtype=np.int32)
+    if mode == 0 and a is None:
+        raise ValueError("Voronoi pooling needs assign")
+    if mode == 1 and kn is None:
+        raise ValueError("kNN pooling needs knn_idx")
+    out = np.empty((B, P, C), np.float32)
+    cnt = np.empty((B, P), np.int32)
+    _check(_load().oracle_pool(_ptr(f), _ptr(o), B, C, charge_col, P, mode, k, int(weighted),
+                               _ptr(tc), _ptr(a), _ptr(kn), _ptr(out), _ptr(cnt)), "pool")
+    return out, cnt
+
+
+def tokenize(coords, features, offsets, P=128, mode=0, k=16, L=0, weighted=True,
+             charge_col=-1, start_idx=None):
+    """The whole tokenizer; returns a dict of numpy arrays."""
+    x = _f32(coords, 4)
+    f = np.ascontiguousarray(features, dtype=np.float32)
+    o = _offs(offsets)
+    B = o.size - 1
+    C = f.shape[1]
+    N = x.shape[0]
+    out = dict(
+        centroid_idx=np.empty((B, P), np.int32),
+        centroids=np.empty((B, P, 4), np.float32),
+        token_count=np.empty(B, np.int32),
+        assign=np.empty(N, np.int32),
+        knn_idx=np.empty((B, P, k), np.int32) if mode == 1 else None,
+        pooled=np.empty((B, P, C), np.float32),
+        cell_count=np.empty((B, P), np.int32),
+    )
+    st = None if start_idx is None else np.ascontiguousarray(start_idx, dtype=np.int32)
+    _check(_load().oracle_tokenize(
+        _ptr(x), _ptr(f), _ptr(o), B, C, charge_col, P, mode, k, L, int(weighted), _ptr(st),
+        _ptr(out["centroid_idx"]), _ptr(out["centroids"]), _ptr(out["token_count"]),
+        _ptr(out["assign"]), _ptr(out["knn_idx"]), _ptr(out["pooled"]),
+        _ptr(out["cell_count"])), "tokenize")
+    return out

@@ -1,0 +1,197 @@
+/*
+ * fpstok.h -- C ABI of libfpstok, the farthest-point-sampling (FPS) tokenizer
+ * of the Neptune point transformer on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, with the passages that define it:
+ *   - An event is an irregular 4D (x, y, z, t) point cloud of pulses; FPS
+ *     reduces it to at most num_patches centroids and the pulses of each
+ *     token are pooled (graphnet pull request #923 "Add Neptune
+ *     point-transformer backbone", section "Summary").
+ *   - Small events keep one token per pulse; larger ones are reduced to
+ *     centroids and pooled by Voronoi assignment or by kNN gather (same page,
+ *     "What is added": FPSTokenizer).
+ *   - The operation family is FPS, FPS fused with the nearest-centroid
+ *     assignment, FPS with a kNN gather, and the standalone nearest
+ *     assignment (same page, "What is added": farthest_point_sampling,
+ *     farthest_point_sampling_with_assign, farthest_point_sampling_with_knn,
+ *     nearest_assign).
+ *   - FPS takes an optional start index and is always computed in float32
+ *     (same page, review replies on the FPS arguments and on the removed
+ *     precision argument).
+ *   - Inputs: coords [N,4] with time in the fourth column, point features,
+ *     per-point batch membership (README of felixyu7/neptune, "Usage"); here
+ *     the batch is given as CSR offsets, events contiguous and ascending.
+ *   - Tokenization = FPS down to num_patches centroids, per-token pooling by
+ *     Voronoi assignment or kNN gather (assign_mode, k_neighbors), optional
+ *     charge-weighted Lloyd refinement (lloyd_iters) (README, "How it works"
+ *     step 1 and "Parameters").
+ *   - Without a charge column every pulse has unit charge (graphnet PR #923,
+ *     review reply on the no-charge case).
+ *
+ * Conventions fixed where the pages are silent:
+ *   - squared distance d2(a,c) = ((dx*dx + dy*dy) + dz*dz) + dt*dt, each
+ *     float32 operation rounded on its own (no fused multiply-add);
+ *   - FPS starts at each event's first pulse unless start_idx is given; the
+ *     next centroid is the not-yet-selected pulse with the largest distance
+ *     to its nearest centroid, lowest pulse index on ties;
+ *   - events with n <= P pass through: token t = pulse t, assign = identity,
+ *     kNN list of token t = [t, -1, ...];
+ *   - Voronoi ties go to the lowest token slot (FPS selection order); kNN
+ *     lists ascend in (d2, pulse index);
+ *   - Lloyd: per token, the charge-weighted mean of its cell accumulated in
+ *     float64 in ascending pulse order and rounded to float32 (a cell with
+ *     zero weight keeps its centroid), then a fresh nearest assignment;
+ *     events with n <= P are not refined;
+ *   - pooling: (charge-weighted) mean of all C feature columns over the
+ *     token's members, float64 accumulation, float32 result, 0 for a token
+ *     whose weight sum is 0;
+ *   - all indices are event-local int32 (add offsets[b] for a global row);
+ *     slots j >= T of an event are padded (-1 for indices, 0 for values).
+ *
+ * Ownership and execution:
+ *   - The caller allocates and owns every buffer, including the workspace; the
+ *     library allocates and frees no device memory.  Every pointer in a
+ *     compute call is a device pointer unless stated otherwise.
+ *   - Every compute call only enqueues work on `stream` (a hipStream_t; NULL
+ *     is the legacy default stream) and returns; it makes no host-device
+ *     synchronization.  Buffers must stay valid until the stream work ends.
+ *   - Argument errors are found on the host before anything is enqueued and
+ *     have no side effects.  Data preconditions (monotone offsets with
+ *     offsets[B] = N, finite coordinates, non-negative charges, start indices
+ *     in range, assignments in [0, T)) are not checked on the hot path;
+ *     fpstok_validate checks them (and synchronizes).
+ *   - Results are bit-identical from run to run (no floating-point atomics).
+ *   - Calls on one workspace must not overlap in time (same stream, or
+ *     ordered with events).  The library keeps no state between calls other
+ *     than a per-device property cache.
+ */
+#ifndef FPSTOK_H
+#define FPSTOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FPSTOK_ABI_VERSION 1
+#define FPSTOK_MAX_PATCHES 1024 /* largest num_patches accepted             */
+#define FPSTOK_MAX_K 64         /* largest kNN list length accepted           */
+#define FPSTOK_MAX_LLOYD 1000   /* largest lloyd_iters accepted               */
+
+typedef enum {
+    FPSTOK_OK = 0,
+    FPSTOK_EINVAL = 1,      /* invalid argument; nothing was enqueued               */
+    FPSTOK_EWORKSPACE = 2,  /* ws is NULL or ws_bytes < fpstok_workspace_size(...)  */
+    FPSTOK_EUNSUPPORTED = 3,/* valid request beyond an implementation limit         */
+    FPSTOK_EHIP = 4         /* a HIP runtime call failed; see fpstok_last_error()   */
+} fpstok_status;
+
+typedef enum { FPSTOK_VORONOI = 0, FPSTOK_KNN = 1 } fpstok_assign_mode;
+
+/* One CSR batch of events.  All pointers are device pointers. */
+typedef struct {
+    const float* coords;     /* [N,4] f32 row-major (x,y,z,t); 16-byte aligned    */
+    const float* features;   /* [N,C] f32 row-major; 4-byte aligned; may be NULL  */
+                             /* for calls that do not read features               */
+    const int64_t* offsets;  /* [B+1] int64: event b is rows offsets[b] ..        */
+                             /* offsets[b+1]-1; offsets[0]=0, offsets[B]=N         */
+    int64_t num_events;      /* B >= 0                                            */
+    int64_t num_points;      /* N >= 0, N < 2^31                                  */
+    int32_t num_features;    /* C >= 1 for calls that read features                */
+    int32_t charge_col;      /* charge column 0..C-1, or -1 for unit charge       */
+} fpstok_batch;
+
+typedef struct {
+    int32_t num_patches;     /* P: 1..FPSTOK_MAX_PATCHES                          */
+    int32_t k;               /* kNN list length 1..FPSTOK_MAX_K (kNN mode only)   */
+    int32_t lloyd_iters;     /* L: 0..FPSTOK_MAX_LLOYD                            */
+    int32_t assign_mode;     /* FPSTOK_VORONOI or FPSTOK_KNN                      */
+    int32_t pool_weighted;   /* 0: plain mean; 1: charge-weighted mean            */
+} fpstok_params;
+
+/* Bytes of device workspace every compute call of this batch shape needs
+ * (depends on B and N only).  Host-only; never fails; 0 for B = 0. */
+size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_params* params);
+
+/* FPS of every event (farthest_point_sampling / _with_assign).  For n > P:
+ * P centroids by FPS from start_idx[b] (NULL: 0); for n <= P: pass-through.
+ *   start_idx    [B] int32 event-local start pulse, or NULL (device)
+ *   centroid_idx [B,P] int32 out: selected pulse of each slot, -1 padded
+ *   centroids    [B,P,4] f32 out: coordinates of each slot, 0 padded
+ *   token_count  [B] int32 out: T = min(n, P)
+ *   assign       [N] int32 out: Voronoi slot of every pulse (the fused
+ *                nearest-centroid assignment), or NULL to skip it
+ * Errors: EINVAL (NULL coords/offsets/outputs, misaligned coords, bad P),
+ * EWORKSPACE, EUNSUPPORTED (N >= 2^31), EHIP. */
+fpstok_status fpstok_sample(const fpstok_batch* batch, const fpstok_params* params,
+                            const int32_t* start_idx, int32_t* centroid_idx, float* centroids,
+                            int32_t* token_count, int32_t* assign, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Standalone nearest-centroid assignment (nearest_assign) of every pulse of
+ * every event to the event's first token_count[b] centroids, lowest slot on
+ * ties.  This is the plain argmin for every event, pass-through ones included.
+ *   centroids   [B,P,4] f32 in;  token_count [B] int32 in (T >= 1 if n >= 1)
+ *   assign      [N] int32 out
+ * Errors: EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP. */
+fpstok_status fpstok_assign(const fpstok_batch* batch, const fpstok_params* params,
+                            const float* centroids, const int32_t* token_count, int32_t* assign,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* kNN gather (farthest_point_sampling_with_knn, assign_mode="knn"): for every
+ * event with n > P and every slot j < token_count[b], the min(k, n) pulses
+ * with the smallest (d2(pulse, centroid_j), pulse index), ascending, -1
+ * padded; pass-through events get [t, -1, ...]; slots j >= T are all -1.
+ *   centroids [B,P,4] f32 in; token_count [B] int32 in
+ *   knn_idx   [B,P,k] int32 out
+ * Errors: EINVAL (k out of range ...), EWORKSPACE, EUNSUPPORTED, EHIP. */
+fpstok_status fpstok_knn(const fpstok_batch* batch, const fpstok_params* params,
+                         const float* centroids, const int32_t* token_count, int32_t* knn_idx,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* params->lloyd_iters rounds of charge-weighted Lloyd refinement on every
+ * event with n > P (others untouched).  Reads the features' charge column
+ * (unit charge if charge_col = -1).
+ *   centroids [B,P,4] f32 in/out; token_count [B] int32 in
+ *   assign    [N] int32 in/out (Voronoi slots, e.g. from fpstok_sample)
+ * L = 0 is a no-op.  Errors: EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP. */
+fpstok_status fpstok_lloyd(const fpstok_batch* batch, const fpstok_params* params,
+                           float* centroids, const int32_t* token_count, int32_t* assign,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token pooling of the features.  Voronoi mode: the members of slot j are
+ * the pulses with assign = j; kNN mode: the entries != -1 of knn_idx[b][j].
+ * Weight = charge if params->pool_weighted and charge_col >= 0, else 1.
+ *   assign     [N] int32 in (Voronoi mode; may be NULL in kNN mode)
+ *   knn_idx    [B,P,k] int32 in (kNN mode; may be NULL in Voronoi mode)
+ *   pooled     [B,P,C] f32 out, 0 for j >= T and for zero-weight tokens
+ *   cell_count [B,P] int32 out: members per slot (may be NULL)
+ * Errors: EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP. */
+fpstok_status fpstok_pool(const fpstok_batch* batch, const fpstok_params* params,
+                          const int32_t* token_count, const int32_t* assign,
+                          const int32_t* knn_idx, float* pooled, int32_t* cell_count, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Debug check of the data preconditions of `batch` (offsets monotone with
+ * offsets[0] = 0 and offsets[B] = N, finite coords, charge >= 0 when
+ * charge_col >= 0).  Copies the inputs to the host and synchronizes `stream`:
+ * not for the hot path.  Returns FPSTOK_OK or FPSTOK_EINVAL (the reason is in
+ * fpstok_last_error()), or FPSTOK_EHIP. */
+fpstok_status fpstok_validate(const fpstok_batch* batch, void* stream);
+
+/* Static description of a status code. */
+const char* fpstok_status_string(fpstok_status status);
+
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* fpstok_last_error(void);
+
+/* FPSTOK_ABI_VERSION of the library. */
+int fpstok_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FPSTOK_H */

@@ -1,0 +1,367 @@
+// C ABI of libfpstok (declared and documented in include/fpstok.h): argument
+// validation, workspace carve-up and kernel launches.  Validation happens on
+// the host before any HIP call, so an invalid call never touches the device.
+#include "fpstok.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "fpstok_internal.h"
+
+#define FPSTOK_API extern "C" __attribute__((visibility("default")))
+
+namespace fpstok {
+
+static thread_local char g_last_error[512] = "";
+
+static fpstok_status fail(fpstok_status st, const char* fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+
+static fpstok_status fail(fpstok_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+static fpstok_status ok() {
+    g_last_error[0] = '\0';
+    return FPSTOK_OK;
+}
+
+static fpstok_status hip_fail(hipError_t e, const char* what) {
+    return fail(FPSTOK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WorkspaceLayout workspace_layout(int64_t B, int64_t N) {
+    WorkspaceLayout L{};
+    if (B <= 0) return L;
+    const int64_t nn = N > 0 ? N : 0;
+    L.max_chunks = (nn + kChunk - 1) / kChunk + B;
+    size_t at = 0;
+    L.header = at;
+    at += align256(64 * sizeof(int32_t));
+    L.chunk_ev = at;
+    at += align256((size_t)L.max_chunks * sizeof(int32_t));
+    L.chunk_beg = at;
+    at += align256((size_t)L.max_chunks * sizeof(int32_t));
+    L.mind = at;
+    at += align256((size_t)nn * sizeof(float));
+    L.near = at;
+    at += align256((size_t)nn * sizeof(int32_t));
+    L.perm = at;
+    at += align256((size_t)nn * sizeof(int32_t));
+    L.total = at;
+    return L;
+}
+
+// Checks shared by every compute call.  `need_features`: the call reads the
+// feature matrix (0: no, 1: yes).
+static fpstok_status check_common(const fpstok_batch* bt, const fpstok_params* pr,
+                                  bool need_features, bool need_weights_col) {
+    if (!bt) return fail(FPSTOK_EINVAL, "batch is NULL");
+    if (!pr) return fail(FPSTOK_EINVAL, "params is NULL");
+    if (bt->num_events < 0) return fail(FPSTOK_EINVAL, "num_events < 0");
+    if (bt->num_points < 0) return fail(FPSTOK_EINVAL, "num_points < 0");
+    if (bt->num_points >= ((int64_t)1 << 31))
+        return fail(FPSTOK_EUNSUPPORTED, "num_points >= 2^31 (indices are int32)");
+    if (bt->num_events >= ((int64_t)1 << 31))
+        return fail(FPSTOK_EUNSUPPORTED, "num_events >= 2^31");
+    if (pr->num_patches < 1 || pr->num_patches > FPSTOK_MAX_PATCHES)
+        return fail(FPSTOK_EINVAL, "num_patches must be in [1, %d]", FPSTOK_MAX_PATCHES);
+    if (pr->assign_mode != FPSTOK_VORONOI && pr->assign_mode != FPSTOK_KNN)
+        return fail(FPSTOK_EINVAL, "unknown assign_mode %d", pr->assign_mode);
+    if (pr->assign_mode == FPSTOK_KNN && (pr->k < 1 || pr->k > FPSTOK_MAX_K))
+        return fail(FPSTOK_EINVAL, "k must be in [1, %d] in kNN mode", FPSTOK_MAX_K);
+    if (pr->lloyd_iters < 0 || pr->lloyd_iters > FPSTOK_MAX_LLOYD)
+        return fail(FPSTOK_EINVAL, "lloyd_iters must be in [0, %d]", FPSTOK_MAX_LLOYD);
+    if (pr->pool_weighted != 0 && pr->pool_weighted != 1)
+        return fail(FPSTOK_EINVAL, "pool_weighted must be 0 or 1");
+    if (bt->num_events == 0) return FPSTOK_OK;
+    if (!bt->offsets) return fail(FPSTOK_EINVAL, "offsets is NULL");
+    if (bt->num_points > 0) {
+        if (!bt->coords) return fail(FPSTOK_EINVAL, "coords is NULL");
+        if (((uintptr_t)bt->coords & 15u) != 0)
+            return fail(FPSTOK_EINVAL, "coords must be 16-byte aligned");
+    }
+    if (need_features) {
+        if (bt->num_features < 1) return fail(FPSTOK_EINVAL, "num_features must be >= 1");
+        if (bt->num_points > 0 && !bt->features) return fail(FPSTOK_EINVAL, "features is NULL");
+        if (bt->features && ((uintptr_t)bt->features & 3u) != 0)
+            return fail(FPSTOK_EINVAL, "features must be 4-byte aligned");
+    }
+    if (need_features || need_weights_col) {
+        if (bt->charge_col < -1 || (bt->num_features >= 1 && bt->charge_col >= bt->num_features))
+            return fail(FPSTOK_EINVAL, "charge_col must be -1 or in [0, num_features)");
+        if (bt->charge_col >= 0 && bt->num_features < 1)
+            return fail(FPSTOK_EINVAL, "charge_col set but num_features < 1");
+        if (bt->charge_col >= 0 && bt->num_points > 0 && !bt->features)
+            return fail(FPSTOK_EINVAL, "charge_col set but features is NULL");
+    }
+    return FPSTOK_OK;
+}
+
+static fpstok_status check_ws(const fpstok_batch* bt, void* ws, size_t ws_bytes,
+                              WorkspaceLayout& L) {
+    L = workspace_layout(bt->num_events, bt->num_points);
+    if (L.total == 0) return FPSTOK_OK;
+    if (!ws) return fail(FPSTOK_EWORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+    if (ws_bytes < L.total)
+        return fail(FPSTOK_EWORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, L.total);
+    if (((uintptr_t)ws & 255u) != 0)
+        return fail(FPSTOK_EINVAL, "workspace must be 256-byte aligned");
+    return FPSTOK_OK;
+}
+
+template <class T>
+static T* at(void* ws, size_t off) {
+    return (T*)((char*)ws + off);
+}
+
+}  // namespace fpstok
+
+using namespace fpstok;
+
+FPSTOK_API size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_params* params) {
+    (void)params;
+    if (!batch) return 0;
+    return workspace_layout(batch->num_events, batch->num_points).total;
+}
+
+FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_params* pr,
+                                       const int32_t* start_idx, int32_t* centroid_idx,
+                                       float* centroids, int32_t* token_count, int32_t* assign,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, false, false);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    if (!centroid_idx || !centroids || !token_count)
+        return fail(FPSTOK_EINVAL, "centroid_idx, centroids and token_count are required");
+    if (((uintptr_t)centroids & 15u) != 0)
+        return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    SampleArgs a{};
+    a.coords = (const float4*)bt->coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.start_idx = start_idx;
+    a.centroid_idx = centroid_idx;
+    a.centroids = (float4*)centroids;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.ws_mind = at<float>(ws, L.mind);
+    a.ws_near = at<int32_t>(ws, L.near);
+    hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_assign(const fpstok_batch* bt, const fpstok_params* pr,
+                                       const float* centroids, const int32_t* token_count,
+                                       int32_t* assign, void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, false, false);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    if (!centroids || !token_count || !assign)
+        return fail(FPSTOK_EINVAL, "centroids, token_count and assign are required");
+    if (((uintptr_t)centroids & 15u) != 0)
+        return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
+    if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+    AssignArgs a{};
+    a.coords = (const float4*)bt->coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.centroids = (const float4*)centroids;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.header = at<int32_t>(ws, L.header);
+    a.chunk_ev = at<int32_t>(ws, L.chunk_ev);
+    a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
+    a.skip_small = 0;
+    e = launch_assign(a, L.max_chunks, s);
+    if (e != hipSuccess) return hip_fail(e, "assign kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_knn(const fpstok_batch* bt, const fpstok_params* pr,
+                                    const float* centroids, const int32_t* token_count,
+                                    int32_t* knn_idx, void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, false, false);
+    if (st != FPSTOK_OK) return st;
+    if (pr->k < 1 || pr->k > FPSTOK_MAX_K)
+        return fail(FPSTOK_EINVAL, "k must be in [1, %d]", FPSTOK_MAX_K);
+    if (bt->num_events == 0) return ok();
+    if (!centroids || !token_count || !knn_idx)
+        return fail(FPSTOK_EINVAL, "centroids, token_count and knn_idx are required");
+    if (((uintptr_t)centroids & 15u) != 0)
+        return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    KnnArgs a{};
+    a.coords = (const float4*)bt->coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.k = pr->k;
+    a.centroids = (const float4*)centroids;
+    a.token_count = token_count;
+    a.knn_idx = knn_idx;
+    hipError_t e = launch_knn(a, bt->num_events, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "knn kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_lloyd(const fpstok_batch* bt, const fpstok_params* pr,
+                                      float* centroids, const int32_t* token_count,
+                                      int32_t* assign, void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, false, true);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0 || pr->lloyd_iters == 0) return ok();
+    if (!centroids || !token_count || !assign)
+        return fail(FPSTOK_EINVAL, "centroids, token_count and assign are required");
+    if (((uintptr_t)centroids & 15u) != 0)
+        return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
+    if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+    LloydArgs u{};
+    u.coords = (const float4*)bt->coords;
+    u.features = bt->features;
+    u.offsets = bt->offsets;
+    u.N = bt->num_points;
+    u.C = bt->num_features;
+    u.charge_col = bt->charge_col;
+    u.P = pr->num_patches;
+    u.centroids = (float4*)centroids;
+    u.token_count = token_count;
+    u.assign = assign;
+    u.perm = at<int32_t>(ws, L.perm);
+    AssignArgs a{};
+    a.coords = u.coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.centroids = (const float4*)centroids;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.header = at<int32_t>(ws, L.header);
+    a.chunk_ev = at<int32_t>(ws, L.chunk_ev);
+    a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
+    a.skip_small = 1;
+    for (int it = 0; it < pr->lloyd_iters; ++it) {
+        e = launch_lloyd_update(u, bt->num_events, s);
+        if (e != hipSuccess) return hip_fail(e, "lloyd update kernel launch");
+        e = launch_assign(a, L.max_chunks, s);
+        if (e != hipSuccess) return hip_fail(e, "assign kernel launch");
+    }
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params* pr,
+                                     const int32_t* token_count, const int32_t* assign,
+                                     const int32_t* knn_idx, float* pooled, int32_t* cell_count,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, true, false);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    if (!token_count || !pooled) return fail(FPSTOK_EINVAL, "token_count and pooled are required");
+    if (pr->assign_mode == FPSTOK_VORONOI && !assign && bt->num_points > 0)
+        return fail(FPSTOK_EINVAL, "assign is required in Voronoi mode");
+    if (pr->assign_mode == FPSTOK_KNN && !knn_idx)
+        return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    PoolArgs a{};
+    a.features = bt->features;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.C = bt->num_features;
+    a.weight_col = pr->pool_weighted ? bt->charge_col : -1;
+    a.P = pr->num_patches;
+    a.k = pr->k;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.knn_idx = knn_idx;
+    a.pooled = pooled;
+    a.cell_count = cell_count;
+    a.perm = at<int32_t>(ws, L.perm);
+    hipError_t e = pr->assign_mode == FPSTOK_VORONOI
+                       ? launch_pool_voronoi(a, bt->num_events, (hipStream_t)stream)
+                       : launch_pool_knn(a, bt->num_events, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_validate(const fpstok_batch* bt, void* stream) {
+    if (!bt) return fail(FPSTOK_EINVAL, "batch is NULL");
+    const int64_t B = bt->num_events, N = bt->num_points;
+    if (B < 0 || N < 0) return fail(FPSTOK_EINVAL, "negative num_events or num_points");
+    if (B == 0) return ok();
+    if (!bt->offsets) return fail(FPSTOK_EINVAL, "offsets is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    std::vector<int64_t> off((size_t)B + 1);
+    e = hipMemcpy(off.data(), bt->offsets, off.size() * sizeof(int64_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy offsets");
+    if (off[0] != 0) return fail(FPSTOK_EINVAL, "offsets[0] = %lld, expected 0", (long long)off[0]);
+    for (int64_t b = 0; b < B; ++b)
+        if (off[(size_t)b + 1] < off[(size_t)b])
+            return fail(FPSTOK_EINVAL, "offsets decrease at event %lld", (long long)b);
+    if (off[(size_t)B] != N)
+        return fail(FPSTOK_EINVAL, "offsets[B] = %lld, expected N = %lld",
+                    (long long)off[(size_t)B], (long long)N);
+    if (N > 0) {
+        if (!bt->coords) return fail(FPSTOK_EINVAL, "coords is NULL");
+        std::vector<float> x((size_t)N * 4);
+        e = hipMemcpy(x.data(), bt->coords, x.size() * sizeof(float), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpy coords");
+        for (size_t q = 0; q < x.size(); ++q)
+            if (!std::isfinite(x[q]))
+                return fail(FPSTOK_EINVAL, "coords[%zu][%zu] is not finite", q / 4, q % 4);
+        if (bt->charge_col >= 0 && bt->features && bt->num_features > bt->charge_col) {
+            const int64_t C = bt->num_features;
+            std::vector<float> f((size_t)(N * C));
+            e = hipMemcpy(f.data(), bt->features, f.size() * sizeof(float), hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpy features");
+            for (int64_t i = 0; i < N; ++i) {
+                const float q = f[(size_t)(i * C + bt->charge_col)];
+                if (!(q >= 0.0f) || !std::isfinite(q))
+                    return fail(FPSTOK_EINVAL, "charge of pulse %lld is %g", (long long)i, q);
+            }
+        }
+    }
+    return ok();
+}
+
+FPSTOK_API const char* fpstok_status_string(fpstok_status status) {
+    switch (status) {
+        case FPSTOK_OK: return "ok";
+        case FPSTOK_EINVAL: return "invalid argument";
+        case FPSTOK_EWORKSPACE: return "workspace too small";
+        case FPSTOK_EUNSUPPORTED: return "unsupported";
+        case FPSTOK_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+FPSTOK_API const char* fpstok_last_error(void) { return g_last_error; }
+
+FPSTOK_API int fpstok_version(void) { return FPSTOK_ABI_VERSION; }

@@ -1,0 +1,107 @@
+// Internal interface between the C ABI (fpstok_api.cpp) and the gfx950
+// kernels (fpstok_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fpstok {
+
+// Pulses per chunk of the chunked kernels (assign).  256 threads x 4 pulses.
+constexpr int kChunk = 1024;
+
+// Workspace carve-up.  Every region starts on a 256-byte boundary.
+struct WorkspaceLayout {
+    size_t header;      // int32[64]: [0] = number of chunks
+    size_t chunk_ev;    // int32[max_chunks]: event of each chunk
+    size_t chunk_beg;   // int32[max_chunks]: first event-local pulse of each chunk
+    size_t mind;        // float[N]: running min distance (large-event FPS)
+    size_t near;        // int32[N]: running nearest slot (large-event FPS, no assign out)
+    size_t perm;        // int32[N]: pulses sorted by token (Lloyd, pool)
+    size_t total;
+    int64_t max_chunks;
+};
+
+WorkspaceLayout workspace_layout(int64_t B, int64_t N);
+
+struct SampleArgs {
+    const float4* coords;
+    const int64_t* offsets;
+    int64_t N;
+    int P;
+    const int32_t* start_idx;
+    int32_t* centroid_idx;
+    float4* centroids;
+    int32_t* token_count;
+    int32_t* assign;
+    float* ws_mind;
+    int32_t* ws_near;
+};
+
+struct AssignArgs {
+    const float4* coords;
+    const int64_t* offsets;
+    int64_t N;
+    int P;
+    const float4* centroids;
+    const int32_t* token_count;
+    int32_t* assign;
+    const int32_t* header;
+    const int32_t* chunk_ev;
+    const int32_t* chunk_beg;
+    int skip_small;  // leave events with n <= P untouched
+};
+
+struct KnnArgs {
+    const float4* coords;
+    const int64_t* offsets;
+    int64_t N;
+    int P;
+    int k;
+    const float4* centroids;
+    const int32_t* token_count;
+    int32_t* knn_idx;
+};
+
+struct LloydArgs {
+    const float4* coords;
+    const float* features;
+    const int64_t* offsets;
+    int64_t N;
+    int C;
+    int charge_col;
+    int P;
+    float4* centroids;
+    const int32_t* token_count;
+    const int32_t* assign;
+    int32_t* perm;
+};
+
+struct PoolArgs {
+    const float* features;
+    const int64_t* offsets;
+    int64_t N;
+    int C;
+    int weight_col;  // -1: unit weights
+    int P;
+    int k;
+    const int32_t* token_count;
+    const int32_t* assign;
+    const int32_t* knn_idx;
+    float* pooled;
+    int32_t* cell_count;
+    int32_t* perm;
+};
+
+hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
+                       const WorkspaceLayout& L, hipStream_t s);
+hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_assign(const AssignArgs& a, int64_t max_chunks, hipStream_t s);
+hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_pool_knn(const PoolArgs& a, int64_t B, hipStream_t s);
+
+}  // namespace fpstok

@@ -1,0 +1,266 @@
+"""ctypes binding of libfpstok (include/fpstok.h).
+
+Argument marshalling only: PyTorch supplies device memory and the current
+HIP stream; every step of the tokenizer runs in the library's gfx950 kernels.
+The library must have been built (``__graft_entry__.build()`` or
+``python -m point_cloud_tokenization_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfpstok.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fpstok.h")
+
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+VORONOI, KNN = 0, 1
+MAX_PATCHES, MAX_K, MAX_LLOYD = 1024, 64, 1000
+
+
+class FpstokError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, _STATUS.get(status, status), detail))
+
+
+_STATUS = {OK: "ok", EINVAL: "invalid argument", EWORKSPACE: "workspace too small",
+           EUNSUPPORTED: "unsupported", EHIP: "HIP runtime error"}
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("coords", ctypes.c_void_p), ("features", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("num_events", ctypes.c_int64),
+                ("num_points", ctypes.c_int64), ("num_features", ctypes.c_int32),
+                ("charge_col", ctypes.c_int32)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("num_patches", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("lloyd_iters", ctypes.c_int32), ("assign_mode", ctypes.c_int32),
+                ("pool_weighted", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfpstok (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfpstok.so is not built (%s); run __graft_entry__.build()"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        B, Pp = ctypes.POINTER(Batch), ctypes.POINTER(Params)
+        L.fpstok_workspace_size.argtypes = [B, Pp]
+        L.fpstok_workspace_size.restype = sz
+        L.fpstok_sample.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_assign.argtypes = [B, Pp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_knn.argtypes = [B, Pp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_lloyd.argtypes = [B, Pp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_pool.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_validate.argtypes = [B, vp]
+        for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
+                  "fpstok_pool", "fpstok_validate"):
+            getattr(L, f).restype = ctypes.c_int
+        L.fpstok_status_string.argtypes = [ctypes.c_int]
+        L.fpstok_status_string.restype = ctypes.c_char_p
+        L.fpstok_last_error.argtypes = []
+        L.fpstok_last_error.restype = ctypes.c_char_p
+        L.fpstok_version.argtypes = []
+        L.fpstok_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def declared_functions():
+    """Names of the functions include/fpstok.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fpstok_[a-z_]+)\s*\(", text)))
+
+
+def _check(rc, where):
+    if rc != OK:
+        raise FpstokError(rc, where, lib().fpstok_last_error().decode())
+
+
+def version():
+    return lib().fpstok_version()
+
+
+# ------------------------------------------------------------ tensor helpers
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, dev=None):
+    import torch
+
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if dev is not None and t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def make_batch(coords, offsets, features=None, charge_col=-1):
+    """A Batch struct (plus the tensors it points into, kept alive)."""
+    import torch
+
+    _need(coords, torch.float32, "coords")
+    _need(offsets, torch.int64, "offsets", coords.device)
+    if coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be [N,4]")
+    C = 0
+    if features is not None:
+        _need(features, torch.float32, "features", coords.device)
+        if features.dim() != 2 or features.shape[0] != coords.shape[0]:
+            raise ValueError("features must be [N,C]")
+        C = features.shape[1]
+    bt = Batch(coords.data_ptr(), features.data_ptr() if features is not None else None,
+               offsets.data_ptr(), offsets.numel() - 1, coords.shape[0], C, charge_col)
+    return bt
+
+
+def make_params(num_patches=128, k=16, lloyd_iters=0, assign_mode=VORONOI, pool_weighted=1):
+    return Params(num_patches, k, lloyd_iters, assign_mode, pool_weighted)
+
+
+def workspace_size(bt, pr):
+    return lib().fpstok_workspace_size(ctypes.byref(bt), ctypes.byref(pr))
+
+
+def alloc_workspace(bt, pr, device):
+    import torch
+
+    n = workspace_size(bt, pr)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------- the five calls
+
+def sample(bt, pr, centroid_idx, centroids, token_count, assign, ws, start_idx=None,
+           stream=None):
+    _check(lib().fpstok_sample(ctypes.byref(bt), ctypes.byref(pr), _ptr(start_idx),
+                               _ptr(centroid_idx), _ptr(centroids), _ptr(token_count),
+                               _ptr(assign), _ptr(ws), ws.numel(), _stream_handle(stream)),
+           "fpstok_sample")
+
+
+def assign(bt, pr, centroids, token_count, out, ws, stream=None):
+    _check(lib().fpstok_assign(ctypes.byref(bt), ctypes.byref(pr), _ptr(centroids),
+                               _ptr(token_count), _ptr(out), _ptr(ws), ws.numel(),
+                               _stream_handle(stream)), "fpstok_assign")
+
+
+def knn(bt, pr, centroids, token_count, knn_idx, ws, stream=None):
+    _check(lib().fpstok_knn(ctypes.byref(bt), ctypes.byref(pr), _ptr(centroids),
+                            _ptr(token_count), _ptr(knn_idx), _ptr(ws), ws.numel(),
+                            _stream_handle(stream)), "fpstok_knn")
+
+
+def lloyd(bt, pr, centroids, token_count, assign_, ws, stream=None):
+    _check(lib().fpstok_lloyd(ctypes.byref(bt), ctypes.byref(pr), _ptr(centroids),
+                              _ptr(token_count), _ptr(assign_), _ptr(ws), ws.numel(),
+                              _stream_handle(stream)), "fpstok_lloyd")
+
+
+def pool(bt, pr, token_count, assign_, knn_idx, pooled, cell_count, ws, stream=None):
+    _check(lib().fpstok_pool(ctypes.byref(bt), ctypes.byref(pr), _ptr(token_count),
+                             _ptr(assign_), _ptr(knn_idx), _ptr(pooled), _ptr(cell_count),
+                             _ptr(ws), ws.numel(), _stream_handle(stream)), "fpstok_pool")
+
+
+def validate(bt, stream=None):
+    _check(lib().fpstok_validate(ctypes.byref(bt), _stream_handle(stream)), "fpstok_validate")
+
+
+# ------------------------------------------------------------- convenience
+
+def offsets_from_batch_ids(batch_ids, num_events):
+    """CSR offsets [B+1] from sorted per-pulse event ids (device-side; pass
+    num_events to avoid a host sync)."""
+    import torch
+
+    counts = torch.bincount(batch_ids, minlength=num_events)
+    off = torch.zeros(num_events + 1, dtype=torch.int64, device=batch_ids.device)
+    torch.cumsum(counts, 0, out=off[1:])
+    return off
+
+
+class Tokenizer:
+    """Preallocated outputs and workspace for one batch shape; call() runs the
+    whole tokenizer (sample -> [Lloyd] -> [kNN] -> pool) on the current
+    stream without host synchronization."""
+
+    def __init__(self, coords, features, offsets, num_patches=128, assign_mode="voronoi", k=16,
+                 lloyd_iters=0, pool="charge", charge_col=-1):
+        import torch
+
+        self.mode = {"voronoi": VORONOI, "knn": KNN}[assign_mode]
+        self.coords, self.features, self.offsets = coords, features, offsets
+        self.bt = make_batch(coords, offsets, features, charge_col)
+        self.pr = make_params(num_patches, k, lloyd_iters, self.mode,
+                              1 if pool == "charge" else 0)
+        dev = coords.device
+        B, N, P = offsets.numel() - 1, coords.shape[0], num_patches
+        C = features.shape[1]
+        self.out = dict(
+            centroid_idx=torch.empty((B, P), dtype=torch.int32, device=dev),
+            centroids=torch.empty((B, P, 4), dtype=torch.float32, device=dev),
+            token_count=torch.empty(B, dtype=torch.int32, device=dev),
+            assign=torch.empty(N, dtype=torch.int32, device=dev),
+            knn_idx=torch.empty((B, P, k), dtype=torch.int32, device=dev)
+            if self.mode == KNN else None,
+            pooled=torch.empty((B, P, C), dtype=torch.float32, device=dev),
+            cell_count=torch.empty((B, P), dtype=torch.int32, device=dev),
+        )
+        self.ws = alloc_workspace(self.bt, self.pr, dev)
+
+    def __call__(self, start_idx=None, stream=None):
+        o = self.out
+        need_assign = self.mode == VORONOI or self.pr.lloyd_iters > 0
+        sample(self.bt, self.pr, o["centroid_idx"], o["centroids"], o["token_count"],
+               o["assign"] if need_assign else None, self.ws, start_idx, stream)
+        if self.pr.lloyd_iters > 0:
+            lloyd(self.bt, self.pr, o["centroids"], o["token_count"], o["assign"], self.ws,
+                  stream)
+        if self.mode == KNN:
+            knn(self.bt, self.pr, o["centroids"], o["token_count"], o["knn_idx"], self.ws,
+                stream)
+        pool(self.bt, self.pr, o["token_count"], o["assign"], o["knn_idx"], o["pooled"],
+             o["cell_count"], self.ws, stream)
+        return o
+
+
+def tokenize(coords, features, offsets=None, batch_ids=None, num_events=None, num_patches=128,
+             assign_mode="voronoi", k=16, lloyd_iters=0, pool="charge", charge_col=-1,
+             start_idx=None, stream=None):
+    """Tokenize one batch: returns a dict of device tensors (centroid_idx,
+    centroids, token_count, assign, knn_idx or None, pooled, cell_count)."""
+    if offsets is None:
+        if batch_ids is None or num_events is None:
+            raise ValueError("give offsets, or batch_ids with num_events")
+        offsets = offsets_from_batch_ids(batch_ids, num_events)
+    t = Tokenizer(coords, features, offsets, num_patches, assign_mode, k, lloyd_iters, pool,
+                  charge_col)
+    return t(start_idx, stream)

@@ -1,0 +1,155 @@
+"""Helpers for the GPU parity tests: run each libfpstok call through the C
+ABI on one batch and compare with the oracle stage by stage.
+
+Acceptance: centroid indices, token counts, assignments, kNN lists and cell
+counts bit-exact; pooled values and Lloyd centroids within
+|gpu - oracle| <= 1e-5 * max(|oracle|, s), where s is the weighted mean of
+|value| over the token's members (the scale of the sum itself; a pure
+relative test is ill-conditioned when a mean of signed values lands near 0).
+"""
+import sys
+
+import numpy as np
+
+RTOL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to("cuda:0")
+
+
+def to_np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def member_scale(values, offsets, P, weights, mode, assign=None, knn_idx=None):
+    """s[b, j, c] = sum(w |v[c]|) / sum(w) over the members of token (b, j)."""
+    B = offsets.size - 1
+    C = values.shape[1]
+    if values.shape[0] == 0:
+        return np.zeros((B, P, C))
+    absv = np.abs(values.astype(np.float64))
+    w = weights.astype(np.float64)
+    num = np.zeros((B * P, C))
+    den = np.zeros(B * P)
+    if mode == 0:
+        ev = np.repeat(np.arange(B), np.diff(offsets))
+        tok = ev * P + assign.astype(np.int64)
+        np.add.at(num, tok, w[:, None] * absv)
+        np.add.at(den, tok, w)
+    else:
+        k = knn_idx.shape[-1]
+        rows = knn_idx.reshape(B * P, k).astype(np.int64)
+        base = np.repeat(offsets[:-1], P)[:, None]
+        valid = rows >= 0
+        g = np.where(valid, rows + base, 0)
+        contrib = np.where(valid[..., None], (w[g])[..., None] * absv[g], 0.0)
+        num = contrib.sum(axis=1)
+        den = np.where(valid, w[g], 0.0).sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        s = np.where(den[:, None] > 0, num / den[:, None], 0.0)
+    return s.reshape(B, P, C)
+
+
+def assert_close_scaled(got, ref, scale, what):
+    got = got.astype(np.float64)
+    ref = ref.astype(np.float64)
+    tol = RTOL * np.maximum(np.abs(ref), scale)
+    bad = np.abs(got - ref) > tol
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d elements out of tolerance, e.g. %s got %s ref %s" % (
+            what, int(bad.sum()), idx.tolist(), got[tuple(idx[0])], ref[tuple(idx[0])]))
+    return float(np.mean(got == ref))
+
+
+def run_pipeline(batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5, start_idx=None):
+    """Every stage on the GPU; returns numpy arrays of each stage's output and
+    the stage inputs needed to replay them on the oracle."""
+    import torch
+
+    from point_cloud_tokenization_amd import fpstok as F
+
+    x = to_dev(batch["coords"])
+    f = to_dev(batch["features"])
+    off = to_dev(batch["offsets"])
+    B = batch["offsets"].size - 1
+    N = batch["coords"].shape[0]
+    C = batch["features"].shape[1]
+    bt = F.make_batch(x, off, f, charge_col)
+    pr = F.make_params(P, k, L, mode, 1 if weighted else 0)
+    ws = F.alloc_workspace(bt, pr, x.device)
+    dev = x.device
+    cidx = torch.empty((B, P), dtype=torch.int32, device=dev)
+    cen = torch.empty((B, P, 4), dtype=torch.float32, device=dev)
+    tc = torch.empty(B, dtype=torch.int32, device=dev)
+    asg = torch.empty(N, dtype=torch.int32, device=dev)
+    st = None if start_idx is None else to_dev(np.asarray(start_idx, np.int32))
+    F.sample(bt, pr, cidx, cen, tc, asg, ws, st)
+    torch.cuda.synchronize()
+    out = dict(centroid_idx=to_np(cidx), centroids=to_np(cen), token_count=to_np(tc),
+               assign=to_np(asg))
+    if L > 0:
+        F.lloyd(bt, pr, cen, tc, asg, ws)
+        torch.cuda.synchronize()
+        out["lloyd_centroids"] = to_np(cen)
+        out["lloyd_assign"] = to_np(asg)
+    kn = None
+    if mode == 1:
+        kn = torch.empty((B, P, k), dtype=torch.int32, device=dev)
+        F.knn(bt, pr, cen, tc, kn, ws)
+        torch.cuda.synchronize()
+        out["knn_idx"] = to_np(kn)
+    pooled = torch.empty((B, P, C), dtype=torch.float32, device=dev)
+    cnt = torch.empty((B, P), dtype=torch.int32, device=dev)
+    F.pool(bt, pr, tc, asg, kn, pooled, cnt, ws)
+    torch.cuda.synchronize()
+    out["pooled"] = to_np(pooled)
+    out["cell_count"] = to_np(cnt)
+    return out
+
+
+def check_pipeline(oracle, batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5,
+                   start_idx=None, label=""):
+    """Run the GPU pipeline and compare every stage with the oracle fed the
+    same inputs.  Returns a dict of exact-match fractions of float outputs."""
+    log("parity case %s: B=%d N=%d P=%d mode=%d k=%d L=%d" % (
+        label, batch["offsets"].size - 1, batch["coords"].shape[0], P, mode, k, L))
+    g = run_pipeline(batch, P, mode, k, L, weighted, charge_col, start_idx)
+    x, f, off = batch["coords"], batch["features"], batch["offsets"]
+    stats = {}
+    sel, cen, tc, asg = oracle.sample(x, off, P, start_idx=start_idx)
+    np.testing.assert_array_equal(g["token_count"], tc, err_msg="token_count " + label)
+    np.testing.assert_array_equal(g["centroid_idx"], sel, err_msg="centroid_idx " + label)
+    np.testing.assert_array_equal(g["centroids"], cen, err_msg="centroids " + label)
+    np.testing.assert_array_equal(g["assign"], asg, err_msg="assign " + label)
+    if L > 0:
+        cen, asg = oracle.lloyd(x, f, off, P, L, cen, tc, asg, charge_col)
+        w = f[:, charge_col] if charge_col >= 0 else np.ones(x.shape[0], np.float32)
+        scale = member_scale(x, off, P, w, 0, assign=asg)
+        stats["lloyd_centroids_exact"] = assert_close_scaled(
+            g["lloyd_centroids"], cen, scale, "lloyd centroids " + label)
+        np.testing.assert_array_equal(g["lloyd_assign"], asg, err_msg="lloyd assign " + label)
+        # the GPU's Lloyd centroids feed the kNN and pool stages below
+        cen = g["lloyd_centroids"]
+    kn = None
+    if mode == 1:
+        kn = oracle.knn(x, off, P, k, cen, tc)
+        np.testing.assert_array_equal(g["knn_idx"], kn, err_msg="knn_idx " + label)
+    pooled, cnt = oracle.pool(f, off, P, tc, mode=mode, assign=asg, knn_idx=kn, k=k,
+                              weighted=weighted, charge_col=charge_col)
+    np.testing.assert_array_equal(g["cell_count"], cnt, err_msg="cell_count " + label)
+    w = f[:, charge_col] if (weighted and charge_col >= 0) else np.ones(x.shape[0], np.float32)
+    scale = member_scale(f, off, P, w, mode, assign=asg, knn_idx=kn)
+    stats["pooled_exact"] = assert_close_scaled(g["pooled"], pooled, scale, "pooled " + label)
+    return stats

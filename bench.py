@@ -1,0 +1,290 @@
+"""Benchmark of the FPS tokenizer on one MI355X.
+
+One step = the whole tokenizer over one batch already resident in HBM:
+fpstok_sample (FPS + fused Voronoi assignment / pass-through), then
+[fpstok_lloyd], [fpstok_knn], fpstok_pool -- every call of the configured
+workload.  The headline workload is 64 IceCube-shaped events with
+num_patches = 128, Voronoi mode, charge-weighted pooling; the metric is
+events/s.  Per-call kernel times are measured live with HIP events on the
+stream the kernels run on, inside the timed region.
+
+Prints ONE JSON line (rank 0).  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "icecube_b64_voronoi"
+# MI355X published peaks used for the roofline (256 CUs, 2.4 GHz):
+HBM_PEAK_GBPS = 8000.0
+# non-packed float32 VALU peak: the published 157.3 TFLOP/s counts a fused
+# multiply-add as 2 flops, i.e. 128 float32 lane-operations per clock per CU
+# (256 CU x 4 SIMD x 32 lanes x 2.4 GHz = 78.6 T lane-ops/s); the FPS path
+# issues plain (unfused) add/mul/compare/select operations, one lane-op each
+VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12
+# algorithmic VALU operations per FPS point-iteration: 4 sub + 4 mul + 3 add
+# (the float32 squared distance), 1 running-min update, 1 fused Voronoi
+# select, 1 argmax compare
+FPS_OPS_PER_POINT_ITER = 14
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def workload_stats(b):
+    n = np.diff(b["offsets"])
+    P = b["P"]
+    big = n[n > P]
+    C = b["features"].shape[1]
+    B = n.size
+    N = int(n.sum())
+    return dict(
+        B=B, N=N, P=P, C=C,
+        fps_events=int(big.size),
+        point_iters=int((big.astype(np.int64) * (P - 1)).sum()),
+        max_n=int(n.max()) if n.size else 0,
+        # pool reads features + assign per pulse, writes pooled + count per slot
+        pool_bytes=int((4 * C + 4) * N + (4 * C + 4) * B * P),
+    )
+
+
+class Runner:
+    """Device-resident inputs, outputs and workspace for one workload, with the
+    per-call HIP events of the timed region."""
+
+    def __init__(self, b):
+        import torch
+
+        from point_cloud_tokenization_amd import fpstok as F
+
+        self.F = F
+        self.b = b
+        dev = torch.device("cuda:0")
+        self.x = torch.from_numpy(b["coords"]).to(dev)
+        self.f = torch.from_numpy(b["features"]).to(dev)
+        self.off = torch.from_numpy(b["offsets"]).to(dev)
+        self.tok = F.Tokenizer(self.x, self.f, self.off, num_patches=b["P"],
+                               assign_mode="knn" if b["mode"] == 1 else "voronoi", k=b["k"],
+                               lloyd_iters=b["L"], pool="charge" if b["weighted"] else "mean",
+                               charge_col=b["charge_col"])
+        self.calls = ["sample"] + (["lloyd"] if b["L"] > 0 else []) + \
+                     (["knn"] if b["mode"] == 1 else []) + ["pool"]
+
+    def step(self, events=None):
+        F, t, o = self.F, self.tok, self.tok.out
+
+        def mark(i):
+            if events is not None:
+                events[i].record()
+
+        mark(0)
+        F.sample(t.bt, t.pr, o["centroid_idx"], o["centroids"], o["token_count"], o["assign"],
+                 t.ws)
+        i = 1
+        mark(i)
+        if t.pr.lloyd_iters > 0:
+            F.lloyd(t.bt, t.pr, o["centroids"], o["token_count"], o["assign"], t.ws)
+            i += 1
+            mark(i)
+        if t.mode == F.KNN:
+            F.knn(t.bt, t.pr, o["centroids"], o["token_count"], o["knn_idx"], t.ws)
+            i += 1
+            mark(i)
+        F.pool(t.bt, t.pr, o["token_count"], o["assign"], o["knn_idx"], o["pooled"],
+               o["cell_count"], t.ws)
+        i += 1
+        mark(i)
+
+    def timed_graph(self, steps, warmup):
+        """Whole steps captured once in a HIP graph and replayed: no host
+        launch overhead between the kernels.  Returns wall seconds of the K
+        timed replays."""
+        import torch
+
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        for _ in range(max(1, warmup // 2)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def timed(self, steps, warmup):
+        import torch
+
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ncalls = len(self.calls)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.step(evs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_call = {c: 0.0 for c in self.calls}
+        for s in range(steps):
+            for i, c in enumerate(self.calls):
+                per_call[c] += evs[s][i].elapsed_time(evs[s][i + 1]) * 1e-3
+        per_call = {c: v / steps for c, v in per_call.items()}
+        return wall, per_call
+
+
+def cpu_baseline(b, budget_s):
+    """The oracle as it stands, single-threaded, on repeats of the same batch
+    until about budget_s seconds of CPU work."""
+    import oracle
+
+    kw = dict(P=b["P"], mode=b["mode"], k=b["k"], L=b["L"], weighted=b["weighted"],
+              charge_col=b["charge_col"])
+    oracle.tokenize(b["coords"], b["features"], b["offsets"], **kw)  # load + warm
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.tokenize(b["coords"], b["features"], b["offsets"], **kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    B = b["offsets"].size - 1
+    return dict(value=B * reps / el, unit="events/s", cores=1, kind="oracle",
+                sample="%d repeats of the same %d-event batch (%.1f s, one host thread)" % (
+                    reps, B, el))
+
+
+def roofline_for(call, st, seconds):
+    if call == "sample":
+        ops = st["point_iters"] * FPS_OPS_PER_POINT_ITER
+        ach = ops / seconds / 1e12
+        return dict(bound="alu", achieved=ach, peak=VALU_PEAK_TOPS, unit="TOP/s",
+                    frac=ach / VALU_PEAK_TOPS, traffic=None, kernel="sample_kernel (FPS)")
+    if call == "pool":
+        ach = st["pool_bytes"] / seconds / 1e9
+        return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBPS, traffic=None, kernel="pool_voronoi_kernel")
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--secondary", type=int, default=1,
+                    help="also time the other workloads (reported under 'secondary')")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph",
+                    help="graph: time replays of one captured step (default); eager: time "
+                         "host-launched steps")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the tokenizer runs on a single MI355X and "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from point_cloud_tokenization_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    b = synth.make_batch(args.workload)
+    st = workload_stats(b)
+    log("workload %s: %s" % (args.workload, st))
+    r = Runner(b)
+    # per-call kernel durations: HIP events on the kernels' stream between the
+    # calls of K host-launched steps
+    wall_eager, per_call = r.timed(args.steps, args.warmup)
+    wall = r.timed_graph(args.steps, args.warmup) if args.launch == "graph" else wall_eager
+    ms = wall / args.steps * 1e3
+    value = st["B"] * args.steps / wall
+    dom = max(per_call, key=per_call.get)
+    roof = roofline_for(dom, st, per_call[dom])
+    fps_rate = st["point_iters"] / per_call["sample"]
+    pool_gbps = st["pool_bytes"] / per_call["pool"] / 1e9
+    log("per-call kernel time (s): %s" % per_call)
+
+    secondary = {}
+    if args.secondary:
+        for name in synth.WORKLOAD_ORDER:
+            if name == args.workload:
+                continue
+            bb = synth.make_batch(name)
+            s2 = workload_stats(bb)
+            steps = 20 if s2["N"] > 1_000_000 else 100
+            rr = Runner(bb)
+            w2, pc2 = rr.timed(steps, 5)
+            if args.launch == "graph":
+                w2 = rr.timed_graph(steps, 5)
+            secondary[name] = dict(
+                events_per_s=s2["B"] * steps / w2, ms_per_step=w2 / steps * 1e3,
+                per_call_us={c: v * 1e6 for c, v in pc2.items()},
+                fps_point_iters_per_s=s2["point_iters"] / pc2["sample"],
+                pool_GBps=s2["pool_bytes"] / pc2["pool"] / 1e9, B=s2["B"], N=s2["N"],
+                P=s2["P"])
+            log("secondary %s: %s" % (name, secondary[name]))
+
+    cpu = cpu_baseline(b, args.cpu_budget)
+    line = {
+        "metric": "events/sec (FPS+assign+pool) at batch 64, P=128",
+        "value": value,
+        "unit": "events/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "events": st["B"], "pulses": st["N"],
+                   "num_patches": st["P"], "features": st["C"],
+                   "assign_mode": "knn" if b["mode"] == 1 else "voronoi",
+                   "lloyd_iters": b["L"], "pool": "charge" if b["weighted"] else "mean",
+                   "seed": b["seed"], "launch": "hipGraph" if args.launch == "graph" else "eager"},
+        "eager_events_per_s": st["B"] * args.steps / wall_eager,
+        "fps_point_iters_per_s": fps_rate,
+        "pool_hbm_GBps": pool_gbps,
+        "per_call_us": {c: v * 1e6 for c, v in per_call.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+        "host": {"cpu": platform.processor() or platform.machine(),
+                 "nproc": os.cpu_count(), "gpu": torch.cuda.get_device_name(0)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

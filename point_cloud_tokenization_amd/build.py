@@ -20,6 +20,10 @@ HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the register-resident FPS reads its pulse arrays with a uniform dynamic
+    # index; this limit lets every instantiation keep them in VGPRs (no
+    # scratch memory)
+    "-mllvm", "-amdgpu-promote-alloca-to-vector-limit=1024",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
@@ -39,6 +43,15 @@ def build(verbose: bool = False, extra=()) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
+
+
+def device_asm(out_path: str) -> str:
+    """Compile the kernels to gfx950 assembly (for the build checks)."""
+    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
+           "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-o", out_path, SOURCES[0]]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out_path
 
 
 def is_stale() -> bool:

@@ -59,6 +59,13 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N) {
     at += align256((size_t)nn * sizeof(int32_t));
     L.perm = at;
     at += align256((size_t)nn * sizeof(int32_t));
+    L.max_items = sample_max_items(B, nn);
+    L.item_ev = at;
+    at += align256((size_t)L.max_items * sizeof(int32_t));
+    L.item_g = at;
+    at += align256((size_t)L.max_items * sizeof(int32_t));
+    L.gang_rec = at;
+    at += align256((size_t)L.max_items * 12 * sizeof(unsigned long long));
     L.total = at;
     return L;
 }
@@ -161,6 +168,10 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
     a.assign = assign;
     a.ws_mind = at<float>(ws, L.mind);
     a.ws_near = at<int32_t>(ws, L.near);
+    a.header = at<int32_t>(ws, L.header);
+    a.item_ev = at<int32_t>(ws, L.item_ev);
+    a.item_g = at<int32_t>(ws, L.item_g);
+    a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
     hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
     return ok();

@@ -9,8 +9,9 @@
 
 namespace fpstok {
 
-// Pulses per chunk of the chunked kernels (assign).  256 threads x 4 pulses.
-constexpr int kChunk = 1024;
+// Pulses per chunk of the chunked kernels (assign): one per thread of a
+// 256-thread workgroup.
+constexpr int kChunk = 256;
 
 // Workspace carve-up.  Every region starts on a 256-byte boundary.
 struct WorkspaceLayout {
@@ -20,11 +21,16 @@ struct WorkspaceLayout {
     size_t mind;        // float[N]: running min distance (large-event FPS)
     size_t near;        // int32[N]: running nearest slot (large-event FPS, no assign out)
     size_t perm;        // int32[N]: pulses sorted by token (Lloyd, pool)
+    size_t item_ev;     // int32[max_items]: FPS work items (event)
+    size_t item_g;      // int32[max_items]: FPS work items (shard)
+    size_t gang_rec;    // uint64[max_items][12]: gang exchange records
     size_t total;
     int64_t max_chunks;
+    int64_t max_items;
 };
 
 WorkspaceLayout workspace_layout(int64_t B, int64_t N);
+int64_t sample_max_items(int64_t B, int64_t N);
 
 struct SampleArgs {
     const float4* coords;
@@ -38,6 +44,10 @@ struct SampleArgs {
     int32_t* assign;
     float* ws_mind;
     int32_t* ws_near;
+    int32_t* header;                // [1] items, [2] claim counter, [3] error word
+    int32_t* item_ev;               // [max_items] event of each work item
+    int32_t* item_g;                // [max_items] shard of each work item
+    unsigned long long* gang_rec;   // [max_items][2][6] gang records
 };
 
 struct AssignArgs {

@@ -60,13 +60,12 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// v permuted across lanes by a DPP control; lanes of rows outside ROW_MASK
+// get `identity`.  Passing the identity of the combining operation lets the
+// compiler fold the move into the ALU instruction (v_max_i32_dpp, ...).
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
-}
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v)));
+__device__ __forceinline__ int dpp_i(int v, int identity) {
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xF, false);
 }
 
 // DPP controls (gfx9 family): quad permutes, row mirrors, row broadcasts.
@@ -77,23 +76,28 @@ constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowBcast15 = 0x142;
 constexpr int kRowBcast31 = 0x143;
 
+// Wave-wide minimum / maximum, returned uniformly: four in-row DPP steps,
+// then the two row broadcasts that carry the result into lane 63.
 __device__ __forceinline__ int wave_min_i(int v) {
-    v = min(v, dpp_i<kQuadSwap1, 0xF>(v));
-    v = min(v, dpp_i<kQuadSwap2, 0xF>(v));
-    v = min(v, dpp_i<kRowHalfMirror, 0xF>(v));
-    v = min(v, dpp_i<kRowMirror, 0xF>(v));
-    v = min(v, dpp_i<kRowBcast15, 0xA>(v));
-    v = min(v, dpp_i<kRowBcast31, 0xC>(v));
+    constexpr int I = INT32_MAX;
+    v = min(v, dpp_i<kQuadSwap1, 0xF>(v, I));
+    v = min(v, dpp_i<kQuadSwap2, 0xF>(v, I));
+    v = min(v, dpp_i<kRowHalfMirror, 0xF>(v, I));
+    v = min(v, dpp_i<kRowMirror, 0xF>(v, I));
+    v = min(v, dpp_i<kRowBcast15, 0xA>(v, I));
+    v = min(v, dpp_i<kRowBcast31, 0xC>(v, I));
     return readlane_i(v, 63);
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-    v = v + dpp_i<kQuadSwap1, 0xF>(v);
-    v = v + dpp_i<kQuadSwap2, 0xF>(v);
-    v = v + dpp_i<kRowHalfMirror, 0xF>(v);
-    v = v + dpp_i<kRowMirror, 0xF>(v);
-    // rows hold their sums; combine the four row sums through readlane
-    return readlane_i(v, 0) + readlane_i(v, 16) + readlane_i(v, 32) + readlane_i(v, 48);
+__device__ __forceinline__ int wave_max_i(int v) {
+    constexpr int I = INT32_MIN;
+    v = max(v, dpp_i<kQuadSwap1, 0xF>(v, I));
+    v = max(v, dpp_i<kQuadSwap2, 0xF>(v, I));
+    v = max(v, dpp_i<kRowHalfMirror, 0xF>(v, I));
+    v = max(v, dpp_i<kRowMirror, 0xF>(v, I));
+    v = max(v, dpp_i<kRowBcast15, 0xA>(v, I));
+    v = max(v, dpp_i<kRowBcast31, 0xC>(v, I));
+    return readlane_i(v, 63);
 }
 
 // Inclusive prefix sum over the wave (Hillis-Steele with cross-lane shuffles).
@@ -170,16 +174,33 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ 
 
 // ---------------------------------------------------------------------- FPS
 
+#define FPSTOK_MAX_SLOTS 1024
 constexpr int kFpsT = 256;                 // threads per workgroup (4 waves)
 constexpr int kFpsW = kFpsT / 64;
 constexpr int kFpsM = 16;                  // register-resident pulses per thread
-constexpr int kFpsCap = kFpsT * kFpsM;     // largest event kept in registers
+constexpr int kFpsCap = kFpsT * kFpsM;     // pulses one workgroup holds in registers
+constexpr int kGangMax = 64;               // workgroups sharing one event at most
+constexpr int kRecWords = 6;               // 64-bit words of a gang record
+constexpr uint32_t kSpinLimit = 1u << 22;  // bound on every inter-workgroup wait
 
 struct __align__(16) FpsSlot {
     float v;
     int i;
     float pad0, pad1;
     float4 c;
+};
+
+// The part of an event one workgroup holds.  A gang is the set of G
+// workgroups that share one event; each keeps a contiguous shard of pulses in
+// registers, and after every iteration the shards exchange their candidates
+// through records in device memory.
+struct Shard {
+    int lo;                    // first event-local pulse of the shard
+    int cnt;                   // pulses in the shard
+    int g;                     // shard index
+    int G;                     // shards of the event (1: no exchange)
+    unsigned long long* rec;   // records of the gang: [G][2][kRecWords]
+    int32_t* err;              // device error word (bounded wait exceeded)
 };
 
 // Workgroup-level argmax over the per-wave candidates written to `slots`:
@@ -193,8 +214,8 @@ __device__ __forceinline__ FpsSlot reduce_slots_blocked(const FpsSlot* slots) {
     FpsSlot s;
     if (has) s = slots[lane];
     const int v = has ? __float_as_int(s.v) : INT32_MIN;
-    int r = max(v, dpp_i<kQuadSwap1, 0xF>(v));
-    r = max(r, dpp_i<kQuadSwap2, 0xF>(r));
+    int r = max(v, dpp_i<kQuadSwap1, 0xF>(v, INT32_MIN));
+    r = max(r, dpp_i<kQuadSwap2, 0xF>(r, INT32_MIN));
     const int gm = readlane_i(r, 0);
     const int L = (int)__builtin_ctzll(ballot(has && v == gm));
     FpsSlot out;
@@ -207,53 +228,121 @@ __device__ __forceinline__ FpsSlot reduce_slots_blocked(const FpsSlot* slots) {
     return out;
 }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-    v = max(v, dpp_i<kQuadSwap1, 0xF>(v));
-    v = max(v, dpp_i<kQuadSwap2, 0xF>(v));
-    v = max(v, dpp_i<kRowHalfMirror, 0xF>(v));
-    v = max(v, dpp_i<kRowMirror, 0xF>(v));
-    v = max(v, dpp_i<kRowBcast15, 0xA>(v));
-    v = max(v, dpp_i<kRowBcast31, 0xC>(v));
-    return readlane_i(v, 63);
+__device__ __forceinline__ unsigned long long tagged(int j, uint32_t payload) {
+    return ((unsigned long long)(uint32_t)(j + 1) << 32) | payload;
 }
 
-// FPS of one event with n in (P, 256*M], every pulse held in registers.
-// Wave w owns the 64*M pulses starting at w*64*M; its register k of lane l
-// holds pulse w*64*M + 64*k + l, so the loads are coalesced and the lowest
-// pulse index among ties is the lowest lane of the lowest register (then the
-// lowest wave) holding the maximum.
+// Gang-wide argmax of iteration j: thread 0 publishes this workgroup's
+// candidate as six tagged 64-bit words (relaxed agent-scope atomics; every
+// word carries the iteration tag, so no ordering between them is needed);
+// every wave then polls the G records until all carry tag j+1 and reduces
+// them: largest value, then lowest shard (= lowest pulse index).  Records
+// are double-buffered by iteration parity: a workgroup writes iteration j+2
+// only after it has seen every record of j+1, which each workgroup publishes
+// only after all of its waves finished reading iteration j.
+__device__ __forceinline__ FpsSlot gang_exchange(const FpsSlot& mine, const Shard& sh, int j) {
+    const int par = j & 1;
+    if (threadIdx.x == 0) {
+        unsigned long long* r = sh.rec + ((size_t)sh.g * 2 + par) * kRecWords;
+        const uint32_t pay[kRecWords] = {__float_as_uint(mine.v), (uint32_t)mine.i,
+                                         __float_as_uint(mine.c.x), __float_as_uint(mine.c.y),
+                                         __float_as_uint(mine.c.z), __float_as_uint(mine.c.w)};
+#pragma unroll
+        for (int q = 0; q < kRecWords; ++q)
+            __hip_atomic_store(r + q, tagged(j, pay[q]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int lane = lane_id();
+    const bool has = lane < sh.G;
+    const unsigned long long* r = sh.rec + ((size_t)(has ? lane : 0) * 2 + par) * kRecWords;
+    unsigned long long w[kRecWords];
+    const uint32_t want = (uint32_t)(j + 1);
+    for (uint32_t spin = 0;; ++spin) {
+        bool ok = true;
+        if (has) {
+#pragma unroll
+            for (int q = 0; q < kRecWords; ++q) {
+                w[q] = __hip_atomic_load(r + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (uint32_t)(w[q] >> 32) == want;
+            }
+        }
+        if (ballot(!ok) == 0) break;
+        if (spin >= kSpinLimit) {
+            if (lane == 0) __hip_atomic_store(sh.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    const int v = has ? (int)(uint32_t)w[0] : INT32_MIN;
+    const int gm = wave_max_i(v);
+    const int L = (int)__builtin_ctzll(ballot(has && v == gm));
+    FpsSlot out;
+    out.v = __int_as_float(gm);
+    out.i = readlane_i((int)(uint32_t)w[1], L);
+    out.c.x = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[2], L));
+    out.c.y = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[3], L));
+    out.c.z = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[4], L));
+    out.c.w = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[5], L));
+    return out;
+}
+
+// Write the selection order (and the selected coordinates) of one event.
+__device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
+                                                const float4* __restrict__ p, const int* s_sel) {
+    __syncthreads();
+    for (int j = threadIdx.x; j < a.P; j += blockDim.x) {
+        const int s = s_sel[j];
+        a.centroid_idx[b * a.P + j] = s;
+        a.centroids[b * a.P + j] = p[s];
+    }
+}
+
+// FPS over one shard of an event (the whole event when G = 1) with at most
+// 256*M pulses, every pulse held in registers.  Lane l of wave w owns the M
+// consecutive pulses starting at shard.lo + (64*w + l)*M, so a lower lane (and
+// a lower wave, then a lower shard) always holds lower pulse indices.
 //
 // Per pulse and iteration: the float32 distance to the newest centroid (11
-// VALU ops), the fused Voronoi update (compare + 2 selects) and a share of a
-// 3-input max.  Minimum distances are float32 values in {-1} U [0, inf]
-// (-1 marks padding), compared as int32 bit patterns.
+// VALU ops), the fused Voronoi update (compare + 2 selects) and the lane's
+// running (first) maximum (compare, select, max).  Minimum distances are
+// float32 values in {-1} U [0, inf] (-1 marks padding), compared as int32
+// bit patterns, whose order they keep.  The wave's argmax is then the lowest
+// lane holding the wave maximum (one ballot), its pulse is that lane's first
+// maximum, and the pulse's coordinates are read from the lane's registers
+// with a uniform index.
 //
 // Selected pulses are not marked: a selected pulse has min distance exactly
 // 0, so while the maximum is > 0 it cannot win; when the maximum is 0 every
 // pulse has min distance 0 and the rule "lowest unselected index" is applied
 // from a selection bitmap over indices 0..2047 (the answer is < P <= 1024).
+//
+// The selection order is kept in LDS (s_sel) and written out after the loop:
+// a global store inside the loop would put its completion on every
+// iteration's barrier.
 template <int M>
-__device__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n, int s0) {
-    __shared__ FpsSlot slots[2][kFpsW];
+__device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n,
+                                              int s0, const Shard& sh, FpsSlot (*slots)[kFpsW],
+                                              int* s_sel) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
     const int P = a.P;
     const float4* __restrict__ p = a.coords + off;
-    const int wbase = wave * 64 * M;
+    const int lbase = sh.lo + tid * M;  // first pulse of this lane
+    const int send = sh.lo + sh.cnt;
 
     float px[M], py[M], pz[M], pt[M], md[M];
     int nr[M];
 #pragma unroll
     for (int k = 0; k < M; ++k) {
-        const int i = wbase + 64 * k + lane;
+        const int i = lbase + k;
         float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < n) q = p[i];
+        if (i < send) q = p[i];
         px[k] = q.x;
         py[k] = q.y;
         pz[k] = q.z;
         pt[k] = q.w;
-        md[k] = i < n ? INFINITY : -1.0f;  // padding never wins and is never updated
+        md[k] = i < send ? INFINITY : -1.0f;  // padding never wins and is never updated
         nr[k] = 0;
     }
 
@@ -261,41 +350,30 @@ __device__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n
     int s = s0;
     float4 c = p[s];
     for (int j = 0; j < P; ++j) {
-        if (tid == 0) {
-            a.centroid_idx[b * P + j] = s;
-            a.centroids[b * P + j] = c;
-        }
+        if (tid == 0) s_sel[j] = s;
         mark_selected(selbits, s);
         int bv = INT32_MIN;
+        int bk = 0;
 #pragma unroll
         for (int k = 0; k < M; ++k) {
             const float d = sqd(px[k], py[k], pz[k], pt[k], c.x, c.y, c.z, c.w);
             const bool u = d < md[k];
             nr[k] = u ? j : nr[k];
             md[k] = u ? d : md[k];
-            bv = max(bv, __float_as_int(md[k]));
+            const int mi = __float_as_int(md[k]);
+            bk = mi > bv ? k : bk;
+            bv = max(bv, mi);
         }
         if (j + 1 == P) break;
 
         const int wm = wave_max_i(bv);
-        // lowest (register, lane) holding the wave maximum; every register
-        // index is a compile-time constant, so no register indexing
-        int wi = 0;
-        float4 wc = make_float4(0.f, 0.f, 0.f, 0.f);
-        bool found = false;
-#pragma unroll
-        for (int k = 0; k < M; ++k) {
-            if (!found) {
-                const uint64_t mk = ballot(__float_as_int(md[k]) == wm);
-                if (mk != 0) {
-                    found = true;
-                    const int L = (int)__builtin_ctzll(mk);
-                    wi = wbase + 64 * k + L;
-                    wc = make_float4(readlane_f(px[k], L), readlane_f(py[k], L),
-                                     readlane_f(pz[k], L), readlane_f(pt[k], L));
-                }
-            }
-        }
+        const int L = (int)__builtin_ctzll(ballot(bv == wm));
+        const int ks = readlane_i(bk, L);
+        // the indexed register reads are per-lane moves: they run with every
+        // lane active, before the single-lane slot write
+        const float4 wc = make_float4(readlane_f(px[ks], L), readlane_f(py[ks], L),
+                                      readlane_f(pz[ks], L), readlane_f(pt[ks], L));
+        const int wi = readlane_i(lbase, L) + ks;
         if (lane == 0) {
             FpsSlot& o = slots[j & 1][wave];
             o.v = __int_as_float(wm);
@@ -303,7 +381,8 @@ __device__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n
             o.c = wc;
         }
         __syncthreads();
-        const FpsSlot g = reduce_slots_blocked(slots[j & 1]);
+        FpsSlot g = reduce_slots_blocked(slots[j & 1]);
+        if (sh.G > 1) g = gang_exchange(g, sh, j);
         if (g.v == 0.0f) {
             s = min(first_unselected(selbits), n - 1);
             c = p[s];
@@ -315,37 +394,39 @@ __device__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n
     if (a.assign) {
 #pragma unroll
         for (int k = 0; k < M; ++k) {
-            const int i = wbase + 64 * k + lane;
-            if (i < n) a.assign[off + i] = nr[k];
+            const int i = lbase + k;
+            if (i < send) a.assign[off + i] = nr[k];
         }
     }
+    if (sh.g == 0) write_selection(a, b, p, s_sel);
 }
 
-// Register-resident FPS for m = ceil(n / 256) pulses per thread.
-__device__ void fps_registers_dispatch(const SampleArgs& a, int64_t b, int64_t off, int n,
-                                       int s0) {
-    switch ((n + kFpsT - 1) / kFpsT) {
-        case 1: fps_registers<1>(a, b, off, n, s0); break;
-        case 2: fps_registers<2>(a, b, off, n, s0); break;
-        case 3: fps_registers<3>(a, b, off, n, s0); break;
-        case 4: fps_registers<4>(a, b, off, n, s0); break;
-        case 5: fps_registers<5>(a, b, off, n, s0); break;
-        case 6: fps_registers<6>(a, b, off, n, s0); break;
-        case 7: fps_registers<7>(a, b, off, n, s0); break;
-        case 8: fps_registers<8>(a, b, off, n, s0); break;
-        case 9: case 10: fps_registers<10>(a, b, off, n, s0); break;
-        case 11: case 12: fps_registers<12>(a, b, off, n, s0); break;
-        case 13: case 14: fps_registers<14>(a, b, off, n, s0); break;
-        default: fps_registers<16>(a, b, off, n, s0); break;
+// Register-resident FPS for m = ceil(shard / 256) pulses per thread.
+__device__ __forceinline__ void fps_registers_dispatch(const SampleArgs& a, int64_t b, int64_t off, int n,
+                                       int s0, const Shard& sh, FpsSlot (*sl)[kFpsW], int* ss) {
+    switch ((sh.cnt + kFpsT - 1) / kFpsT) {
+        case 1: fps_registers<1>(a, b, off, n, s0, sh, sl, ss); break;
+        case 2: fps_registers<2>(a, b, off, n, s0, sh, sl, ss); break;
+        case 3: fps_registers<3>(a, b, off, n, s0, sh, sl, ss); break;
+        case 4: fps_registers<4>(a, b, off, n, s0, sh, sl, ss); break;
+        case 5: fps_registers<5>(a, b, off, n, s0, sh, sl, ss); break;
+        case 6: fps_registers<6>(a, b, off, n, s0, sh, sl, ss); break;
+        case 7: fps_registers<7>(a, b, off, n, s0, sh, sl, ss); break;
+        case 8: fps_registers<8>(a, b, off, n, s0, sh, sl, ss); break;
+        case 9: case 10: fps_registers<10>(a, b, off, n, s0, sh, sl, ss); break;
+        case 11: case 12: fps_registers<12>(a, b, off, n, s0, sh, sl, ss); break;
+        case 13: case 14: fps_registers<14>(a, b, off, n, s0, sh, sl, ss); break;
+        default: fps_registers<16>(a, b, off, n, s0, sh, sl, ss); break;
     }
 }
 
-// FPS of one event of any size, state streamed from the workspace (min
-// distance) and from `assign` or the workspace (nearest slot) every
-// iteration.  Thread t owns pulses t, t+256, ...; the argmax resolves ties
-// by an explicit minimum over the index.
-__device__ void fps_streaming(const SampleArgs& a, int64_t b, int64_t off, int n, int s0) {
-    __shared__ FpsSlot slots[2][kFpsW];
+// FPS of one event of any size by one workgroup, state streamed from the
+// workspace (min distance) and from `assign` or the workspace (nearest slot)
+// every iteration.  Used only for events beyond kGangMax * kFpsCap pulses.
+// Thread t owns pulses t, t+256, ...; the argmax resolves ties by an
+// explicit minimum over the index.
+__device__ __forceinline__ void fps_streaming(const SampleArgs& a, int64_t b, int64_t off, int n, int s0,
+                              FpsSlot (*slots)[kFpsW], int* s_sel) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
@@ -358,10 +439,7 @@ __device__ void fps_streaming(const SampleArgs& a, int64_t b, int64_t off, int n
     int s = s0;
     float4 c = p[s];
     for (int j = 0; j < P; ++j) {
-        if (tid == 0) {
-            a.centroid_idx[b * P + j] = s;
-            a.centroids[b * P + j] = c;
-        }
+        if (tid == 0) s_sel[j] = s;
         mark_selected(selbits, s);
         float bv = -1.0f;
         int bi = 0x7fffffff;
@@ -396,23 +474,91 @@ __device__ void fps_streaming(const SampleArgs& a, int64_t b, int64_t off, int n
         FpsSlot sl;
         if (has) sl = slots[j & 1][lane];
         const int v = has ? __float_as_int(sl.v) : INT32_MIN;
-        int r = max(v, dpp_i<kQuadSwap1, 0xF>(v));
-        r = max(r, dpp_i<kQuadSwap2, 0xF>(r));
+        int r = max(v, dpp_i<kQuadSwap1, 0xF>(v, INT32_MIN));
+        r = max(r, dpp_i<kQuadSwap2, 0xF>(r, INT32_MIN));
         const float gm = __int_as_float(readlane_i(r, 0));
         const int gi = wave_min_i(has && v == __float_as_int(gm) ? sl.i : 0x7fffffff);
         s = gm == 0.0f ? first_unselected(selbits) : gi;
         s = min(max(s, 0), n - 1);
         c = p[s];
     }
+    write_selection(a, b, p, s_sel);
+}
+
+// Work list of the sample call, built by one workgroup of 1024 threads:
+// first every shard of every event that needs a gang (kFpsCap < n <=
+// kGangMax*kFpsCap; shards of one event consecutive), then one item per other
+// event.  Zeroes the gang records and the claim counter.
+__global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B) {
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    int carry = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int64_t base = 0; base < B; base += 1024) {
+            const int64_t b = base + tid;
+            int cnt = 0;
+            if (b < B) {
+                int64_t off;
+                int n;
+                event_range(a.offsets, a.N, b, off, n);
+                const bool gang = n > kFpsCap && n <= kGangMax * kFpsCap && n > a.P;
+                if (pass == 0 && gang) cnt = (n + kFpsCap - 1) / kFpsCap;
+                if (pass == 1 && !gang) cnt = 1;
+            }
+            const int incl = wave_incl_scan(cnt);
+            if (lane == 63) s_wsum[wave] = incl;
+            __syncthreads();
+            int wb = 0, total = 0;
+            for (int w = 0; w < 16; ++w) {
+                const int v = s_wsum[w];
+                if (w < wave) wb += v;
+                total += v;
+            }
+            const int pos = carry + wb + incl - cnt;
+            // malformed (overlapping) offsets could ask for more items than
+            // the list holds; those are dropped, never written out of bounds
+            const int64_t max_items = B + a.N / kFpsCap;
+            for (int q = 0; q < cnt && pos + q < max_items; ++q) {
+                a.item_ev[pos + q] = (int32_t)b;
+                a.item_g[pos + q] = q;
+                if (cnt > 1) {
+                    unsigned long long* r = a.gang_rec + (size_t)(pos + q) * 2 * kRecWords;
+                    for (int w = 0; w < 2 * kRecWords; ++w) r[w] = 0ull;
+                }
+            }
+            carry += total;
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        a.header[1] = (int)min((int64_t)carry, B + a.N / kFpsCap);  // items
+        a.header[2] = 0;      // claim counter
+        a.header[3] = 0;      // device error word
+    }
 }
 
 __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
-    const int64_t b = blockIdx.x;
+    __shared__ int s_item;
+    __shared__ FpsSlot s_slots[2][kFpsW];
+    __shared__ int s_sel[FPSTOK_MAX_SLOTS];
+    const int tid = threadIdx.x;
+    // items are claimed in list order, so the shards of one gang go to
+    // workgroups that start one after another: a gang whose workgroups wait
+    // for a partner only ever waits for a workgroup that will start once
+    // earlier, complete gangs or single events finish
+    if (tid == 0)
+        s_item = __hip_atomic_fetch_add(a.header + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= a.header[1]) return;
+    const int64_t b = a.item_ev[item];
+    const int g = a.item_g[item];
     int64_t off;
     int n;
     event_range(a.offsets, a.N, b, off, n);
     const int P = a.P;
-    const int tid = threadIdx.x;
     if (n <= P) {
         // small events keep one token per pulse
         for (int j = tid; j < P; j += kFpsT) {
@@ -430,11 +576,20 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
     }
     int s0 = a.start_idx ? a.start_idx[b] : 0;
     if (s0 < 0 || s0 >= n) s0 = 0;
-    if (n <= kFpsCap)
-        fps_registers_dispatch(a, b, off, n, s0);
-    else
-        fps_streaming(a, b, off, n, s0);
-    if (tid == 0) a.token_count[b] = P;
+    if (n <= kFpsCap) {
+        const Shard sh{0, n, 0, 1, nullptr, a.header + 3};
+        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel);
+    } else if (n <= kGangMax * kFpsCap) {
+        const int G = (n + kFpsCap - 1) / kFpsCap;
+        const int S = (n + G - 1) / G;
+        const int lo = g * S;
+        const Shard sh{lo, min(S, n - lo), g, G,
+                       a.gang_rec + (size_t)(item - g) * 2 * kRecWords, a.header + 3};
+        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel);
+    } else {
+        fps_streaming(a, b, off, n, s0, s_slots, s_sel);
+    }
+    if (tid == 0 && g == 0) a.token_count[b] = P;
 }
 
 // ------------------------------------------------------------------- assign
@@ -610,16 +765,20 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
 constexpr int kSortT = 256;
 constexpr int kSortW = kSortT / 64;
 constexpr int kMaxP = 1024;
+constexpr int kLdsPerm = 4096;  // events up to this size keep their permutation in LDS
+constexpr int kBatch = 8;       // members whose loads are issued together
 
 // Workgroup-wide stable counting sort of one event's pulses by slot:
 // perm[s_off[j] + r] = the r-th pulse (ascending) with asg = j.  Pulses whose
 // slot is outside [0, T) are left out.  Wave w handles the contiguous segment
 // [w*seg, (w+1)*seg); inside a 64-pulse tile the rank of a pulse among equal
 // slots comes from a bitwise ballot match, so the order is stable without
-// atomics.  Two passes: count per (wave, slot), then place.
+// atomics.  Two passes: count per (wave, slot), then place.  `perm` may point
+// to LDS or to device memory.
 //   s_cnt: LDS int[kSortW * kMaxP];  s_off: LDS int[kMaxP + 1]
-__device__ void block_sort_by_token(const int32_t* __restrict__ asg, int n, int T,
-                                    int32_t* __restrict__ perm, int* s_cnt, int* s_off) {
+__device__ __forceinline__ void block_sort_by_token(const int32_t* __restrict__ asg, int n, int T,
+                                                    int* __restrict__ perm, int* s_cnt,
+                                                    int* s_off) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
@@ -666,7 +825,6 @@ __device__ void block_sort_by_token(const int32_t* __restrict__ asg, int n, int 
                 tot[r] = t;
                 local += t;
             }
-            // block exclusive scan of `local`
             __shared__ int s_wsum[kSortW];
             const int incl = wave_incl_scan(local);
             if (lane == 63) s_wsum[wave] = incl;
@@ -697,12 +855,54 @@ __device__ void block_sort_by_token(const int32_t* __restrict__ asg, int n, int 
 
 // ------------------------------------------------------------ Lloyd update
 
-// One workgroup per event with n > P: stable sort by slot, then every slot's
-// charge-weighted mean in float64 over its members in ascending pulse order,
-// rounded to float32; a zero-weight slot keeps its centroid.
+// New centroids of one event's slots j = tid, tid+256, ... < T: the
+// charge-weighted mean of the members perm[s_off[j] .. s_off[j+1]) in that
+// (ascending pulse) order, float64, rounded to float32; a zero-weight slot
+// keeps its centroid.  Member loads are issued kBatch at a time.
+__device__ __forceinline__ void lloyd_slot_means(const LloydArgs& a, int64_t b, int64_t off, int T,
+                                                 const int* __restrict__ perm, const int* s_off) {
+    for (int j = threadIdx.x; j < T; j += kSortT) {
+        double W = 0.0, sx = 0.0, sy = 0.0, sz = 0.0, st = 0.0;
+        const int e = s_off[j + 1];
+        for (int m0 = s_off[j]; m0 < e; m0 += kBatch) {
+            int idx[kBatch];
+            float4 x[kBatch];
+            float w[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) idx[q] = m0 + q < e ? perm[m0 + q] : -1;
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                if (idx[q] >= 0) {
+                    x[q] = a.coords[off + idx[q]];
+                    w[q] = a.charge_col >= 0
+                               ? a.features[(off + idx[q]) * (int64_t)a.C + a.charge_col]
+                               : 1.0f;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                if (idx[q] >= 0) {
+                    const double wd = (double)w[q];
+                    W += wd;
+                    sx += wd * (double)x[q].x;
+                    sy += wd * (double)x[q].y;
+                    sz += wd * (double)x[q].z;
+                    st += wd * (double)x[q].w;
+                }
+            }
+        }
+        if (W > 0.0)
+            a.centroids[b * a.P + j] =
+                make_float4((float)(sx / W), (float)(sy / W), (float)(sz / W), (float)(st / W));
+    }
+}
+
+// One workgroup per event with n > P: stable sort by slot (permutation in
+// LDS when it fits), then every slot's charge-weighted mean.
 __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
     __shared__ int s_cnt[kSortW * kMaxP];
     __shared__ int s_off[kMaxP + 1];
+    __shared__ int s_perm[kLdsPerm];
     const int64_t b = blockIdx.x;
     int64_t off;
     int n;
@@ -711,26 +911,12 @@ __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
     int T = a.token_count[b];
     T = T > a.P ? a.P : T;
     if (T < 1) return;
-    block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
-    const int32_t* __restrict__ perm = a.perm + off;
-    for (int j = threadIdx.x; j < T; j += kSortT) {
-        double W = 0.0, sx = 0.0, sy = 0.0, sz = 0.0, st = 0.0;
-        const int e = s_off[j + 1];
-        for (int q = s_off[j]; q < e; ++q) {
-            const int i = perm[q];
-            const double w = a.charge_col >= 0
-                                 ? (double)a.features[(off + i) * (int64_t)a.C + a.charge_col]
-                                 : 1.0;
-            const float4 x = a.coords[off + i];
-            W += w;
-            sx += w * (double)x.x;
-            sy += w * (double)x.y;
-            sz += w * (double)x.z;
-            st += w * (double)x.w;
-        }
-        if (W > 0.0)
-            a.centroids[b * a.P + j] =
-                make_float4((float)(sx / W), (float)(sy / W), (float)(sz / W), (float)(st / W));
+    if (n <= kLdsPerm) {
+        block_sort_by_token(a.assign + off, n, T, s_perm, s_cnt, s_off);
+        lloyd_slot_means(a, b, off, T, s_perm, s_off);
+    } else {
+        block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
+        lloyd_slot_means(a, b, off, T, a.perm + off, s_off);
     }
 }
 
@@ -746,45 +932,105 @@ __device__ __forceinline__ void pool_write(const PoolArgs& a, int64_t b, int j, 
         if (q < nc) out[q] = W != 0.0 ? (float)(S[q] / W) : 0.0f;
 }
 
-// Voronoi pooling, one workgroup per event: stable sort by slot, then for
-// every slot the (weighted) mean of its members in ascending pulse order.
-__global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
-    __shared__ int s_cnt[kSortW * kMaxP];
-    __shared__ int s_off[kMaxP + 1];
-    const int64_t b = blockIdx.x;
-    int64_t off;
-    int n;
-    event_range(a.offsets, a.N, b, off, n);
-    int T = a.token_count[b];
-    T = T < 0 ? 0 : (T > a.P ? a.P : T);
-    if (T > 0) block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
-    const int32_t* __restrict__ perm = a.perm + off;
+// (Weighted) mean of columns [c0, c0+nc) over members given by `member(m)`
+// for m in [beg, end), in that order, float64; loads issued kBatch at a time.
+template <class Member>
+__device__ __forceinline__ void pool_slot(const PoolArgs& a, int64_t off, int beg, int end,
+                                          int c0, int nc, Member member, double& W, double* S) {
+    const int C = a.C;
+    W = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
+    for (int m0 = beg; m0 < end; m0 += kBatch) {
+        int idx[kBatch];
+        float w[kBatch];
+        float f[kBatch][kPoolCols];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) idx[q] = m0 + q < end ? member(m0 + q) : -1;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            if (idx[q] >= 0) {
+                const float* __restrict__ row = a.features + (off + idx[q]) * (int64_t)C;
+                w[q] = a.weight_col >= 0 ? row[a.weight_col] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < kPoolCols; ++c)
+                    if (c < nc) f[q][c] = row[c0 + c];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            if (idx[q] >= 0) {
+                const double wd = (double)w[q];
+                W += wd;
+#pragma unroll
+                for (int c = 0; c < kPoolCols; ++c)
+                    if (c < nc) S[c] += wd * (double)f[q][c];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void pool_slots_sorted(const PoolArgs& a, int64_t b, int64_t off,
+                                                  int T, const int* __restrict__ perm,
+                                                  const int* s_off) {
     const int C = a.C;
     for (int j = threadIdx.x; j < a.P; j += kSortT) {
         const int beg = j < T ? s_off[j] : 0;
         const int end = j < T ? s_off[j + 1] : 0;
         for (int c0 = 0; c0 < C; c0 += kPoolCols) {
             const int nc = min(kPoolCols, C - c0);
-            double W = 0.0;
-            double S[kPoolCols];
-#pragma unroll
-            for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
-            for (int m = beg; m < end; ++m) {
-                const float* __restrict__ f = a.features + (off + perm[m]) * (int64_t)C;
-                const double w = a.weight_col >= 0 ? (double)f[a.weight_col] : 1.0;
-                W += w;
-#pragma unroll
-                for (int q = 0; q < kPoolCols; ++q)
-                    if (q < nc) S[q] += w * (double)f[c0 + q];
-            }
+            double W, S[kPoolCols];
+            pool_slot(a, off, beg, end, c0, nc, [&](int m) { return perm[m]; }, W, S);
             pool_write(a, b, j, c0, nc, W, S);
         }
         if (a.cell_count) a.cell_count[b * a.P + j] = end - beg;
     }
 }
 
-// kNN pooling, one workgroup per event: every slot's list entries != -1 in
-// list order.
+// Voronoi pooling, one workgroup per event.  An event whose slots are the
+// identity (every pass-through event) pools each pulse on its own; otherwise
+// a stable sort by slot (permutation in LDS when it fits) and, for every
+// slot, the (weighted) mean of its members in ascending pulse order.
+__global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
+    __shared__ int s_cnt[kSortW * kMaxP];
+    __shared__ int s_off[kMaxP + 1];
+    __shared__ int s_perm[kLdsPerm];
+    const int64_t b = blockIdx.x;
+    int64_t off;
+    int n;
+    event_range(a.offsets, a.N, b, off, n);
+    int T = a.token_count[b];
+    T = T < 0 ? 0 : (T > a.P ? a.P : T);
+    const int tid = threadIdx.x;
+    bool ident = n == T;
+    for (int i = tid; ident && i < n; i += kSortT) ident = a.assign[off + i] == i;
+    if (__syncthreads_and(ident)) {
+        const int C = a.C;
+        for (int j = tid; j < a.P; j += kSortT) {
+            if (j < T) {
+                const float* __restrict__ row = a.features + (off + j) * (int64_t)C;
+                const double w = a.weight_col >= 0 ? (double)row[a.weight_col] : 1.0;
+                for (int c = 0; c < C; ++c)
+                    a.pooled[(b * a.P + j) * (int64_t)C + c] =
+                        w != 0.0 ? (float)((w * (double)row[c]) / w) : 0.0f;
+            } else {
+                for (int c = 0; c < C; ++c) a.pooled[(b * a.P + j) * (int64_t)C + c] = 0.0f;
+            }
+            if (a.cell_count) a.cell_count[b * a.P + j] = j < T ? 1 : 0;
+        }
+        return;
+    }
+    if (n <= kLdsPerm) {
+        block_sort_by_token(a.assign + off, n, T, s_perm, s_cnt, s_off);
+        pool_slots_sorted(a, b, off, T, s_perm, s_off);
+    } else {
+        block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
+        pool_slots_sorted(a, b, off, T, a.perm + off, s_off);
+    }
+}
+
+// kNN pooling, one workgroup per event: every slot's list entries that are
+// valid pulse indices, in list order.
 __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
     const int64_t b = blockIdx.x;
     int64_t off;
@@ -796,30 +1042,22 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
     const int k = a.k;
     for (int j = threadIdx.x; j < a.P; j += kSortT) {
         const int32_t* __restrict__ lst = a.knn_idx + (b * a.P + j) * (int64_t)k;
-        int count = 0;
+        const int len = j < T ? k : 0;
+        auto member = [&](int e) {
+            const int i = lst[e];
+            return i < n ? i : -1;
+        };
         for (int c0 = 0; c0 < C; c0 += kPoolCols) {
             const int nc = min(kPoolCols, C - c0);
-            double W = 0.0;
-            double S[kPoolCols];
-#pragma unroll
-            for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
-            count = 0;
-            if (j < T) {
-                for (int e = 0; e < k; ++e) {
-                    const int i = lst[e];
-                    if (i < 0 || i >= n) continue;
-                    const float* __restrict__ f = a.features + (off + i) * (int64_t)C;
-                    const double w = a.weight_col >= 0 ? (double)f[a.weight_col] : 1.0;
-                    W += w;
-                    ++count;
-#pragma unroll
-                    for (int q = 0; q < kPoolCols; ++q)
-                        if (q < nc) S[q] += w * (double)f[c0 + q];
-                }
-            }
+            double W, S[kPoolCols];
+            pool_slot(a, off, 0, len, c0, nc, member, W, S);
             pool_write(a, b, j, c0, nc, W, S);
         }
-        if (a.cell_count) a.cell_count[b * a.P + j] = count;
+        if (a.cell_count) {
+            int count = 0;
+            for (int e = 0; e < len; ++e) count += member(e) >= 0 ? 1 : 0;
+            a.cell_count[b * a.P + j] = count;
+        }
     }
 }
 
@@ -836,8 +1074,13 @@ hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
     return hipGetLastError();
 }
 
+int64_t sample_max_items(int64_t B, int64_t N) { return B + N / kFpsCap; }
+
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(sample_kernel, dim3(grid1(B)), dim3(kFpsT), 0, s, a);
+    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(1024), 0, s, a, B);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sample_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -228,7 +228,9 @@ class Tokenizer:
             centroid_idx=torch.empty((B, P), dtype=torch.int32, device=dev),
             centroids=torch.empty((B, P, 4), dtype=torch.float32, device=dev),
             token_count=torch.empty(B, dtype=torch.int32, device=dev),
-            assign=torch.empty(N, dtype=torch.int32, device=dev),
+            # the Voronoi slots are computed in Voronoi mode and for Lloyd
+            assign=torch.empty(N, dtype=torch.int32, device=dev)
+            if self.mode == VORONOI or lloyd_iters > 0 else None,
             knn_idx=torch.empty((B, P, k), dtype=torch.int32, device=dev)
             if self.mode == KNN else None,
             pooled=torch.empty((B, P, C), dtype=torch.float32, device=dev),
@@ -238,9 +240,8 @@ class Tokenizer:
 
     def __call__(self, start_idx=None, stream=None):
         o = self.out
-        need_assign = self.mode == VORONOI or self.pr.lloyd_iters > 0
         sample(self.bt, self.pr, o["centroid_idx"], o["centroids"], o["token_count"],
-               o["assign"] if need_assign else None, self.ws, start_idx, stream)
+               o["assign"], self.ws, start_idx, stream)
         if self.pr.lloyd_iters > 0:
             lloyd(self.bt, self.pr, o["centroids"], o["token_count"], o["assign"], self.ws,
                   stream)

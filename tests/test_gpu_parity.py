@@ -121,3 +121,51 @@ def test_repeatable_bit_for_bit():
     r2 = run_pipeline(b, 128, 0, 16, 3, True, 5)
     for key in r1:
         assert np.array_equal(r1[key], r2[key]), key
+
+
+def test_gang_and_streaming_paths(oracle_mod):
+    """Events split over several workgroups (4096 < n <= 262144) and one
+    beyond that (single-workgroup streaming path)."""
+    b = synth.icecube_events([4097, 8193, 20000, 262144, 300], 17, C=6)
+    check_pipeline(oracle_mod, b, P=256, mode=0, label="gangs")
+    b = synth.uniform_events([270000, 5000], 18, C=6)
+    check_pipeline(oracle_mod, b, P=64, mode=0, label="streaming")
+
+
+def test_graph_replay_matches_eager(oracle_mod):
+    """The whole tokenizer captured in a HIP graph: every replay (with eager
+    work and synchronizations in between) equals the eager result."""
+    import torch
+
+    from point_cloud_tokenization_amd import fpstok as F
+
+    for name in ("icecube_b64_voronoi", "icecube_b64_knn16", "icecube_b256_lloyd3"):
+        b = synth.make_batch(name, 77)
+        w = synth.WORKLOADS[name]
+        x, f, off = to_dev(b["coords"]), to_dev(b["features"]), to_dev(b["offsets"])
+        tok = F.Tokenizer(x, f, off, num_patches=w["P"],
+                          assign_mode="knn" if w["mode"] == 1 else "voronoi", k=w["k"],
+                          lloyd_iters=w["L"], pool="charge", charge_col=5)
+        ref = {k_: (to_np(v) if v is not None else None) for k_, v in tok().items()}
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            tok()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            tok()
+        for rep in range(4):
+            for v in tok.out.values():
+                if v is not None:
+                    v.fill_(-7)
+            scratch = torch.randn(1000, device=x.device).sum()  # eager work in between
+            g.replay()
+            torch.cuda.synchronize()
+            float(scratch)
+            for k_, v in tok.out.items():
+                if v is not None:
+                    assert np.array_equal(to_np(v), ref[k_]), (name, rep, k_)
+        log("graph replay ok: %s" % name)

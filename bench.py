@@ -201,6 +201,9 @@ def main():
     ap.add_argument("--secondary", type=int, default=1,
                     help="also time the other workloads (reported under 'secondary')")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times), "
+                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, and exit")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph",
                     help="graph: time replays of one captured step (default); eager: time "
                          "host-launched steps")
@@ -217,6 +220,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 5}), flush=True)
+        return
 
     b = synth.make_batch(args.workload)
     st = workload_stats(b)

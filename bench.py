@@ -61,8 +61,7 @@ def workload_stats(b):
 
 
 class Runner:
-    """Device-resident inputs, outputs and workspace for one workload, with the
-    per-call HIP events of the timed region."""
+    """Device-resident inputs, outputs and workspace for one workload."""
 
     def __init__(self, b):
         import torch
@@ -82,30 +81,30 @@ class Runner:
         self.calls = ["sample"] + (["lloyd"] if b["L"] > 0 else []) + \
                      (["knn"] if b["mode"] == 1 else []) + ["pool"]
 
-    def step(self, events=None):
+    def step(self):
+        """One step: the whole tokenizer, fpstok_tokenize."""
+        self.tok()
+
+    def stepwise(self, events):
+        """The five calls one after another, an event after each."""
         F, t, o = self.F, self.tok, self.tok.out
-
-        def mark(i):
-            if events is not None:
-                events[i].record()
-
-        mark(0)
+        events[0].record()
         F.sample(t.bt, t.pr, o["centroid_idx"], o["centroids"], o["token_count"], o["assign"],
                  t.ws)
         i = 1
-        mark(i)
+        events[i].record()
         if t.pr.lloyd_iters > 0:
             F.lloyd(t.bt, t.pr, o["centroids"], o["token_count"], o["assign"], t.ws)
             i += 1
-            mark(i)
+            events[i].record()
         if t.mode == F.KNN:
             F.knn(t.bt, t.pr, o["centroids"], o["token_count"], o["knn_idx"], t.ws)
             i += 1
-            mark(i)
+            events[i].record()
         F.pool(t.bt, t.pr, o["token_count"], o["assign"], o["knn_idx"], o["pooled"],
                o["cell_count"], t.ws)
         i += 1
-        mark(i)
+        events[i].record()
 
     def timed_graph(self, steps, warmup):
         """Whole steps captured once in a HIP graph and replayed: no host
@@ -135,26 +134,40 @@ class Runner:
         return time.perf_counter() - t0
 
     def timed(self, steps, warmup):
+        """K host-launched steps with a HIP event pair around each (on the
+        stream the kernels run on).  Returns (wall seconds, mean step seconds
+        on the GPU)."""
         import torch
 
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        ncalls = len(self.calls)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(steps):
-            self.step(evs[s])
+            evs[s][0].record()
+            self.step()
+            evs[s][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per_call = {c: 0.0 for c in self.calls}
+        gpu = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e-3 / steps
+        return wall, gpu
+
+    def per_call(self, steps):
+        """Mean duration of each of the five calls (stepwise path)."""
+        import torch
+
+        n = len(self.calls)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+        for s in range(steps):
+            self.stepwise(evs[s])
+        torch.cuda.synchronize()
+        out = {c: 0.0 for c in self.calls}
         for s in range(steps):
             for i, c in enumerate(self.calls):
-                per_call[c] += evs[s][i].elapsed_time(evs[s][i + 1]) * 1e-3
-        per_call = {c: v / steps for c, v in per_call.items()}
-        return wall, per_call
+                out[c] += evs[s][i].elapsed_time(evs[s][i + 1]) * 1e-3
+        return {c: v / steps for c, v in out.items()}
 
 
 def cpu_baseline(b, budget_s):
@@ -179,17 +192,12 @@ def cpu_baseline(b, budget_s):
                     reps, B, el))
 
 
-def roofline_for(call, st, seconds):
-    if call == "sample":
-        ops = st["point_iters"] * FPS_OPS_PER_POINT_ITER
-        ach = ops / seconds / 1e12
-        return dict(bound="alu", achieved=ach, peak=VALU_PEAK_TOPS, unit="TOP/s",
-                    frac=ach / VALU_PEAK_TOPS, traffic=None, kernel="sample_kernel (FPS)")
-    if call == "pool":
-        ach = st["pool_bytes"] / seconds / 1e9
-        return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=ach / HBM_PEAK_GBPS, traffic=None, kernel="pool_voronoi_kernel")
-    return None
+def fps_roofline(st, seconds, kernel):
+    """FPS algorithmic VALU lane-ops per launch over the launch duration."""
+    ops = st["point_iters"] * FPS_OPS_PER_POINT_ITER
+    ach = ops / seconds / 1e12
+    return dict(bound="alu", achieved=ach, peak=VALU_PEAK_TOPS, unit="TOP/s",
+                frac=ach / VALU_PEAK_TOPS, traffic=None, kernel=kernel)
 
 
 def main():
@@ -234,17 +242,22 @@ def main():
     st = workload_stats(b)
     log("workload %s: %s" % (args.workload, st))
     r = Runner(b)
-    # per-call kernel durations: HIP events on the kernels' stream between the
-    # calls of K host-launched steps
-    wall_eager, per_call = r.timed(args.steps, args.warmup)
+    # per-step GPU time: a HIP event pair around each of K host-launched
+    # steps, on the stream the kernels run on
+    wall_eager, step_gpu = r.timed(args.steps, args.warmup)
     wall = r.timed_graph(args.steps, args.warmup) if args.launch == "graph" else wall_eager
     ms = wall / args.steps * 1e3
     value = st["B"] * args.steps / wall
-    dom = max(per_call, key=per_call.get)
-    roof = roofline_for(dom, st, per_call[dom])
-    fps_rate = st["point_iters"] / per_call["sample"]
-    pool_gbps = st["pool_bytes"] / per_call["pool"] / 1e9
-    log("per-call kernel time (s): %s" % per_call)
+    per_call = r.per_call(max(10, args.steps // 4))
+    fused = b["mode"] == 0 and b["L"] == 0
+    # the dominant kernel of the step: the fused FPS + pooling kernel (one
+    # call = the work-list kernel + tokenize_kernel) in Voronoi mode without
+    # Lloyd, else fpstok_sample
+    roof = fps_roofline(st, step_gpu if fused else per_call["sample"],
+                        "tokenize_kernel (FPS + fused Voronoi pooling)" if fused
+                        else "sample_kernel (FPS)")
+    log("per-step GPU %.1f us; per call (stepwise) %s" % (
+        step_gpu * 1e6, {c: round(v * 1e6, 1) for c, v in per_call.items()}))
 
     secondary = {}
     if args.secondary:
@@ -255,11 +268,13 @@ def main():
             s2 = workload_stats(bb)
             steps = 20 if s2["N"] > 1_000_000 else 100
             rr = Runner(bb)
-            w2, pc2 = rr.timed(steps, 5)
+            w2, g2 = rr.timed(steps, 5)
             if args.launch == "graph":
                 w2 = rr.timed_graph(steps, 5)
+            pc2 = rr.per_call(max(5, steps // 4))
             secondary[name] = dict(
                 events_per_s=s2["B"] * steps / w2, ms_per_step=w2 / steps * 1e3,
+                step_gpu_us=g2 * 1e6,
                 per_call_us={c: v * 1e6 for c, v in pc2.items()},
                 fps_point_iters_per_s=s2["point_iters"] / pc2["sample"],
                 pool_GBps=s2["pool_bytes"] / pc2["pool"] / 1e9, B=s2["B"], N=s2["N"],
@@ -286,8 +301,8 @@ def main():
                    "lloyd_iters": b["L"], "pool": "charge" if b["weighted"] else "mean",
                    "seed": b["seed"], "launch": "hipGraph" if args.launch == "graph" else "eager"},
         "eager_events_per_s": st["B"] * args.steps / wall_eager,
-        "fps_point_iters_per_s": fps_rate,
-        "pool_hbm_GBps": pool_gbps,
+        "step_gpu_us": step_gpu * 1e6,
+        "fps_point_iters_per_s": st["point_iters"] / step_gpu,
         "per_call_us": {c: v * 1e6 for c, v in per_call.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -112,7 +112,8 @@ typedef struct {
 } fpstok_params;
 
 /* Bytes of device workspace every compute call of this batch shape needs
- * (depends on B and N only).  Host-only; never fails; 0 for B = 0. */
+ * (depends on B, N and num_patches; params may be NULL for the largest
+ * num_patches).  Host-only; never fails; 0 for B = 0. */
 size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_params* params);
 
 /* FPS of every event (farthest_point_sampling / _with_assign).  For n > P:
@@ -173,6 +174,21 @@ fpstok_status fpstok_pool(const fpstok_batch* batch, const fpstok_params* params
                           const int32_t* token_count, const int32_t* assign,
                           const int32_t* knn_idx, float* pooled, int32_t* cell_count, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* The whole tokenizer in one call: fpstok_sample, then fpstok_lloyd
+ * (lloyd_iters > 0), fpstok_knn (kNN mode), fpstok_pool, with the same
+ * results as calling them in that order (README of felixyu7/neptune, "How it
+ * works" step 1: FPS, Voronoi or kNN pooling, optional Lloyd).  In Voronoi mode without Lloyd the
+ * FPS and the pooling run in one kernel: each workgroup pools its event as
+ * soon as its sampling ends.  Outputs as in the calls above; `assign` is
+ * required in Voronoi mode and for Lloyd (else it may be NULL), `knn_idx` in
+ * kNN mode (else it may be NULL), `features` are always read.
+ * Errors: those of the calls it makes. */
+fpstok_status fpstok_tokenize(const fpstok_batch* batch, const fpstok_params* params,
+                              const int32_t* start_idx, int32_t* centroid_idx, float* centroids,
+                              int32_t* token_count, int32_t* assign, int32_t* knn_idx,
+                              float* pooled, int32_t* cell_count, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* Debug check of the data preconditions of `batch` (offsets monotone with
  * offsets[0] = 0 and offsets[B] = N, finite coords, charge >= 0 when

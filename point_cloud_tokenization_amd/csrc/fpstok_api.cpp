@@ -41,7 +41,7 @@ static fpstok_status hip_fail(hipError_t e, const char* what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WorkspaceLayout workspace_layout(int64_t B, int64_t N) {
+WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P) {
     WorkspaceLayout L{};
     if (B <= 0) return L;
     const int64_t nn = N > 0 ? N : 0;
@@ -66,6 +66,8 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N) {
     at += align256((size_t)L.max_items * sizeof(int32_t));
     L.gang_rec = at;
     at += align256((size_t)L.max_items * 12 * sizeof(unsigned long long));
+    L.shard_cells = at;
+    at += align256((size_t)L.max_items * (size_t)(P + 1) * sizeof(int32_t));
     L.total = at;
     return L;
 }
@@ -116,9 +118,9 @@ static fpstok_status check_common(const fpstok_batch* bt, const fpstok_params* p
     return FPSTOK_OK;
 }
 
-static fpstok_status check_ws(const fpstok_batch* bt, void* ws, size_t ws_bytes,
-                              WorkspaceLayout& L) {
-    L = workspace_layout(bt->num_events, bt->num_points);
+static fpstok_status check_ws(const fpstok_batch* bt, const fpstok_params* pr, void* ws,
+                              size_t ws_bytes, WorkspaceLayout& L) {
+    L = workspace_layout(bt->num_events, bt->num_points, pr->num_patches);
     if (L.total == 0) return FPSTOK_OK;
     if (!ws) return fail(FPSTOK_EWORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
     if (ws_bytes < L.total)
@@ -138,9 +140,10 @@ static T* at(void* ws, size_t off) {
 using namespace fpstok;
 
 FPSTOK_API size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_params* params) {
-    (void)params;
     if (!batch) return 0;
-    return workspace_layout(batch->num_events, batch->num_points).total;
+    int P = params ? params->num_patches : FPSTOK_MAX_PATCHES;
+    if (P < 1 || P > FPSTOK_MAX_PATCHES) P = FPSTOK_MAX_PATCHES;
+    return workspace_layout(batch->num_events, batch->num_points, P).total;
 }
 
 FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_params* pr,
@@ -155,7 +158,7 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
     if (((uintptr_t)centroids & 15u) != 0)
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
-    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     SampleArgs a{};
     a.coords = (const float4*)bt->coords;
     a.offsets = bt->offsets;
@@ -172,6 +175,7 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
     a.item_ev = at<int32_t>(ws, L.item_ev);
     a.item_g = at<int32_t>(ws, L.item_g);
     a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
+    a.shard_cells = at<int32_t>(ws, L.shard_cells);
     hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
     return ok();
@@ -188,7 +192,7 @@ FPSTOK_API fpstok_status fpstok_assign(const fpstok_batch* bt, const fpstok_para
     if (((uintptr_t)centroids & 15u) != 0)
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
-    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
@@ -222,7 +226,7 @@ FPSTOK_API fpstok_status fpstok_knn(const fpstok_batch* bt, const fpstok_params*
     if (((uintptr_t)centroids & 15u) != 0)
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
-    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     KnnArgs a{};
     a.coords = (const float4*)bt->coords;
     a.offsets = bt->offsets;
@@ -248,7 +252,7 @@ FPSTOK_API fpstok_status fpstok_lloyd(const fpstok_batch* bt, const fpstok_param
     if (((uintptr_t)centroids & 15u) != 0)
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
-    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
@@ -298,7 +302,7 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
     if (pr->assign_mode == FPSTOK_KNN && !knn_idx)
         return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
     WorkspaceLayout L;
-    if ((st = check_ws(bt, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     PoolArgs a{};
     a.features = bt->features;
     a.offsets = bt->offsets;
@@ -317,6 +321,74 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
                        ? launch_pool_voronoi(a, bt->num_events, (hipStream_t)stream)
                        : launch_pool_knn(a, bt->num_events, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
+                                         const int32_t* start_idx, int32_t* centroid_idx,
+                                         float* centroids, int32_t* token_count, int32_t* assign,
+                                         int32_t* knn_idx, float* pooled, int32_t* cell_count,
+                                         void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, true, true);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    if (!centroid_idx || !centroids || !token_count || !pooled)
+        return fail(FPSTOK_EINVAL, "centroid_idx, centroids, token_count and pooled are required");
+    if (((uintptr_t)centroids & 15u) != 0)
+        return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
+    const bool voronoi = pr->assign_mode == FPSTOK_VORONOI;
+    if ((voronoi || pr->lloyd_iters > 0) && !assign && bt->num_points > 0)
+        return fail(FPSTOK_EINVAL, "assign is required in Voronoi mode and for Lloyd");
+    if (!voronoi && !knn_idx) return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    if (!voronoi || pr->lloyd_iters > 0) {
+        // the calls one after another on the same stream and workspace
+        if ((st = fpstok_sample(bt, pr, start_idx, centroid_idx, centroids, token_count, assign,
+                                ws, ws_bytes, stream)) != FPSTOK_OK)
+            return st;
+        if ((st = fpstok_lloyd(bt, pr, centroids, token_count, assign, ws, ws_bytes, stream)) !=
+            FPSTOK_OK)
+            return st;
+        if (!voronoi && (st = fpstok_knn(bt, pr, centroids, token_count, knn_idx, ws, ws_bytes,
+                                         stream)) != FPSTOK_OK)
+            return st;
+        return fpstok_pool(bt, pr, token_count, assign, knn_idx, pooled, cell_count, ws, ws_bytes,
+                           stream);
+    }
+    SampleArgs a{};
+    a.coords = (const float4*)bt->coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.start_idx = start_idx;
+    a.centroid_idx = centroid_idx;
+    a.centroids = (float4*)centroids;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.ws_mind = at<float>(ws, L.mind);
+    a.ws_near = at<int32_t>(ws, L.near);
+    a.header = at<int32_t>(ws, L.header);
+    a.item_ev = at<int32_t>(ws, L.item_ev);
+    a.item_g = at<int32_t>(ws, L.item_g);
+    a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
+    a.shard_cells = at<int32_t>(ws, L.shard_cells);
+    PoolArgs p{};
+    p.features = bt->features;
+    p.offsets = bt->offsets;
+    p.N = bt->num_points;
+    p.C = bt->num_features;
+    p.weight_col = pr->pool_weighted ? bt->charge_col : -1;
+    p.P = pr->num_patches;
+    p.k = pr->k;
+    p.token_count = token_count;
+    p.assign = assign;
+    p.knn_idx = nullptr;
+    p.pooled = pooled;
+    p.cell_count = cell_count;
+    p.perm = at<int32_t>(ws, L.perm);
+    hipError_t e = launch_tokenize(a, p, bt->num_events, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "tokenize kernel launch");
     return ok();
 }
 

@@ -24,12 +24,13 @@ struct WorkspaceLayout {
     size_t item_ev;     // int32[max_items]: FPS work items (event)
     size_t item_g;      // int32[max_items]: FPS work items (shard)
     size_t gang_rec;    // uint64[max_items][12]: gang exchange records
+    size_t shard_cells; // int32[max_items][P+1]: per-shard slot offsets (fused pooling)
     size_t total;
     int64_t max_chunks;
     int64_t max_items;
 };
 
-WorkspaceLayout workspace_layout(int64_t B, int64_t N);
+WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P);
 int64_t sample_max_items(int64_t B, int64_t N);
 
 struct SampleArgs {
@@ -48,6 +49,7 @@ struct SampleArgs {
     int32_t* item_ev;               // [max_items] event of each work item
     int32_t* item_g;                // [max_items] shard of each work item
     unsigned long long* gang_rec;   // [max_items][2][6] gang records
+    int32_t* shard_cells;           // [max_items][P+1] per-shard slot offsets (fused pooling)
 };
 
 struct AssignArgs {
@@ -108,6 +110,7 @@ struct PoolArgs {
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
                        const WorkspaceLayout& L, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s);
 hipError_t launch_assign(const AssignArgs& a, int64_t max_chunks, hipStream_t s);
 hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s);

@@ -203,31 +203,6 @@ struct Shard {
     int32_t* err;              // device error word (bounded wait exceeded)
 };
 
-// Workgroup-level argmax over the per-wave candidates written to `slots`:
-// the largest value, then the lowest wave (waves hold increasing index
-// ranges, so this is the lowest pulse index).  Values are compared as the
-// int32 bit patterns of floats in {-1} U [0, inf], whose order they keep.
-// Returns the winning slot uniformly.
-__device__ __forceinline__ FpsSlot reduce_slots_blocked(const FpsSlot* slots) {
-    const int lane = lane_id();
-    const bool has = lane < kFpsW;
-    FpsSlot s;
-    if (has) s = slots[lane];
-    const int v = has ? __float_as_int(s.v) : INT32_MIN;
-    int r = max(v, dpp_i<kQuadSwap1, 0xF>(v, INT32_MIN));
-    r = max(r, dpp_i<kQuadSwap2, 0xF>(r, INT32_MIN));
-    const int gm = readlane_i(r, 0);
-    const int L = (int)__builtin_ctzll(ballot(has && v == gm));
-    FpsSlot out;
-    out.v = __int_as_float(gm);
-    out.i = readlane_i(s.i, L);
-    out.c.x = readlane_f(s.c.x, L);
-    out.c.y = readlane_f(s.c.y, L);
-    out.c.z = readlane_f(s.c.z, L);
-    out.c.w = readlane_f(s.c.w, L);
-    return out;
-}
-
 __device__ __forceinline__ unsigned long long tagged(int j, uint32_t payload) {
     return ((unsigned long long)(uint32_t)(j + 1) << 32) | payload;
 }
@@ -304,12 +279,16 @@ __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
 //
 // Per pulse and iteration: the float32 distance to the newest centroid (11
 // VALU ops), the fused Voronoi update (compare + 2 selects) and the lane's
-// running (first) maximum (compare, select, max).  Minimum distances are
-// float32 values in {-1} U [0, inf] (-1 marks padding), compared as int32
-// bit patterns, whose order they keep.  The wave's argmax is then the lowest
-// lane holding the wave maximum (one ballot), its pulse is that lane's first
-// maximum, and the pulse's coordinates are read from the lane's registers
-// with a uniform index.
+// running first maximum with its pulse (compare, max, 5 selects).  Minimum
+// distances are float32 values in {-1} U [0, inf] (-1 marks padding),
+// compared as int32 bit patterns, whose order they keep.
+//
+// One iteration's argmax: a DPP wave maximum; the lowest lane holding it
+// (one ballot) gives the wave's candidate, which lane 0 writes to an LDS slot;
+// after the barrier every lane reads the kFpsW slots (broadcast reads) and
+// keeps the largest, lowest wave on ties, with plain compares and selects.
+// The centroid therefore stays in VGPRs and no value travels back through a
+// scalar register between the barrier and the next update.
 //
 // Selected pulses are not marked: a selected pulse has min distance exactly
 // 0, so while the maximum is > 0 it cannot win; when the maximum is 0 every
@@ -322,7 +301,7 @@ __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
 template <int M>
 __device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n,
                                               int s0, const Shard& sh, FpsSlot (*slots)[kFpsW],
-                                              int* s_sel) {
+                                              int* s_sel, int* s_asg) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
@@ -353,7 +332,8 @@ __device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, in
         if (tid == 0) s_sel[j] = s;
         mark_selected(selbits, s);
         int bv = INT32_MIN;
-        int bk = 0;
+        int bi = 0;
+        float bx = 0.f, by = 0.f, bz = 0.f, bt = 0.f;
 #pragma unroll
         for (int k = 0; k < M; ++k) {
             const float d = sqd(px[k], py[k], pz[k], pt[k], c.x, c.y, c.z, c.w);
@@ -361,19 +341,21 @@ __device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, in
             nr[k] = u ? j : nr[k];
             md[k] = u ? d : md[k];
             const int mi = __float_as_int(md[k]);
-            bk = mi > bv ? k : bk;
-            bv = max(bv, mi);
+            const bool g = mi > bv;
+            bv = g ? mi : bv;
+            bi = g ? k : bi;
+            bx = g ? px[k] : bx;
+            by = g ? py[k] : by;
+            bz = g ? pz[k] : bz;
+            bt = g ? pt[k] : bt;
         }
         if (j + 1 == P) break;
 
         const int wm = wave_max_i(bv);
         const int L = (int)__builtin_ctzll(ballot(bv == wm));
-        const int ks = readlane_i(bk, L);
-        // the indexed register reads are per-lane moves: they run with every
-        // lane active, before the single-lane slot write
-        const float4 wc = make_float4(readlane_f(px[ks], L), readlane_f(py[ks], L),
-                                      readlane_f(pz[ks], L), readlane_f(pt[ks], L));
-        const int wi = readlane_i(lbase, L) + ks;
+        const int wi = readlane_i(lbase + bi, L);
+        const float4 wc = make_float4(readlane_f(bx, L), readlane_f(by, L), readlane_f(bz, L),
+                                      readlane_f(bt, L));
         if (lane == 0) {
             FpsSlot& o = slots[j & 1][wave];
             o.v = __int_as_float(wm);
@@ -381,7 +363,19 @@ __device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, in
             o.c = wc;
         }
         __syncthreads();
-        FpsSlot g = reduce_slots_blocked(slots[j & 1]);
+        const FpsSlot* sl = slots[j & 1];
+        FpsSlot g = sl[0];
+#pragma unroll
+        for (int w = 1; w < kFpsW; ++w) {
+            const FpsSlot o = sl[w];
+            const bool better = __float_as_int(o.v) > __float_as_int(g.v);
+            g.v = better ? o.v : g.v;
+            g.i = better ? o.i : g.i;
+            g.c.x = better ? o.c.x : g.c.x;
+            g.c.y = better ? o.c.y : g.c.y;
+            g.c.z = better ? o.c.z : g.c.z;
+            g.c.w = better ? o.c.w : g.c.w;
+        }
         if (sh.G > 1) g = gang_exchange(g, sh, j);
         if (g.v == 0.0f) {
             s = min(first_unselected(selbits), n - 1);
@@ -398,25 +392,33 @@ __device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, in
             if (i < send) a.assign[off + i] = nr[k];
         }
     }
+    if (s_asg) {
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int i = lbase + k;
+            if (i < send) s_asg[i - sh.lo] = nr[k];
+        }
+    }
     if (sh.g == 0) write_selection(a, b, p, s_sel);
 }
 
 // Register-resident FPS for m = ceil(shard / 256) pulses per thread.
 __device__ __forceinline__ void fps_registers_dispatch(const SampleArgs& a, int64_t b, int64_t off, int n,
-                                       int s0, const Shard& sh, FpsSlot (*sl)[kFpsW], int* ss) {
+                                       int s0, const Shard& sh, FpsSlot (*sl)[kFpsW], int* ss,
+                                       int* sa) {
     switch ((sh.cnt + kFpsT - 1) / kFpsT) {
-        case 1: fps_registers<1>(a, b, off, n, s0, sh, sl, ss); break;
-        case 2: fps_registers<2>(a, b, off, n, s0, sh, sl, ss); break;
-        case 3: fps_registers<3>(a, b, off, n, s0, sh, sl, ss); break;
-        case 4: fps_registers<4>(a, b, off, n, s0, sh, sl, ss); break;
-        case 5: fps_registers<5>(a, b, off, n, s0, sh, sl, ss); break;
-        case 6: fps_registers<6>(a, b, off, n, s0, sh, sl, ss); break;
-        case 7: fps_registers<7>(a, b, off, n, s0, sh, sl, ss); break;
-        case 8: fps_registers<8>(a, b, off, n, s0, sh, sl, ss); break;
-        case 9: case 10: fps_registers<10>(a, b, off, n, s0, sh, sl, ss); break;
-        case 11: case 12: fps_registers<12>(a, b, off, n, s0, sh, sl, ss); break;
-        case 13: case 14: fps_registers<14>(a, b, off, n, s0, sh, sl, ss); break;
-        default: fps_registers<16>(a, b, off, n, s0, sh, sl, ss); break;
+        case 1: fps_registers<1>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 2: fps_registers<2>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 3: fps_registers<3>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 4: fps_registers<4>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 5: fps_registers<5>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 6: fps_registers<6>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 7: fps_registers<7>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 8: fps_registers<8>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 9: case 10: fps_registers<10>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 11: case 12: fps_registers<12>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 13: case 14: fps_registers<14>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        default: fps_registers<16>(a, b, off, n, s0, sh, sl, ss, sa); break;
     }
 }
 
@@ -539,25 +541,44 @@ __global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B)
     }
 }
 
-__global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
-    __shared__ int s_item;
-    __shared__ FpsSlot s_slots[2][kFpsW];
-    __shared__ int s_sel[FPSTOK_MAX_SLOTS];
+// What one workgroup did for its work item, for the fused pooling that may
+// follow.
+struct ItemInfo {
+    int64_t b;    // event (-1: no item)
+    int64_t off;  // first row of the event
+    int n;        // pulses of the event
+    int kind;     // 0 pass-through, 1 single workgroup, 2 gang shard, 3 streaming
+    int g, G;     // shard and shards (gangs)
+    int lo, cnt;  // the shard's pulses
+    int item0;    // work item of shard 0 (gangs)
+};
+
+// Claim one work item and run FPS (or pass-through) for it.  s_asg, when not
+// null, receives the shard's Voronoi slots (register-resident paths only).
+__device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item,
+                                                FpsSlot (*s_slots)[kFpsW], int* s_sel,
+                                                int* s_asg) {
     const int tid = threadIdx.x;
+    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0};
     // items are claimed in list order, so the shards of one gang go to
     // workgroups that start one after another: a gang whose workgroups wait
     // for a partner only ever waits for a workgroup that will start once
     // earlier, complete gangs or single events finish
     if (tid == 0)
-        s_item = __hip_atomic_fetch_add(a.header + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_item = __hip_atomic_fetch_add(a.header + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int item = s_item;
-    if (item >= a.header[1]) return;
+    const int item = *s_item;
+    if (item >= a.header[1]) return it;
     const int64_t b = a.item_ev[item];
     const int g = a.item_g[item];
     int64_t off;
     int n;
     event_range(a.offsets, a.N, b, off, n);
+    it.b = b;
+    it.off = off;
+    it.n = n;
+    it.g = g;
+    it.item0 = item - g;
     const int P = a.P;
     if (n <= P) {
         // small events keep one token per pulse
@@ -572,24 +593,42 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
             }
         }
         if (tid == 0) a.token_count[b] = n;
-        return;
+        it.kind = 0;
+        it.cnt = n;
+        return it;
     }
     int s0 = a.start_idx ? a.start_idx[b] : 0;
     if (s0 < 0 || s0 >= n) s0 = 0;
     if (n <= kFpsCap) {
         const Shard sh{0, n, 0, 1, nullptr, a.header + 3};
-        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel);
+        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel, s_asg);
+        it.kind = 1;
+        it.cnt = n;
     } else if (n <= kGangMax * kFpsCap) {
         const int G = (n + kFpsCap - 1) / kFpsCap;
         const int S = (n + G - 1) / G;
         const int lo = g * S;
         const Shard sh{lo, min(S, n - lo), g, G,
                        a.gang_rec + (size_t)(item - g) * 2 * kRecWords, a.header + 3};
-        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel);
+        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel, s_asg);
+        it.kind = 2;
+        it.G = G;
+        it.lo = lo;
+        it.cnt = sh.cnt;
     } else {
         fps_streaming(a, b, off, n, s0, s_slots, s_sel);
+        it.kind = 3;
+        it.cnt = n;
     }
     if (tid == 0 && g == 0) a.token_count[b] = P;
+    return it;
+}
+
+__global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
+    __shared__ int s_item;
+    __shared__ FpsSlot s_slots[2][kFpsW];
+    __shared__ int s_sel[FPSTOK_MAX_SLOTS];
+    sample_item(a, &s_item, s_slots, s_sel, nullptr);
 }
 
 // ------------------------------------------------------------------- assign
@@ -935,12 +974,10 @@ __device__ __forceinline__ void pool_write(const PoolArgs& a, int64_t b, int j, 
 // (Weighted) mean of columns [c0, c0+nc) over members given by `member(m)`
 // for m in [beg, end), in that order, float64; loads issued kBatch at a time.
 template <class Member>
-__device__ __forceinline__ void pool_slot(const PoolArgs& a, int64_t off, int beg, int end,
-                                          int c0, int nc, Member member, double& W, double* S) {
+__device__ __forceinline__ void pool_slot_acc(const PoolArgs& a, int64_t off, int beg, int end,
+                                              int c0, int nc, Member member, double& W,
+                                              double* S) {
     const int C = a.C;
-    W = 0.0;
-#pragma unroll
-    for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
     for (int m0 = beg; m0 < end; m0 += kBatch) {
         int idx[kBatch];
         float w[kBatch];
@@ -970,6 +1007,15 @@ __device__ __forceinline__ void pool_slot(const PoolArgs& a, int64_t off, int be
     }
 }
 
+template <class Member>
+__device__ __forceinline__ void pool_slot(const PoolArgs& a, int64_t off, int beg, int end,
+                                          int c0, int nc, Member member, double& W, double* S) {
+    W = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
+    pool_slot_acc(a, off, beg, end, c0, nc, member, W, S);
+}
+
 __device__ __forceinline__ void pool_slots_sorted(const PoolArgs& a, int64_t b, int64_t off,
                                                   int T, const int* __restrict__ perm,
                                                   const int* s_off) {
@@ -984,6 +1030,24 @@ __device__ __forceinline__ void pool_slots_sorted(const PoolArgs& a, int64_t b, 
             pool_write(a, b, j, c0, nc, W, S);
         }
         if (a.cell_count) a.cell_count[b * a.P + j] = end - beg;
+    }
+}
+
+// Pooling of an event whose slot j is pulse j alone (j < T): each pulse's
+// features through the general formula (w f / w, exact for w != 0).
+__device__ __forceinline__ void pool_identity(const PoolArgs& a, int64_t b, int64_t off, int T) {
+    const int C = a.C;
+    for (int j = threadIdx.x; j < a.P; j += blockDim.x) {
+        if (j < T) {
+            const float* __restrict__ row = a.features + (off + j) * (int64_t)C;
+            const double w = a.weight_col >= 0 ? (double)row[a.weight_col] : 1.0;
+            for (int c = 0; c < C; ++c)
+                a.pooled[(b * a.P + j) * (int64_t)C + c] =
+                    w != 0.0 ? (float)((w * (double)row[c]) / w) : 0.0f;
+        } else {
+            for (int c = 0; c < C; ++c) a.pooled[(b * a.P + j) * (int64_t)C + c] = 0.0f;
+        }
+        if (a.cell_count) a.cell_count[b * a.P + j] = j < T ? 1 : 0;
     }
 }
 
@@ -1005,19 +1069,7 @@ __global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
     bool ident = n == T;
     for (int i = tid; ident && i < n; i += kSortT) ident = a.assign[off + i] == i;
     if (__syncthreads_and(ident)) {
-        const int C = a.C;
-        for (int j = tid; j < a.P; j += kSortT) {
-            if (j < T) {
-                const float* __restrict__ row = a.features + (off + j) * (int64_t)C;
-                const double w = a.weight_col >= 0 ? (double)row[a.weight_col] : 1.0;
-                for (int c = 0; c < C; ++c)
-                    a.pooled[(b * a.P + j) * (int64_t)C + c] =
-                        w != 0.0 ? (float)((w * (double)row[c]) / w) : 0.0f;
-            } else {
-                for (int c = 0; c < C; ++c) a.pooled[(b * a.P + j) * (int64_t)C + c] = 0.0f;
-            }
-            if (a.cell_count) a.cell_count[b * a.P + j] = j < T ? 1 : 0;
-        }
+        pool_identity(a, b, off, T);
         return;
     }
     if (n <= kLdsPerm) {
@@ -1061,6 +1113,111 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
     }
 }
 
+// ------------------------------------------- fused FPS + Voronoi pooling
+
+// Tokenizer in one launch for Voronoi mode without Lloyd: every workgroup
+// claims a work item, runs FPS (or pass-through) and then pools its event
+// while other workgroups are still sampling.
+//  * pass-through: each pulse pooled on its own;
+//  * one workgroup: the slots it just computed are sorted in LDS (stable, so
+//    each slot's members stay in ascending order) and pooled;
+//  * a gang: every shard sorts its own pulses, publishes its member lists
+//    (event-local indices in the workspace permutation, and its per-slot
+//    offsets), raises a tagged flag, waits for all shards, and then pools the
+//    slots j = g, g+G, ... by walking the shards in order -- again ascending
+//    pulse order;
+//  * streaming (beyond gang size): a workgroup-wide sort in device memory.
+// Dynamic LDS: s_cnt[kSortW*P], s_off[P+1], s_asg[kFpsCap], s_perm[kFpsCap].
+__global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs pa) {
+    __shared__ int s_item;
+    __shared__ FpsSlot s_slots[2][kFpsW];
+    __shared__ int s_sel[FPSTOK_MAX_SLOTS];
+    extern __shared__ int s_dyn[];
+    const int P = a.P;
+    int* s_cnt = s_dyn;
+    int* s_off = s_cnt + kSortW * P;
+    int* s_asg = s_off + P + 1;
+    int* s_perm = s_asg + kFpsCap;
+    const ItemInfo it = sample_item(a, &s_item, s_slots, s_sel, s_asg);
+    if (it.b < 0) return;
+    const int64_t b = it.b;
+    const int64_t off = it.off;
+    const int tid = threadIdx.x;
+    const int C = pa.C;
+    if (it.kind == 0) {
+        pool_identity(pa, b, off, it.n);
+        return;
+    }
+    if (it.kind == 3) {
+        __syncthreads();
+        block_sort_by_token(a.assign + off, it.n, P, pa.perm + off, s_cnt, s_off);
+        pool_slots_sorted(pa, b, off, P, pa.perm + off, s_off);
+        return;
+    }
+    __syncthreads();
+    block_sort_by_token(s_asg, it.cnt, P, s_perm, s_cnt, s_off);
+    if (it.kind == 1) {
+        pool_slots_sorted(pa, b, off, P, s_perm, s_off);
+        return;
+    }
+    // gang: publish this shard's member lists
+    int32_t* __restrict__ gperm = pa.perm + off;
+    int32_t* __restrict__ cells = a.shard_cells + (size_t)(it.item0 + it.g) * (P + 1);
+    for (int m = tid; m < it.cnt; m += kFpsT) gperm[it.lo + m] = it.lo + s_perm[m];
+    for (int j = tid; j <= P; j += kFpsT) cells[j] = s_off[j];
+    __threadfence();
+    __syncthreads();
+    // the flag is word 0 of this shard's record of parity (P-1)&1, tag P+1:
+    // every exchange of the FPS loop has completed, so that buffer is free
+    unsigned long long* rec = a.gang_rec + (size_t)it.item0 * 2 * kRecWords;
+    const int par = (P - 1) & 1;
+    if (tid == 0)
+        __hip_atomic_store(rec + ((size_t)it.g * 2 + par) * kRecWords, tagged(P, 0u),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    {
+        const int lane = lane_id();
+        const uint32_t want = (uint32_t)(P + 1);
+        for (uint32_t spin = 0;; ++spin) {
+            bool ok = true;
+            for (int q = lane; q < it.G; q += 64) {
+                const unsigned long long w = __hip_atomic_load(
+                    rec + ((size_t)q * 2 + par) * kRecWords, __ATOMIC_RELAXED,
+                    __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (uint32_t)(w >> 32) == want;
+            }
+            if (ballot(!ok) == 0) break;
+            if (spin >= kSpinLimit) {
+                if (lane == 0)
+                    __hip_atomic_store(a.header + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __threadfence();
+    const int32_t* __restrict__ cells0 = a.shard_cells + (size_t)it.item0 * (P + 1);
+    const int S = (it.n + it.G - 1) / it.G;  // shard size; shard sh starts at sh*S
+    for (int j = it.g + it.G * tid; j < P; j += it.G * kFpsT) {
+        int count = 0;
+        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+            const int nc = min(kPoolCols, C - c0);
+            double W = 0.0, Sx[kPoolCols];
+#pragma unroll
+            for (int q = 0; q < kPoolCols; ++q) Sx[q] = 0.0;
+            count = 0;
+            for (int sh = 0; sh < it.G; ++sh) {
+                const int32_t* cs = cells0 + (size_t)sh * (P + 1);
+                const int beg = cs[j], end = cs[j + 1];
+                count += end - beg;
+                const int32_t* __restrict__ sp = gperm + sh * S;
+                pool_slot_acc(pa, off, beg, end, c0, nc, [&](int m) { return sp[m]; }, W, Sx);
+            }
+            pool_write(pa, b, j, c0, nc, W, Sx);
+        }
+        if (pa.cell_count) pa.cell_count[b * P + j] = count;
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline unsigned grid1(int64_t x) { return (unsigned)(x < 1 ? 1 : x); }
@@ -1081,6 +1238,16 @@ hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sample_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s) {
+    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(1024), 0, s, a, B);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = sizeof(int) * ((size_t)kSortW * a.P + a.P + 1 + 2 * (size_t)kFpsCap);
+    hipLaunchKernelGGL(tokenize_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), lds, s,
+                       a, pa);
     return hipGetLastError();
 }
 

@@ -63,9 +63,10 @@ def lib():
         L.fpstok_knn.argtypes = [B, Pp, vp, vp, vp, vp, sz, vp]
         L.fpstok_lloyd.argtypes = [B, Pp, vp, vp, vp, vp, sz, vp]
         L.fpstok_pool.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_tokenize.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fpstok_validate.argtypes = [B, vp]
         for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
-                  "fpstok_pool", "fpstok_validate"):
+                  "fpstok_pool", "fpstok_tokenize", "fpstok_validate"):
             getattr(L, f).restype = ctypes.c_int
         L.fpstok_status_string.argtypes = [ctypes.c_int]
         L.fpstok_status_string.restype = ctypes.c_char_p
@@ -190,6 +191,15 @@ def pool(bt, pr, token_count, assign_, knn_idx, pooled, cell_count, ws, stream=N
                              _ptr(ws), ws.numel(), _stream_handle(stream)), "fpstok_pool")
 
 
+def tokenize_call(bt, pr, centroid_idx, centroids, token_count, assign_, knn_idx, pooled,
+                  cell_count, ws, start_idx=None, stream=None):
+    """fpstok_tokenize: the whole tokenizer in one call."""
+    _check(lib().fpstok_tokenize(ctypes.byref(bt), ctypes.byref(pr), _ptr(start_idx),
+                                 _ptr(centroid_idx), _ptr(centroids), _ptr(token_count),
+                                 _ptr(assign_), _ptr(knn_idx), _ptr(pooled), _ptr(cell_count),
+                                 _ptr(ws), ws.numel(), _stream_handle(stream)), "fpstok_tokenize")
+
+
 def validate(bt, stream=None):
     _check(lib().fpstok_validate(ctypes.byref(bt), _stream_handle(stream)), "fpstok_validate")
 
@@ -239,6 +249,15 @@ class Tokenizer:
         self.ws = alloc_workspace(self.bt, self.pr, dev)
 
     def __call__(self, start_idx=None, stream=None):
+        """fpstok_tokenize on the preallocated buffers."""
+        o = self.out
+        tokenize_call(self.bt, self.pr, o["centroid_idx"], o["centroids"], o["token_count"],
+                      o["assign"], o["knn_idx"], o["pooled"], o["cell_count"], self.ws,
+                      start_idx, stream)
+        return o
+
+    def stepwise(self, start_idx=None, stream=None):
+        """The same result through the five separate calls."""
         o = self.out
         sample(self.bt, self.pr, o["centroid_idx"], o["centroids"], o["token_count"],
                o["assign"], self.ws, start_idx, stream)

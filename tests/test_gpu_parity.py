@@ -169,3 +169,57 @@ def test_graph_replay_matches_eager(oracle_mod):
                 if v is not None:
                     assert np.array_equal(to_np(v), ref[k_]), (name, rep, k_)
         log("graph replay ok: %s" % name)
+
+
+def _tokenize_vs_oracle(oracle_mod, b, P, mode=0, k=16, L=0, weighted=True, charge_col=5,
+                        stepwise=False, label=""):
+    """fpstok_tokenize (or the five calls) against oracle.tokenize."""
+    from point_cloud_tokenization_amd import fpstok as F
+    from tests.gpu_util import assert_close_scaled, member_scale
+
+    log("tokenize case %s: B=%d N=%d P=%d mode=%d L=%d stepwise=%d" % (
+        label, b["offsets"].size - 1, b["coords"].shape[0], P, mode, L, stepwise))
+    x, f, off = to_dev(b["coords"]), to_dev(b["features"]), to_dev(b["offsets"])
+    tok = F.Tokenizer(x, f, off, num_patches=P, assign_mode="knn" if mode else "voronoi", k=k,
+                      lloyd_iters=L, pool="charge" if weighted else "mean", charge_col=charge_col)
+    out = tok.stepwise() if stepwise else tok()
+    got = {key: to_np(v) for key, v in out.items() if v is not None}
+    ref = oracle_mod.tokenize(b["coords"], b["features"], b["offsets"], P=P, mode=mode, k=k, L=L,
+                              weighted=weighted, charge_col=charge_col)
+    for key in ("token_count", "centroid_idx", "cell_count"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key + " " + label)
+    if mode == 0 or L > 0:
+        np.testing.assert_array_equal(got["assign"], ref["assign"], err_msg="assign " + label)
+    if mode == 1:
+        np.testing.assert_array_equal(got["knn_idx"], ref["knn_idx"], err_msg="knn " + label)
+    w = b["features"][:, charge_col] if (weighted and charge_col >= 0) else \
+        np.ones(b["coords"].shape[0], np.float32)
+    scale = member_scale(b["features"], b["offsets"], P, w, mode, assign=ref["assign"],
+                         knn_idx=ref["knn_idx"])
+    assert_close_scaled(got["pooled"], ref["pooled"], scale, "pooled " + label)
+    cw = b["features"][:, charge_col] if charge_col >= 0 else np.ones(b["coords"].shape[0],
+                                                                       np.float32)
+    cscale = member_scale(b["coords"], b["offsets"], P, cw, 0, assign=ref["assign"])
+    assert_close_scaled(got["centroids"], ref["centroids"], cscale, "centroids " + label)
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_tokenize_workloads(oracle_mod, name):
+    w = synth.WORKLOADS[name]
+    b = synth.make_batch(name, synth.parity_seed(name, 1))
+    _tokenize_vs_oracle(oracle_mod, b, w["P"], w["mode"], w["k"], w["L"], w["weighted"], 5,
+                        label=name)
+
+
+def test_tokenize_fused_edges(oracle_mod):
+    """The fused Voronoi kernel on every path: pass-through, one workgroup,
+    gangs (cooperative pooling across shards) and the streaming fallback."""
+    b = synth.icecube_events([0, 3, 128, 129, 700, 4096, 4097, 9000, 30001, 50], 23, C=6)
+    _tokenize_vs_oracle(oracle_mod, b, 128, label="fused edges")
+    _tokenize_vs_oracle(oracle_mod, b, 256, weighted=False, label="fused edges plain mean")
+    b = synth.grid_events([20000, 700], 24, C=11, side=2)
+    _tokenize_vs_oracle(oracle_mod, b, 64, label="fused tie-rich gang C=11")
+    b = synth.uniform_events([270000, 600], 25, C=6)
+    _tokenize_vs_oracle(oracle_mod, b, 32, label="fused streaming")
+    b = synth.icecube_events([800, 12000, 90], 26, C=6)
+    _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=16, L=1, stepwise=True, label="stepwise")

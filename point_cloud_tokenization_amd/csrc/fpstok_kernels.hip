@@ -402,20 +402,318 @@ __device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, in
     if (sh.g == 0) write_selection(a, b, p, s_sel);
 }
 
-// Register-resident FPS for m = ceil(shard / 256) pulses per thread.
+// ------------------------------------ single-workgroup FPS, candidate list
+
+constexpr int kListCap = 64;  // entries of the candidate list (one per lane)
+
+// LDS of the single-workgroup FPS.
+struct FpsLds {
+    FpsSlot wl[kFpsW][64];    // each wave's contribution to an exchange
+    FpsSlot list[kListCap];   // the workgroup's new candidate list
+    int wc[kFpsW];            // entries of each wave's contribution
+    int wb[kFpsW];            // each wave's bound
+    uint32_t bm[kFpsW][64];   // per-wave selection bitmap (degenerate case only)
+};
+
+// Lowest pulse index that no iteration 0..j has selected (the caller knows
+// one exists below 2048).  Selections 0 .. 64*(j/64)-1 are in s_sel; those
+// of the current block of 64 are in `selv` (lane q: iteration 64*(j/64)+q).
+// Built per wave in LDS with atomic ORs; used only when every pulse has
+// minimum distance 0.
+__device__ __forceinline__ int first_unselected_lds(uint32_t* bm, const int* s_sel, int selv,
+                                                    int j) {
+    const int lane = lane_id();
+    bm[lane] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    const int blk = j & ~63;
+    for (int q = lane; q < blk; q += 64) {
+        const int v = s_sel[q];
+        if (v >= 0 && v < 2048) atomicOr(&bm[v >> 5], 1u << (v & 31));
+    }
+    if (lane <= (j & 63) && selv >= 0 && selv < 2048) atomicOr(&bm[selv >> 5], 1u << (selv & 31));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    return first_unselected(bm[lane]);
+}
+
+// FPS of one event of at most 256*M pulses by one workgroup, every pulse in
+// registers (lane-blocked: thread t owns pulses t*M .. t*M+M-1).
+//
+// The argmax is exact but is computed from a cached candidate list most of
+// the time.  Minimum distances only decrease, so if at some iteration every
+// pulse outside a list has min distance <= U, that stays true afterwards;
+// while the best listed pulse (its min distance kept current alongside the
+// pulses) is > U it is the farthest pulse, ties included: every pulse with
+// that distance is listed and the list is in pulse order.
+//
+// When the test fails (and at the first iteration) the workgroup exchanges:
+//  * every group of pulses -- a lane's M pulses, or a pair of lanes when
+//    M = 1 -- offers its farthest pulse (lowest index on ties), and its
+//    second largest distance bounds the rest of the group;
+//  * a wave keeps the offers >= the largest second distance of the wave and
+//    writes them, in lane order, to LDS; U is the largest wave bound;
+//  * after a barrier every wave reads all offers: the best one is this
+//    iteration's argmax (the global maximum is always offered), and the
+//    offers > U, in pulse order, become the new list.  If more than 64
+//    remain, the first 64 are kept and U is raised to the largest of the
+//    others.
+// Every wave holds the same list (lane l: entry l) and takes the same
+// decisions; between exchanges the waves never synchronise.  One wave on a
+// SIMD issues a vector instruction only every few cycles, so a run of list
+// hits is kept to one short straight loop: the list's distances and their
+// wave maximum, the pulses' update, a ballot and five lane reads for the
+// winner; the centroid stays in scalar registers.  U is kept >= 0, so a
+// maximum of 0 (every pulse selected or duplicate) always goes through an
+// exchange, where the "lowest unselected index" rule is applied.  The
+// selection order is buffered in a register (lane j mod 64 holds iteration
+// j) and flushed to LDS by wave 0 every 64 iterations.
+template <int M>
+__device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64_t off, int n,
+                                           int s0, FpsLds& L, int* s_sel, int* s_asg) {
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int P = a.P;
+    const float4* __restrict__ p = a.coords + off;
+    const int lbase = tid * M;
+
+    float px[M], py[M], pz[M], pt[M], md[M];
+    int nr[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+        const int i = lbase + k;
+        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < n) q = p[i];
+        px[k] = q.x;
+        py[k] = q.y;
+        pz[k] = q.z;
+        pt[k] = q.w;
+        md[k] = i < n ? INFINITY : -1.0f;  // padding never wins and is never updated
+        nr[k] = 0;
+    }
+    // candidate list entry of this lane (-1: none)
+    float lv = -1.0f, lx = 0.f, ly = 0.f, lz = 0.f, lt = 0.f;
+    int li = 0;
+    int U = INT32_MAX;  // bound on every unlisted pulse (float bits); no list yet
+
+    int selv = 0;
+    int s = s0;
+    float cx, cy, cz, ct;  // the newest centroid (uniform)
+    {
+        const float4 q = p[s];
+        cx = readlane_f(q.x, 0);
+        cy = readlane_f(q.y, 0);
+        cz = readlane_f(q.z, 0);
+        ct = readlane_f(q.w, 0);
+    }
+    int j = 0;
+    for (;;) {
+        // ---- a run of iterations decided by the list
+        int wm;
+        for (;;) {
+            selv = lane == (j & 63) ? s : selv;
+            if ((j & 63) == 63 && wave == 0) s_sel[j - 63 + lane] = selv;
+            {
+                const float d = sqd(lx, ly, lz, lt, cx, cy, cz, ct);
+                lv = d < lv ? d : lv;
+            }
+            wm = wave_max_i(__float_as_int(lv));
+#pragma unroll
+            for (int k = 0; k < M; ++k) {
+                const float d = sqd(px[k], py[k], pz[k], pt[k], cx, cy, cz, ct);
+                const bool u = d < md[k];
+                nr[k] = u ? j : nr[k];
+                md[k] = u ? d : md[k];
+            }
+            if (j + 1 == P || wm <= U) break;
+            // the best listed pulse; lanes hold the list in pulse order
+            const int Lw = (int)__builtin_ctzll(ballot(__float_as_int(lv) == wm));
+            s = readlane_i(li, Lw);
+            cx = readlane_f(lx, Lw);
+            cy = readlane_f(ly, Lw);
+            cz = readlane_f(lz, Lw);
+            ct = readlane_f(lt, Lw);
+            ++j;
+        }
+        if (j + 1 == P) break;
+
+        // ---- exchange
+        int b1 = INT32_MIN, b2 = INT32_MIN, k1 = 0;
+        float bx = 0.f, by = 0.f, bz = 0.f, bt = 0.f;
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int v = __float_as_int(md[k]);
+            const bool g = v > b1;
+            b2 = g ? b1 : max(b2, v);
+            b1 = g ? v : b1;
+            k1 = g ? k : k1;
+            bx = g ? px[k] : bx;
+            by = g ? py[k] : by;
+            bz = g ? pz[k] : bz;
+            bt = g ? pt[k] : bt;
+        }
+        bool lead = true;
+        if (M == 1) {
+            // groups are lane pairs (2l, 2l+1)
+            const int q = dpp_i<kQuadSwap1, 0xF>(b1, INT32_MIN);
+            lead = b1 > q || (b1 == q && (lane & 1) == 0);
+            b2 = min(b1, q);
+        }
+        const int wb2 = wave_max_i(b2);
+        const bool offer = lead && b1 >= wb2;
+        const uint64_t ob = ballot(offer);
+        if (offer) {
+            FpsSlot& o = L.wl[wave][mbcnt(ob)];
+            o.v = __int_as_float(b1);
+            o.i = lbase + k1;
+            o.c = make_float4(bx, by, bz, bt);
+        }
+        if (lane == 0) {
+            L.wc[wave] = __popcll(ob);
+            L.wb[wave] = wb2;
+        }
+        __syncthreads();
+        int cw[kFpsW];
+        int Un = 0;
+#pragma unroll
+        for (int w = 0; w < kFpsW; ++w) {
+            cw[w] = __builtin_amdgcn_readfirstlane(L.wc[w]);
+            Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wb[w]));
+        }
+        int rv[kFpsW], ri[kFpsW];
+        float rx[kFpsW], ry[kFpsW], rz[kFpsW], rt[kFpsW];
+        int rb = INT32_MIN, re = 0;
+#pragma unroll
+        for (int w = 0; w < kFpsW; ++w) {
+            const bool has = lane < cw[w];
+            const FpsSlot& o = L.wl[w][has ? lane : 0];
+            rv[w] = has ? __float_as_int(o.v) : INT32_MIN;
+            ri[w] = o.i;
+            rx[w] = o.c.x;
+            ry[w] = o.c.y;
+            rz[w] = o.c.z;
+            rt[w] = o.c.w;
+            const bool g = rv[w] > rb;
+            rb = g ? rv[w] : rb;
+            re = g ? w : re;
+        }
+        // this iteration's argmax: largest offer, then lowest (wave, lane)
+        const int gm = wave_max_i(rb);
+        {
+            const uint64_t m = ballot(rb == gm);
+            int Lw, ew;
+            if (__popcll(m) == 1) {
+                Lw = (int)__builtin_ctzll(m);
+                ew = readlane_i(re, Lw);
+            } else {
+                const int f = wave_min_i(rb == gm ? re * 64 + lane : INT32_MAX);
+                Lw = f & 63;
+                ew = f >> 6;
+            }
+            int oi = ri[0];
+            float ox = rx[0], oy = ry[0], oz = rz[0], ot = rt[0];
+#pragma unroll
+            for (int w = 1; w < kFpsW; ++w) {
+                const bool t = ew == w;
+                oi = t ? ri[w] : oi;
+                ox = t ? rx[w] : ox;
+                oy = t ? ry[w] : oy;
+                oz = t ? rz[w] : oz;
+                ot = t ? rt[w] : ot;
+            }
+            if (gm <= 0) {
+                s = min(first_unselected_lds(L.bm[wave], s_sel, selv, j), n - 1);
+                const float4 q = p[s];
+                cx = readlane_f(q.x, 0);
+                cy = readlane_f(q.y, 0);
+                cz = readlane_f(q.z, 0);
+                ct = readlane_f(q.w, 0);
+            } else {
+                s = min(max(readlane_i(oi, Lw), 0), n - 1);
+                cx = readlane_f(ox, Lw);
+                cy = readlane_f(oy, Lw);
+                cz = readlane_f(oz, Lw);
+                ct = readlane_f(ot, Lw);
+            }
+        }
+        // new list: the offers > U, in pulse order; beyond 64 entries the
+        // rest only raise U
+        int C = 0;
+        int dropped = INT32_MIN;
+#pragma unroll
+        for (int w = 0; w < kFpsW; ++w) {
+            const bool keep = rv[w] > Un;
+            const uint64_t kb = ballot(keep);
+            const int pos = C + mbcnt(kb);
+            if (w == wave && keep && pos < kListCap) {
+                FpsSlot& o = L.list[pos];
+                o.v = __int_as_float(rv[w]);
+                o.i = ri[w];
+                o.c = make_float4(rx[w], ry[w], rz[w], rt[w]);
+            }
+            dropped = keep && pos >= kListCap ? max(dropped, rv[w]) : dropped;
+            C += __popcll(kb);
+        }
+        if (C > kListCap) Un = max(Un, wave_max_i(dropped));
+        __syncthreads();
+        U = __builtin_amdgcn_readfirstlane(Un);
+        if (lane < C) {
+            const FpsSlot o = L.list[lane];
+            lv = o.v;
+            li = o.i;
+            lx = o.c.x;
+            ly = o.c.y;
+            lz = o.c.z;
+            lt = o.c.w;
+        } else {
+            lv = -1.0f;
+        }
+        ++j;
+    }
+    if (wave == 0 && lane <= (j & 63)) s_sel[(j & ~63) + lane] = selv;
+    if (a.assign) {
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int i = lbase + k;
+            if (i < n) a.assign[off + i] = nr[k];
+        }
+    }
+    if (s_asg) {
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int i = lbase + k;
+            if (i < n) s_asg[i] = nr[k];
+        }
+    }
+    write_selection(a, b, p, s_sel);
+}
+
+__device__ __forceinline__ void fps_single_dispatch(const SampleArgs& a, int64_t b, int64_t off,
+                                                    int n, int s0, FpsLds& L, int* ss, int* sa) {
+    switch ((n + kFpsT - 1) / kFpsT) {
+        case 1: fps_single<1>(a, b, off, n, s0, L, ss, sa); break;
+        case 2: fps_single<2>(a, b, off, n, s0, L, ss, sa); break;
+        case 3: fps_single<3>(a, b, off, n, s0, L, ss, sa); break;
+        case 4: fps_single<4>(a, b, off, n, s0, L, ss, sa); break;
+        case 5: fps_single<5>(a, b, off, n, s0, L, ss, sa); break;
+        case 6: fps_single<6>(a, b, off, n, s0, L, ss, sa); break;
+        case 7: fps_single<7>(a, b, off, n, s0, L, ss, sa); break;
+        case 8: fps_single<8>(a, b, off, n, s0, L, ss, sa); break;
+        case 9: case 10: fps_single<10>(a, b, off, n, s0, L, ss, sa); break;
+        case 11: case 12: fps_single<12>(a, b, off, n, s0, L, ss, sa); break;
+        case 13: case 14: fps_single<14>(a, b, off, n, s0, L, ss, sa); break;
+        default: fps_single<16>(a, b, off, n, s0, L, ss, sa); break;
+    }
+}
+
+// Register-resident FPS of a gang shard (2049 .. 4096 pulses).
 __device__ __forceinline__ void fps_registers_dispatch(const SampleArgs& a, int64_t b, int64_t off, int n,
                                        int s0, const Shard& sh, FpsSlot (*sl)[kFpsW], int* ss,
                                        int* sa) {
     switch ((sh.cnt + kFpsT - 1) / kFpsT) {
-        case 1: fps_registers<1>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 2: fps_registers<2>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 3: fps_registers<3>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 4: fps_registers<4>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 5: fps_registers<5>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 6: fps_registers<6>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 7: fps_registers<7>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 8: fps_registers<8>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 9: case 10: fps_registers<10>(a, b, off, n, s0, sh, sl, ss, sa); break;
+        case 1: case 2: case 3: case 4: case 5: case 6: case 7: case 8: case 9: case 10:
+            fps_registers<10>(a, b, off, n, s0, sh, sl, ss, sa); break;
         case 11: case 12: fps_registers<12>(a, b, off, n, s0, sh, sl, ss, sa); break;
         case 13: case 14: fps_registers<14>(a, b, off, n, s0, sh, sl, ss, sa); break;
         default: fps_registers<16>(a, b, off, n, s0, sh, sl, ss, sa); break;
@@ -556,8 +854,8 @@ struct ItemInfo {
 // Claim one work item and run FPS (or pass-through) for it.  s_asg, when not
 // null, receives the shard's Voronoi slots (register-resident paths only).
 __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item,
-                                                FpsSlot (*s_slots)[kFpsW], int* s_sel,
-                                                int* s_asg) {
+                                                FpsSlot (*s_slots)[kFpsW], FpsLds& s_fps,
+                                                int* s_sel, int* s_asg) {
     const int tid = threadIdx.x;
     ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0};
     // items are claimed in list order, so the shards of one gang go to
@@ -600,8 +898,7 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     int s0 = a.start_idx ? a.start_idx[b] : 0;
     if (s0 < 0 || s0 >= n) s0 = 0;
     if (n <= kFpsCap) {
-        const Shard sh{0, n, 0, 1, nullptr, a.header + 3};
-        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel, s_asg);
+        fps_single_dispatch(a, b, off, n, s0, s_fps, s_sel, s_asg);
         it.kind = 1;
         it.cnt = n;
     } else if (n <= kGangMax * kFpsCap) {
@@ -628,7 +925,8 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
     __shared__ int s_item;
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
-    sample_item(a, &s_item, s_slots, s_sel, nullptr);
+    __shared__ FpsLds s_fps;
+    sample_item(a, &s_item, s_slots, s_fps, s_sel, nullptr);
 }
 
 // ------------------------------------------------------------------- assign
@@ -1127,18 +1425,21 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
 //    slots j = g, g+G, ... by walking the shards in order -- again ascending
 //    pulse order;
 //  * streaming (beyond gang size): a workgroup-wide sort in device memory.
-// Dynamic LDS: s_cnt[kSortW*P], s_off[P+1], s_asg[kFpsCap], s_perm[kFpsCap].
+// Dynamic LDS: s_perm[kFpsCap] (during FPS: the FpsLds of a single-workgroup
+// event), s_asg[kFpsCap], s_cnt[kSortW*P], s_off[P+1].
 __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs pa) {
     __shared__ int s_item;
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
-    extern __shared__ int s_dyn[];
+    extern __shared__ __align__(16) int s_dyn[];
+    static_assert(sizeof(FpsLds) <= sizeof(int) * kFpsCap, "FpsLds must fit in s_perm");
     const int P = a.P;
-    int* s_cnt = s_dyn;
+    int* s_perm = s_dyn;
+    int* s_asg = s_perm + kFpsCap;
+    int* s_cnt = s_asg + kFpsCap;
     int* s_off = s_cnt + kSortW * P;
-    int* s_asg = s_off + P + 1;
-    int* s_perm = s_asg + kFpsCap;
-    const ItemInfo it = sample_item(a, &s_item, s_slots, s_sel, s_asg);
+    FpsLds& s_fps = *reinterpret_cast<FpsLds*>(s_perm);
+    const ItemInfo it = sample_item(a, &s_item, s_slots, s_fps, s_sel, s_asg);
     if (it.b < 0) return;
     const int64_t b = it.b;
     const int64_t off = it.off;

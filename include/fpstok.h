@@ -112,8 +112,8 @@ typedef struct {
 } fpstok_params;
 
 /* Bytes of device workspace every compute call of this batch shape needs
- * (depends on B, N and num_patches; params may be NULL for the largest
- * num_patches).  Host-only; never fails; 0 for B = 0. */
+ * (depends on B, N, num_patches and num_features; params may be NULL for
+ * the largest num_patches).  Host-only; never fails; 0 for B = 0. */
 size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_params* params);
 
 /* FPS of every event (farthest_point_sampling / _with_assign).  For n > P:

@@ -41,7 +41,7 @@ static fpstok_status hip_fail(hipError_t e, const char* what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P) {
+WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     WorkspaceLayout L{};
     if (B <= 0) return L;
     const int64_t nn = N > 0 ? N : 0;
@@ -65,9 +65,11 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P) {
     L.item_g = at;
     at += align256((size_t)L.max_items * sizeof(int32_t));
     L.gang_rec = at;
-    at += align256((size_t)L.max_items * 12 * sizeof(unsigned long long));
+    at += align256((size_t)L.max_items * 2 * kGangRecWords * sizeof(unsigned long long));
     L.shard_cells = at;
     at += align256((size_t)L.max_items * (size_t)(P + 1) * sizeof(int32_t));
+    L.gang_part = at;
+    at += align256((size_t)(nn / kGangPulsesPerShard + 1) * (size_t)P * (size_t)(C + 1) * sizeof(double));
     L.total = at;
     return L;
 }
@@ -120,7 +122,8 @@ static fpstok_status check_common(const fpstok_batch* bt, const fpstok_params* p
 
 static fpstok_status check_ws(const fpstok_batch* bt, const fpstok_params* pr, void* ws,
                               size_t ws_bytes, WorkspaceLayout& L) {
-    L = workspace_layout(bt->num_events, bt->num_points, pr->num_patches);
+    L = workspace_layout(bt->num_events, bt->num_points, pr->num_patches,
+                         bt->num_features > 0 ? bt->num_features : 1);
     if (L.total == 0) return FPSTOK_OK;
     if (!ws) return fail(FPSTOK_EWORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
     if (ws_bytes < L.total)
@@ -143,7 +146,9 @@ FPSTOK_API size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_
     if (!batch) return 0;
     int P = params ? params->num_patches : FPSTOK_MAX_PATCHES;
     if (P < 1 || P > FPSTOK_MAX_PATCHES) P = FPSTOK_MAX_PATCHES;
-    return workspace_layout(batch->num_events, batch->num_points, P).total;
+    return workspace_layout(batch->num_events, batch->num_points, P,
+                            batch->num_features > 0 ? batch->num_features : 1)
+        .total;
 }
 
 FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_params* pr,
@@ -176,6 +181,7 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
     a.item_g = at<int32_t>(ws, L.item_g);
     a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
     a.shard_cells = at<int32_t>(ws, L.shard_cells);
+    a.gang_part = at<double>(ws, L.gang_part);
     hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
     return ok();
@@ -373,6 +379,7 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     a.item_g = at<int32_t>(ws, L.item_g);
     a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
     a.shard_cells = at<int32_t>(ws, L.shard_cells);
+    a.gang_part = at<double>(ws, L.gang_part);
     PoolArgs p{};
     p.features = bt->features;
     p.offsets = bt->offsets;

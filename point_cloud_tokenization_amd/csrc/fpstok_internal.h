@@ -13,6 +13,10 @@ namespace fpstok {
 // 256-thread workgroup.
 constexpr int kChunk = 256;
 
+// 64-bit words of one gang exchange record (one shard, one parity): 64
+// candidate entries of one word each, the shard's bound, padding.
+constexpr int kGangRecWords = 64 + 8;
+
 // Workspace carve-up.  Every region starts on a 256-byte boundary.
 struct WorkspaceLayout {
     size_t header;      // int32[64]: [0] = number of chunks
@@ -23,14 +27,19 @@ struct WorkspaceLayout {
     size_t perm;        // int32[N]: pulses sorted by token (Lloyd, pool)
     size_t item_ev;     // int32[max_items]: FPS work items (event)
     size_t item_g;      // int32[max_items]: FPS work items (shard)
-    size_t gang_rec;    // uint64[max_items][12]: gang exchange records
-    size_t shard_cells; // int32[max_items][P+1]: per-shard slot offsets (fused pooling)
+    size_t gang_rec;    // uint64[max_items][2][kGangRecWords]: gang exchange records
+    size_t shard_cells; // int32[max_items][P+1]: per-shard slot sizes (fused pooling)
+    size_t gang_part;   // double[max_gang_items][P][C+1]: per-shard partial sums (fused pooling)
     size_t total;
     int64_t max_chunks;
     int64_t max_items;
 };
 
-WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P);
+// A gang event of n pulses has at most n / kGangPulsesPerShard shards, so
+// all gangs together have at most N / kGangPulsesPerShard.
+constexpr int64_t kGangPulsesPerShard = 2048;
+
+WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C);
 int64_t sample_max_items(int64_t B, int64_t N);
 
 struct SampleArgs {
@@ -48,8 +57,9 @@ struct SampleArgs {
     int32_t* header;                // [1] items, [2] claim counter, [3] error word
     int32_t* item_ev;               // [max_items] event of each work item
     int32_t* item_g;                // [max_items] shard of each work item
-    unsigned long long* gang_rec;   // [max_items][2][6] gang records
-    int32_t* shard_cells;           // [max_items][P+1] per-shard slot offsets (fused pooling)
+    unsigned long long* gang_rec;   // [max_items][2][kGangRecWords] gang records
+    int32_t* shard_cells;           // [max_items][P+1] per-shard slot sizes (fused pooling)
+    double* gang_part;              // [gang items][P][C+1] per-shard partial sums (fused pooling)
 };
 
 struct AssignArgs {

@@ -180,7 +180,6 @@ constexpr int kFpsW = kFpsT / 64;
 constexpr int kFpsM = 16;                  // register-resident pulses per thread
 constexpr int kFpsCap = kFpsT * kFpsM;     // pulses one workgroup holds in registers
 constexpr int kGangMax = 64;               // workgroups sharing one event at most
-constexpr int kRecWords = 6;               // 64-bit words of a gang record
 constexpr uint32_t kSpinLimit = 1u << 22;  // bound on every inter-workgroup wait
 
 struct __align__(16) FpsSlot {
@@ -192,74 +191,17 @@ struct __align__(16) FpsSlot {
 
 // The part of an event one workgroup holds.  A gang is the set of G
 // workgroups that share one event; each keeps a contiguous shard of pulses in
-// registers, and after every iteration the shards exchange their candidates
-// through records in device memory.
+// registers, and the shards exchange candidates through records in device
+// memory.
 struct Shard {
     int lo;                    // first event-local pulse of the shard
     int cnt;                   // pulses in the shard
     int g;                     // shard index
-    int G;                     // shards of the event (1: no exchange)
-    unsigned long long* rec;   // records of the gang: [G][2][kRecWords]
+    int G;                     // shards of the event
+    unsigned long long* rec;   // records of the gang: [G][2][kGangRecWords]
     int32_t* err;              // device error word (bounded wait exceeded)
 };
 
-__device__ __forceinline__ unsigned long long tagged(int j, uint32_t payload) {
-    return ((unsigned long long)(uint32_t)(j + 1) << 32) | payload;
-}
-
-// Gang-wide argmax of iteration j: thread 0 publishes this workgroup's
-// candidate as six tagged 64-bit words (relaxed agent-scope atomics; every
-// word carries the iteration tag, so no ordering between them is needed);
-// every wave then polls the G records until all carry tag j+1 and reduces
-// them: largest value, then lowest shard (= lowest pulse index).  Records
-// are double-buffered by iteration parity: a workgroup writes iteration j+2
-// only after it has seen every record of j+1, which each workgroup publishes
-// only after all of its waves finished reading iteration j.
-__device__ __forceinline__ FpsSlot gang_exchange(const FpsSlot& mine, const Shard& sh, int j) {
-    const int par = j & 1;
-    if (threadIdx.x == 0) {
-        unsigned long long* r = sh.rec + ((size_t)sh.g * 2 + par) * kRecWords;
-        const uint32_t pay[kRecWords] = {__float_as_uint(mine.v), (uint32_t)mine.i,
-                                         __float_as_uint(mine.c.x), __float_as_uint(mine.c.y),
-                                         __float_as_uint(mine.c.z), __float_as_uint(mine.c.w)};
-#pragma unroll
-        for (int q = 0; q < kRecWords; ++q)
-            __hip_atomic_store(r + q, tagged(j, pay[q]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const int lane = lane_id();
-    const bool has = lane < sh.G;
-    const unsigned long long* r = sh.rec + ((size_t)(has ? lane : 0) * 2 + par) * kRecWords;
-    unsigned long long w[kRecWords];
-    const uint32_t want = (uint32_t)(j + 1);
-    for (uint32_t spin = 0;; ++spin) {
-        bool ok = true;
-        if (has) {
-#pragma unroll
-            for (int q = 0; q < kRecWords; ++q) {
-                w[q] = __hip_atomic_load(r + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && (uint32_t)(w[q] >> 32) == want;
-            }
-        }
-        if (ballot(!ok) == 0) break;
-        if (spin >= kSpinLimit) {
-            if (lane == 0) __hip_atomic_store(sh.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    const int v = has ? (int)(uint32_t)w[0] : INT32_MIN;
-    const int gm = wave_max_i(v);
-    const int L = (int)__builtin_ctzll(ballot(has && v == gm));
-    FpsSlot out;
-    out.v = __int_as_float(gm);
-    out.i = readlane_i((int)(uint32_t)w[1], L);
-    out.c.x = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[2], L));
-    out.c.y = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[3], L));
-    out.c.z = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[4], L));
-    out.c.w = __uint_as_float((uint32_t)readlane_i((int)(uint32_t)w[5], L));
-    return out;
-}
 
 // Write the selection order (and the selected coordinates) of one event.
 __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
@@ -272,139 +214,10 @@ __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
     }
 }
 
-// FPS over one shard of an event (the whole event when G = 1) with at most
-// 256*M pulses, every pulse held in registers.  Lane l of wave w owns the M
-// consecutive pulses starting at shard.lo + (64*w + l)*M, so a lower lane (and
-// a lower wave, then a lower shard) always holds lower pulse indices.
-//
-// Per pulse and iteration: the float32 distance to the newest centroid (11
-// VALU ops), the fused Voronoi update (compare + 2 selects) and the lane's
-// running first maximum with its pulse (compare, max, 5 selects).  Minimum
-// distances are float32 values in {-1} U [0, inf] (-1 marks padding),
-// compared as int32 bit patterns, whose order they keep.
-//
-// One iteration's argmax: a DPP wave maximum; the lowest lane holding it
-// (one ballot) gives the wave's candidate, which lane 0 writes to an LDS slot;
-// after the barrier every lane reads the kFpsW slots (broadcast reads) and
-// keeps the largest, lowest wave on ties, with plain compares and selects.
-// The centroid therefore stays in VGPRs and no value travels back through a
-// scalar register between the barrier and the next update.
-//
-// Selected pulses are not marked: a selected pulse has min distance exactly
-// 0, so while the maximum is > 0 it cannot win; when the maximum is 0 every
-// pulse has min distance 0 and the rule "lowest unselected index" is applied
-// from a selection bitmap over indices 0..2047 (the answer is < P <= 1024).
-//
-// The selection order is kept in LDS (s_sel) and written out after the loop:
-// a global store inside the loop would put its completion on every
-// iteration's barrier.
-template <int M>
-__device__ __forceinline__ void fps_registers(const SampleArgs& a, int64_t b, int64_t off, int n,
-                                              int s0, const Shard& sh, FpsSlot (*slots)[kFpsW],
-                                              int* s_sel, int* s_asg) {
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid >> 6;
-    const int P = a.P;
-    const float4* __restrict__ p = a.coords + off;
-    const int lbase = sh.lo + tid * M;  // first pulse of this lane
-    const int send = sh.lo + sh.cnt;
-
-    float px[M], py[M], pz[M], pt[M], md[M];
-    int nr[M];
-#pragma unroll
-    for (int k = 0; k < M; ++k) {
-        const int i = lbase + k;
-        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < send) q = p[i];
-        px[k] = q.x;
-        py[k] = q.y;
-        pz[k] = q.z;
-        pt[k] = q.w;
-        md[k] = i < send ? INFINITY : -1.0f;  // padding never wins and is never updated
-        nr[k] = 0;
-    }
-
-    uint32_t selbits = 0;
-    int s = s0;
-    float4 c = p[s];
-    for (int j = 0; j < P; ++j) {
-        if (tid == 0) s_sel[j] = s;
-        mark_selected(selbits, s);
-        int bv = INT32_MIN;
-        int bi = 0;
-        float bx = 0.f, by = 0.f, bz = 0.f, bt = 0.f;
-#pragma unroll
-        for (int k = 0; k < M; ++k) {
-            const float d = sqd(px[k], py[k], pz[k], pt[k], c.x, c.y, c.z, c.w);
-            const bool u = d < md[k];
-            nr[k] = u ? j : nr[k];
-            md[k] = u ? d : md[k];
-            const int mi = __float_as_int(md[k]);
-            const bool g = mi > bv;
-            bv = g ? mi : bv;
-            bi = g ? k : bi;
-            bx = g ? px[k] : bx;
-            by = g ? py[k] : by;
-            bz = g ? pz[k] : bz;
-            bt = g ? pt[k] : bt;
-        }
-        if (j + 1 == P) break;
-
-        const int wm = wave_max_i(bv);
-        const int L = (int)__builtin_ctzll(ballot(bv == wm));
-        const int wi = readlane_i(lbase + bi, L);
-        const float4 wc = make_float4(readlane_f(bx, L), readlane_f(by, L), readlane_f(bz, L),
-                                      readlane_f(bt, L));
-        if (lane == 0) {
-            FpsSlot& o = slots[j & 1][wave];
-            o.v = __int_as_float(wm);
-            o.i = wi;
-            o.c = wc;
-        }
-        __syncthreads();
-        const FpsSlot* sl = slots[j & 1];
-        FpsSlot g = sl[0];
-#pragma unroll
-        for (int w = 1; w < kFpsW; ++w) {
-            const FpsSlot o = sl[w];
-            const bool better = __float_as_int(o.v) > __float_as_int(g.v);
-            g.v = better ? o.v : g.v;
-            g.i = better ? o.i : g.i;
-            g.c.x = better ? o.c.x : g.c.x;
-            g.c.y = better ? o.c.y : g.c.y;
-            g.c.z = better ? o.c.z : g.c.z;
-            g.c.w = better ? o.c.w : g.c.w;
-        }
-        if (sh.G > 1) g = gang_exchange(g, sh, j);
-        if (g.v == 0.0f) {
-            s = min(first_unselected(selbits), n - 1);
-            c = p[s];
-        } else {
-            s = min(max(g.i, 0), n - 1);
-            c = g.c;
-        }
-    }
-    if (a.assign) {
-#pragma unroll
-        for (int k = 0; k < M; ++k) {
-            const int i = lbase + k;
-            if (i < send) a.assign[off + i] = nr[k];
-        }
-    }
-    if (s_asg) {
-#pragma unroll
-        for (int k = 0; k < M; ++k) {
-            const int i = lbase + k;
-            if (i < send) s_asg[i - sh.lo] = nr[k];
-        }
-    }
-    if (sh.g == 0) write_selection(a, b, p, s_sel);
-}
-
 // ------------------------------------ single-workgroup FPS, candidate list
 
 constexpr int kListCap = 64;  // entries of the candidate list (one per lane)
+constexpr int kNoEntry = (int)0xBF800000;  // bit pattern of -1.0f: an empty entry
 
 // LDS of the single-workgroup FPS.
 struct FpsLds {
@@ -412,6 +225,7 @@ struct FpsLds {
     FpsSlot list[kListCap];   // the workgroup's new candidate list
     int wc[kFpsW];            // entries of each wave's contribution
     int wb[kFpsW];            // each wave's bound
+    int wd[kFpsW];            // each wave's largest offer left out of a full list
     uint32_t bm[kFpsW][64];   // per-wave selection bitmap (degenerate case only)
 };
 
@@ -453,11 +267,11 @@ __device__ __forceinline__ int first_unselected_lds(uint32_t* bm, const int* s_s
 //    second largest distance bounds the rest of the group;
 //  * a wave keeps the offers >= the largest second distance of the wave and
 //    writes them, in lane order, to LDS; U is the largest wave bound;
-//  * after a barrier every wave reads all offers: the best one is this
-//    iteration's argmax (the global maximum is always offered), and the
-//    offers > U, in pulse order, become the new list.  If more than 64
-//    remain, the first 64 are kept and U is raised to the largest of the
-//    others.
+//  * after a barrier every wave reads the offered distances: the best offer
+//    is this iteration's argmax (the global maximum is always offered), and
+//    the offers > U, in pulse order, become the new list, each wave writing
+//    its own offers from registers.  If more than 64 remain, the first 64
+//    are kept and U is raised to the largest of the others.
 // Every wave holds the same list (lane l: entry l) and takes the same
 // decisions; between exchanges the waves never synchronise.  One wave on a
 // SIMD issues a vector instruction only every few cycles, so a run of list
@@ -574,31 +388,24 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             L.wb[wave] = wb2;
         }
         __syncthreads();
-        int cw[kFpsW];
+        // every wave: U, this iteration's argmax (largest offer, then lowest
+        // (wave, position) = lowest pulse index) and the list layout
         int Un = 0;
+        int rb = INT32_MIN, re = 0;
+        int kcnt[kFpsW];
 #pragma unroll
         for (int w = 0; w < kFpsW; ++w) {
-            cw[w] = __builtin_amdgcn_readfirstlane(L.wc[w]);
             Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wb[w]));
         }
-        int rv[kFpsW], ri[kFpsW];
-        float rx[kFpsW], ry[kFpsW], rz[kFpsW], rt[kFpsW];
-        int rb = INT32_MIN, re = 0;
 #pragma unroll
         for (int w = 0; w < kFpsW; ++w) {
-            const bool has = lane < cw[w];
-            const FpsSlot& o = L.wl[w][has ? lane : 0];
-            rv[w] = has ? __float_as_int(o.v) : INT32_MIN;
-            ri[w] = o.i;
-            rx[w] = o.c.x;
-            ry[w] = o.c.y;
-            rz[w] = o.c.z;
-            rt[w] = o.c.w;
-            const bool g = rv[w] > rb;
-            rb = g ? rv[w] : rb;
+            const int cw = __builtin_amdgcn_readfirstlane(L.wc[w]);
+            const int v = lane < cw ? __float_as_int(L.wl[w][lane < cw ? lane : 0].v) : INT32_MIN;
+            const bool g = v > rb;
+            rb = g ? v : rb;
             re = g ? w : re;
+            kcnt[w] = __popcll(ballot(v > Un));
         }
-        // this iteration's argmax: largest offer, then lowest (wave, lane)
         const int gm = wave_max_i(rb);
         {
             const uint64_t m = ballot(rb == gm);
@@ -611,17 +418,6 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
                 Lw = f & 63;
                 ew = f >> 6;
             }
-            int oi = ri[0];
-            float ox = rx[0], oy = ry[0], oz = rz[0], ot = rt[0];
-#pragma unroll
-            for (int w = 1; w < kFpsW; ++w) {
-                const bool t = ew == w;
-                oi = t ? ri[w] : oi;
-                ox = t ? rx[w] : ox;
-                oy = t ? ry[w] : oy;
-                oz = t ? rz[w] : oz;
-                ot = t ? rt[w] : ot;
-            }
             if (gm <= 0) {
                 s = min(first_unselected_lds(L.bm[wave], s_sel, selv, j), n - 1);
                 const float4 q = p[s];
@@ -630,32 +426,40 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
                 cz = readlane_f(q.z, 0);
                 ct = readlane_f(q.w, 0);
             } else {
-                s = min(max(readlane_i(oi, Lw), 0), n - 1);
-                cx = readlane_f(ox, Lw);
-                cy = readlane_f(oy, Lw);
-                cz = readlane_f(oz, Lw);
-                ct = readlane_f(ot, Lw);
+                const FpsSlot& o = L.wl[ew][Lw];
+                s = min(max((int)__builtin_amdgcn_readfirstlane(o.i), 0), n - 1);
+                cx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.x)));
+                cy = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.y)));
+                cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.z)));
+                ct = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.w)));
             }
         }
-        // new list: the offers > U, in pulse order; beyond 64 entries the
-        // rest only raise U
-        int C = 0;
-        int dropped = INT32_MIN;
+        // new list: the offers > U in (wave, position) order, each wave
+        // writing its own from registers; beyond 64 entries the rest only
+        // raise U
+        int base = 0, C = 0;
 #pragma unroll
         for (int w = 0; w < kFpsW; ++w) {
-            const bool keep = rv[w] > Un;
-            const uint64_t kb = ballot(keep);
-            const int pos = C + mbcnt(kb);
-            if (w == wave && keep && pos < kListCap) {
-                FpsSlot& o = L.list[pos];
-                o.v = __int_as_float(rv[w]);
-                o.i = ri[w];
-                o.c = make_float4(rx[w], ry[w], rz[w], rt[w]);
-            }
-            dropped = keep && pos >= kListCap ? max(dropped, rv[w]) : dropped;
-            C += __popcll(kb);
+            base += w < wave ? kcnt[w] : 0;
+            C += kcnt[w];
         }
-        if (C > kListCap) Un = max(Un, wave_max_i(dropped));
+        const bool keep = offer && b1 > Un;
+        const int pos = base + mbcnt(ballot(keep));
+        if (keep && pos < kListCap) {
+            FpsSlot& o = L.list[pos];
+            o.v = __int_as_float(b1);
+            o.i = lbase + k1;
+            o.c = make_float4(bx, by, bz, bt);
+        }
+        if (C > kListCap) {
+            const int d = wave_max_i(keep && pos >= kListCap ? b1 : INT32_MIN);
+            // every wave needs the same U: combine the per-wave maxima
+            if (lane == 0) L.wd[wave] = d;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kFpsW; ++w)
+                Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wd[w]));
+        }
         __syncthreads();
         U = __builtin_amdgcn_readfirstlane(Un);
         if (lane < C) {
@@ -707,16 +511,429 @@ __device__ __forceinline__ void fps_single_dispatch(const SampleArgs& a, int64_t
     }
 }
 
-// Register-resident FPS of a gang shard (2049 .. 4096 pulses).
-__device__ __forceinline__ void fps_registers_dispatch(const SampleArgs& a, int64_t b, int64_t off, int n,
-                                       int s0, const Shard& sh, FpsSlot (*sl)[kFpsW], int* ss,
-                                       int* sa) {
+// ----------------------------------------- gang FPS, shared candidate list
+
+constexpr int kGangE = 4;                 // gang-list entries per lane
+constexpr int kGangCap = 64 * kGangE;     // entries of the gang list
+constexpr int kRecSlots = 64;             // entries a shard publishes per exchange
+constexpr int kRecBound = kRecSlots;      // record word holding the shard's bound
+constexpr int kGangQ = kGangMax * kRecSlots / kFpsT;  // record entries read per thread at most
+
+struct GangLds {
+    FpsLds w;                   // the workgroup's own exchange
+    FpsSlot glist[kGangCap];    // the new gang list
+    FpsSlot gwin;               // the gang's argmax of an exchange
+    int gU;                     // the gang's bound
+    int gcnt[kGangQ * kFpsW];   // kept record entries per (read round, wave)
+    int gdrop[kFpsW];
+};
+
+// A record word: tag (14 bits: the iteration + 1, at most 1025) | pulse
+// index (18 bits, < kGangMax * kFpsCap) | distance bits (32).  One word per
+// entry, so one relaxed agent-scope load sees a whole entry; the
+// coordinates are read back from the (read-only) input.
+__device__ __forceinline__ unsigned long long rec_word(int tag, int idx, int v) {
+    return ((unsigned long long)(uint32_t)tag << 50) |
+           ((unsigned long long)((uint32_t)idx & 0x3FFFFu) << 32) | (uint32_t)v;
+}
+__device__ __forceinline__ unsigned long long rec_load(const unsigned long long* w) {
+    return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void rec_store(unsigned long long* w, unsigned long long word) {
+    __hip_atomic_store(w, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool rec_ok(unsigned long long w, int tag) {
+    return (uint32_t)(w >> 50) == (uint32_t)tag;
+}
+__device__ __forceinline__ int rec_idx(unsigned long long w) { return (int)((w >> 32) & 0x3FFFFu); }
+__device__ __forceinline__ int rec_val(unsigned long long w) { return (int)(uint32_t)w; }
+
+// FPS over one shard of an event shared by a gang of G workgroups (shard g
+// holds pulses lo .. lo+cnt-1, at most 256*M, in registers as in
+// fps_single).  The same exact candidate-list scheme, one level up: every
+// shard holds the same gang-wide list (up to 256 entries, entry f = 64*e +
+// lane in register e) and decides alone while the best listed pulse beats
+// the gang bound U.  An exchange (the first iteration, and whenever the test
+// fails):
+//  1. inside the workgroup, as in fps_single: offers, the shard's best
+//     pulse, its bound U_g and its offers > U_g (the first 63 in pulse
+//     order; any others raise U_g);
+//  2. the shard publishes a record: those entries in slots 0..62, its best
+//     pulse in slot 63 and U_g, one 64-bit word each, tagged with the
+//     iteration so that no ordering between the words is needed (relaxed
+//     agent-scope atomics; records are double-buffered by exchange parity);
+//  3. every workgroup polls all G records (bounded waits), takes the best of
+//     the G shard bests (lowest shard on ties: lowest pulse index) as this
+//     iteration's argmax, U = max U_g, and the record entries > U, in
+//     (shard, slot) order, as the new gang list (the first 256; any others
+//     raise U).  A shard's best may also sit among its slots 0..62; the
+//     copy is harmless, and on ties the lowest (shard, slot) is still the
+//     lowest pulse index.
+// Returns the number of exchanges (the parity of the record buffer that no
+// shard reads any more).
+template <int M>
+__device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t off, int n, int s0,
+                                        const Shard& sh, GangLds& L, int* s_sel, int* s_asg) {
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int P = a.P;
+    const int G = sh.G;
+    const float4* __restrict__ p = a.coords + off;
+    const int lbase = sh.lo + tid * M;  // event-local index of this lane's first pulse
+    const int send = sh.lo + sh.cnt;
+
+    float px[M], py[M], pz[M], pt[M], md[M];
+    int nr[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+        const int i = lbase + k;
+        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < send) q = p[i];
+        px[k] = q.x;
+        py[k] = q.y;
+        pz[k] = q.z;
+        pt[k] = q.w;
+        md[k] = i < send ? INFINITY : -1.0f;
+        nr[k] = 0;
+    }
+    float lv[kGangE], lx[kGangE], ly[kGangE], lz[kGangE], lt[kGangE];
+    int li[kGangE];
+#pragma unroll
+    for (int e = 0; e < kGangE; ++e) {
+        lv[e] = -1.0f;
+        li[e] = 0;
+        lx[e] = ly[e] = lz[e] = lt[e] = 0.f;
+    }
+    int nreg = 0;
+    int U = INT32_MAX;
+    int ex = 0;
+
+    int selv = 0;
+    int s = s0;
+    float cx, cy, cz, ct;
+    {
+        const float4 q = p[s];
+        cx = readlane_f(q.x, 0);
+        cy = readlane_f(q.y, 0);
+        cz = readlane_f(q.z, 0);
+        ct = readlane_f(q.w, 0);
+    }
+    int j = 0;
+    for (;;) {
+        for (;;) {
+            selv = lane == (j & 63) ? s : selv;
+            if ((j & 63) == 63 && wave == 0) s_sel[j - 63 + lane] = selv;
+            int lb = INT32_MIN, le = 0;
+#pragma unroll
+            for (int e = 0; e < kGangE; ++e) {
+                if (e < nreg) {
+                    const float d = sqd(lx[e], ly[e], lz[e], lt[e], cx, cy, cz, ct);
+                    lv[e] = d < lv[e] ? d : lv[e];
+                    const int v = __float_as_int(lv[e]);
+                    const bool g = v > lb;
+                    lb = g ? v : lb;
+                    le = g ? e : le;
+                }
+            }
+            const int wm = wave_max_i(lb);
+#pragma unroll
+            for (int k = 0; k < M; ++k) {
+                const float d = sqd(px[k], py[k], pz[k], pt[k], cx, cy, cz, ct);
+                const bool u = d < md[k];
+                nr[k] = u ? j : nr[k];
+                md[k] = u ? d : md[k];
+            }
+            if (j + 1 == P || wm <= U) break;
+            const uint64_t m = ballot(lb == wm);
+            int Lw, ew;
+            if (__popcll(m) == 1) {
+                Lw = (int)__builtin_ctzll(m);
+                ew = readlane_i(le, Lw);
+            } else {
+                const int f = wave_min_i(lb == wm ? le * 64 + lane : INT32_MAX);
+                Lw = f & 63;
+                ew = f >> 6;
+            }
+            int oi = li[0];
+            float ox = lx[0], oy = ly[0], oz = lz[0], ot = lt[0];
+#pragma unroll
+            for (int e = 1; e < kGangE; ++e) {
+                const bool t = ew == e;
+                oi = t ? li[e] : oi;
+                ox = t ? lx[e] : ox;
+                oy = t ? ly[e] : oy;
+                oz = t ? lz[e] : oz;
+                ot = t ? lt[e] : ot;
+            }
+            s = readlane_i(oi, Lw);
+            cx = readlane_f(ox, Lw);
+            cy = readlane_f(oy, Lw);
+            cz = readlane_f(oz, Lw);
+            ct = readlane_f(ot, Lw);
+            ++j;
+        }
+        if (j + 1 == P) break;
+
+        // ---- 1. the workgroup's offers, best pulse, bound and entries
+        int b1 = INT32_MIN, b2 = INT32_MIN, k1 = 0;
+        float bx = 0.f, by = 0.f, bz = 0.f, bt = 0.f;
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int v = __float_as_int(md[k]);
+            const bool g = v > b1;
+            b2 = g ? b1 : max(b2, v);
+            b1 = g ? v : b1;
+            k1 = g ? k : k1;
+            bx = g ? px[k] : bx;
+            by = g ? py[k] : by;
+            bz = g ? pz[k] : bz;
+            bt = g ? pt[k] : bt;
+        }
+        const int wb2 = wave_max_i(b2);
+        const bool offer = b1 >= wb2;
+        const uint64_t ob = ballot(offer);
+        if (offer) {
+            FpsSlot& o = L.w.wl[wave][mbcnt(ob)];
+            o.v = __int_as_float(b1);
+            o.i = lbase + k1;
+            o.c = make_float4(bx, by, bz, bt);
+        }
+        if (lane == 0) {
+            L.w.wc[wave] = __popcll(ob);
+            L.w.wb[wave] = wb2;
+        }
+        __syncthreads();
+        int Uw = 0;
+#pragma unroll
+        for (int w = 0; w < kFpsW; ++w) Uw = max(Uw, (int)__builtin_amdgcn_readfirstlane(L.w.wb[w]));
+        int rb = INT32_MIN, re = 0;
+        int kcnt[kFpsW];
+#pragma unroll
+        for (int w = 0; w < kFpsW; ++w) {
+            const int cw = __builtin_amdgcn_readfirstlane(L.w.wc[w]);
+            const int v = lane < cw ? __float_as_int(L.w.wl[w][lane < cw ? lane : 0].v) : INT32_MIN;
+            const bool g = v > rb;
+            rb = g ? v : rb;
+            re = g ? w : re;
+            kcnt[w] = __popcll(ballot(v > Uw));
+        }
+        const int gm = wave_max_i(rb);
+        int Lb, eb;
+        {
+            const uint64_t m = ballot(rb == gm);
+            if (__popcll(m) == 1) {
+                Lb = (int)__builtin_ctzll(m);
+                eb = readlane_i(re, Lb);
+            } else {
+                const int f = wave_min_i(rb == gm ? re * 64 + lane : INT32_MAX);
+                Lb = f & 63;
+                eb = f >> 6;
+            }
+        }
+        int base = 0, C = 0;
+#pragma unroll
+        for (int w = 0; w < kFpsW; ++w) {
+            base += w < wave ? kcnt[w] : 0;
+            C += kcnt[w];
+        }
+        const bool keep = offer && b1 > Uw;
+        const int pos = base + mbcnt(ballot(keep));
+        if (keep && pos < kRecSlots - 1) {
+            FpsSlot& o = L.w.list[pos];
+            o.v = __int_as_float(b1);
+            o.i = lbase + k1;
+            o.c = make_float4(bx, by, bz, bt);
+        }
+        if (C > kRecSlots - 1) {
+            const int d = wave_max_i(keep && pos >= kRecSlots - 1 ? b1 : INT32_MIN);
+            if (lane == 0) L.w.wd[wave] = d;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kFpsW; ++w) Uw = max(Uw, (int)__builtin_amdgcn_readfirstlane(L.w.wd[w]));
+        }
+        __syncthreads();
+
+        // ---- 2. publish this shard's record
+        const int tag = j + 1;
+        const int par = ex & 1;
+        // record of shard q: rec0 + q * 2 * kGangRecWords
+        unsigned long long* rec0 = sh.rec + (size_t)par * kGangRecWords;
+        if (wave == 0) {
+            unsigned long long* r = rec0 + (size_t)sh.g * 2 * kGangRecWords;
+            int ov = kNoEntry, oi = 0;
+            if (lane == kRecSlots - 1) {
+                const FpsSlot& o = L.w.wl[eb][Lb];
+                ov = __float_as_int(o.v);
+                oi = o.i;
+            } else if (lane < C) {
+                const FpsSlot& o = L.w.list[lane];
+                ov = __float_as_int(o.v);
+                oi = o.i;
+            }
+            rec_store(r + lane, rec_word(tag, oi, ov));
+            if (lane == 0) rec_store(r + kRecBound, rec_word(tag, 0, Uw));
+        }
+
+        // ---- 3. read every shard's record
+        // thread t reads record entries F = t + 256q (shard F/64, slot
+        // F%64); threads t < G also the best pulse and the bound of shard t
+        const int nF = G * kRecSlots;
+        const char* rbase = reinterpret_cast<const char*>(rec0);
+        unsigned long long vw[kGangQ];
+        unsigned long long bw0 = 0, bw1 = 0;
+        {
+            const uint32_t so = (uint32_t)(tid < G ? tid : 0) * 2u * kGangRecWords * 8u;
+            for (uint32_t spin = 0;; ++spin) {
+                bool ok = true;
+                // an opaque zero keeps the offsets from being hoisted out of
+                // the wait loop (they are cheap; registers are not)
+                int z;
+                asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+#pragma unroll
+                for (int q = 0; q < kGangQ; ++q) {
+                    const int F = tid + kFpsT * q + z;
+                    if (F < nF) {
+                        const uint32_t o = ((uint32_t)(F >> 6) * 2u * kGangRecWords + (uint32_t)(F & 63)) * 8u;
+                        vw[q] = rec_load(reinterpret_cast<const unsigned long long*>(rbase + o));
+                        ok = ok && rec_ok(vw[q], tag);
+                    }
+                }
+                if (tid < G) {
+                    bw0 = rec_load(reinterpret_cast<const unsigned long long*>(rbase + so + (kRecSlots - 1) * 8u));
+                    bw1 = rec_load(reinterpret_cast<const unsigned long long*>(rbase + so + kRecBound * 8u));
+                    ok = ok && rec_ok(bw0, tag) && rec_ok(bw1, tag);
+                }
+                if (__syncthreads_and(ok)) break;
+                if (spin >= kSpinLimit) {
+                    if (tid == 0)
+                        __hip_atomic_store(sh.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        // the gang's argmax and bound (wave 0 holds every shard's)
+        if (wave == 0) {
+            const bool has = lane < G;
+            const int u = has ? rec_val(bw1) : 0;
+            const int Ug = wave_max_i(u);
+            const int v = has ? rec_val(bw0) : INT32_MIN;
+            const int vm = wave_max_i(v);
+            const int Lg = (int)__builtin_ctzll(ballot(has && v == vm));
+            if (lane == Lg) {
+                L.gwin.v = __int_as_float(v);
+                L.gwin.i = rec_idx(bw0);
+            }
+            if (lane == 0) L.gU = Ug;
+        }
+        __syncthreads();
+        int Ug = __builtin_amdgcn_readfirstlane(L.gU);
+#pragma unroll
+        for (int q = 0; q < kGangQ; ++q) {
+            const int F = tid + kFpsT * q;
+            const bool kq = F < nF && rec_val(vw[q]) > Ug;
+            const uint64_t kb = ballot(kq);
+            if (lane == 0) L.gcnt[q * kFpsW + wave] = __popcll(kb);
+        }
+        __syncthreads();
+        // positions in (shard, slot) order = F order: round q, then wave,
+        // then lane; an exclusive scan of the (q, wave) counts, one per lane
+        static_assert(kGangQ * kFpsW == 64, "one count per lane");
+        const int cnt_l = L.gcnt[lane];
+        const int incl_l = wave_incl_scan(cnt_l);
+        const int excl_l = incl_l - cnt_l;
+        const int Cg = readlane_i(incl_l, 63);
+        int dropped = INT32_MIN;
+#pragma unroll
+        for (int q = 0; q < kGangQ; ++q) {
+            const int F = tid + kFpsT * q;
+            const bool kq = F < nF && rec_val(vw[q]) > Ug;
+            const int gpos = readlane_i(excl_l, q * kFpsW + wave) + mbcnt(ballot(kq));
+            if (kq && gpos < kGangCap) {
+                const int gi = min(rec_idx(vw[q]), n - 1);
+                FpsSlot& o = L.glist[gpos];
+                o.v = __int_as_float(rec_val(vw[q]));
+                o.i = gi;
+                o.c = p[gi];
+            }
+            dropped = kq && gpos >= kGangCap ? max(dropped, rec_val(vw[q])) : dropped;
+        }
+        if (Cg > kGangCap) {
+            const int d = wave_max_i(dropped);
+            if (lane == 0) L.gdrop[wave] = d;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kFpsW; ++w) Ug = max(Ug, (int)__builtin_amdgcn_readfirstlane(L.gdrop[w]));
+        }
+        __syncthreads();
+        {
+            const int gv = __builtin_amdgcn_readfirstlane(__float_as_int(L.gwin.v));
+            if (gv <= 0) {
+                s = min(first_unselected_lds(L.w.bm[wave], s_sel, selv, j), n - 1);
+                const float4 q = p[s];
+                cx = readlane_f(q.x, 0);
+                cy = readlane_f(q.y, 0);
+                cz = readlane_f(q.z, 0);
+                ct = readlane_f(q.w, 0);
+            } else {
+                s = min(max((int)__builtin_amdgcn_readfirstlane(L.gwin.i), 0), n - 1);
+                const float4 q = p[s];
+                cx = readlane_f(q.x, 0);
+                cy = readlane_f(q.y, 0);
+                cz = readlane_f(q.z, 0);
+                ct = readlane_f(q.w, 0);
+            }
+        }
+        const int Cl = min(Cg, kGangCap);
+        nreg = __builtin_amdgcn_readfirstlane((Cl + 63) >> 6);
+        U = __builtin_amdgcn_readfirstlane(Ug);
+#pragma unroll
+        for (int e = 0; e < kGangE; ++e) {
+            const int f = e * 64 + lane;
+            if (f < Cl) {
+                const FpsSlot o = L.glist[f];
+                lv[e] = o.v;
+                li[e] = o.i;
+                lx[e] = o.c.x;
+                ly[e] = o.c.y;
+                lz[e] = o.c.z;
+                lt[e] = o.c.w;
+            } else {
+                lv[e] = -1.0f;
+            }
+        }
+        ++ex;
+        ++j;
+    }
+    if (wave == 0 && lane <= (j & 63)) s_sel[(j & ~63) + lane] = selv;
+    if (a.assign) {
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int i = lbase + k;
+            if (i < send) a.assign[off + i] = nr[k];
+        }
+    }
+    if (s_asg) {
+        __syncthreads();  // s_asg overlaps this function's LDS
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int i = lbase + k;
+            if (i < send) s_asg[i - sh.lo] = nr[k];
+        }
+    }
+    if (sh.g == 0) write_selection(a, b, p, s_sel);
+    return ex;
+}
+
+__device__ __forceinline__ int fps_gang_dispatch(const SampleArgs& a, int64_t b, int64_t off, int n,
+                                                 int s0, const Shard& sh, GangLds& L, int* ss, int* sa) {
     switch ((sh.cnt + kFpsT - 1) / kFpsT) {
         case 1: case 2: case 3: case 4: case 5: case 6: case 7: case 8: case 9: case 10:
-            fps_registers<10>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 11: case 12: fps_registers<12>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        case 13: case 14: fps_registers<14>(a, b, off, n, s0, sh, sl, ss, sa); break;
-        default: fps_registers<16>(a, b, off, n, s0, sh, sl, ss, sa); break;
+            return fps_gang<10>(a, b, off, n, s0, sh, L, ss, sa);
+        case 11: case 12: return fps_gang<12>(a, b, off, n, s0, sh, L, ss, sa);
+        case 13: case 14: return fps_gang<14>(a, b, off, n, s0, sh, L, ss, sa);
+        default: return fps_gang<16>(a, b, off, n, s0, sh, L, ss, sa);
     }
 }
 
@@ -823,13 +1040,15 @@ __global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B)
             for (int q = 0; q < cnt && pos + q < max_items; ++q) {
                 a.item_ev[pos + q] = (int32_t)b;
                 a.item_g[pos + q] = q;
-                if (cnt > 1) {
-                    unsigned long long* r = a.gang_rec + (size_t)(pos + q) * 2 * kRecWords;
-                    for (int w = 0; w < 2 * kRecWords; ++w) r[w] = 0ull;
-                }
             }
             carry += total;
             __syncthreads();
+        }
+        // gang items are the first `carry` items after pass 0: clear their
+        // records (stale tags of an earlier call must not match)
+        if (pass == 0) {
+            const int64_t gw = (int64_t)min((int64_t)carry, B + a.N / kFpsCap) * 2 * kGangRecWords;
+            for (int64_t w = tid; w < gw; w += 1024) a.gang_rec[w] = 0ull;
         }
     }
     if (tid == 0) {
@@ -849,15 +1068,16 @@ struct ItemInfo {
     int g, G;     // shard and shards (gangs)
     int lo, cnt;  // the shard's pulses
     int item0;    // work item of shard 0 (gangs)
+    int par;      // gang record parity no shard reads any more (gangs)
 };
 
 // Claim one work item and run FPS (or pass-through) for it.  s_asg, when not
 // null, receives the shard's Voronoi slots (register-resident paths only).
 __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item,
-                                                FpsSlot (*s_slots)[kFpsW], FpsLds& s_fps,
+                                                FpsSlot (*s_slots)[kFpsW], GangLds& s_gang,
                                                 int* s_sel, int* s_asg) {
     const int tid = threadIdx.x;
-    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0};
+    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0};
     // items are claimed in list order, so the shards of one gang go to
     // workgroups that start one after another: a gang whose workgroups wait
     // for a partner only ever waits for a workgroup that will start once
@@ -898,7 +1118,7 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     int s0 = a.start_idx ? a.start_idx[b] : 0;
     if (s0 < 0 || s0 >= n) s0 = 0;
     if (n <= kFpsCap) {
-        fps_single_dispatch(a, b, off, n, s0, s_fps, s_sel, s_asg);
+        fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg);
         it.kind = 1;
         it.cnt = n;
     } else if (n <= kGangMax * kFpsCap) {
@@ -906,8 +1126,8 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
         const int S = (n + G - 1) / G;
         const int lo = g * S;
         const Shard sh{lo, min(S, n - lo), g, G,
-                       a.gang_rec + (size_t)(item - g) * 2 * kRecWords, a.header + 3};
-        fps_registers_dispatch(a, b, off, n, s0, sh, s_slots, s_sel, s_asg);
+                       a.gang_rec + (size_t)(item - g) * 2 * kGangRecWords, a.header + 3};
+        it.par = fps_gang_dispatch(a, b, off, n, s0, sh, s_gang, s_sel, s_asg) & 1;
         it.kind = 2;
         it.G = G;
         it.lo = lo;
@@ -925,8 +1145,8 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
     __shared__ int s_item;
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
-    __shared__ FpsLds s_fps;
-    sample_item(a, &s_item, s_slots, s_fps, s_sel, nullptr);
+    __shared__ GangLds s_gang;
+    sample_item(a, &s_item, s_slots, s_gang, s_sel, nullptr);
 }
 
 // ------------------------------------------------------------------- assign
@@ -1419,11 +1639,12 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
 //  * pass-through: each pulse pooled on its own;
 //  * one workgroup: the slots it just computed are sorted in LDS (stable, so
 //    each slot's members stay in ascending order) and pooled;
-//  * a gang: every shard sorts its own pulses, publishes its member lists
-//    (event-local indices in the workspace permutation, and its per-slot
-//    offsets), raises a tagged flag, waits for all shards, and then pools the
-//    slots j = g, g+G, ... by walking the shards in order -- again ascending
-//    pulse order;
+//  * a gang: every shard sorts its own pulses, publishes float64 partial
+//    sums (weight and every column) and member counts per slot, raises a
+//    tagged flag, waits for all shards, and then finishes the slots j = g,
+//    g+G, ... by adding the shards' partials in shard order (each partial in
+//    ascending pulse order: only the grouping at shard boundaries differs
+//    from one ascending sum);
 //  * streaming (beyond gang size): a workgroup-wide sort in device memory.
 // Dynamic LDS: s_perm[kFpsCap] (during FPS: the FpsLds of a single-workgroup
 // event), s_asg[kFpsCap], s_cnt[kSortW*P], s_off[P+1].
@@ -1432,14 +1653,17 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
     extern __shared__ __align__(16) int s_dyn[];
+    // single events keep their FPS state inside s_perm; gangs spill into
+    // s_asg, which fps_gang writes only after a final barrier
     static_assert(sizeof(FpsLds) <= sizeof(int) * kFpsCap, "FpsLds must fit in s_perm");
+    static_assert(sizeof(GangLds) <= sizeof(int) * 2 * kFpsCap, "GangLds must fit in s_perm+s_asg");
     const int P = a.P;
     int* s_perm = s_dyn;
     int* s_asg = s_perm + kFpsCap;
     int* s_cnt = s_asg + kFpsCap;
     int* s_off = s_cnt + kSortW * P;
-    FpsLds& s_fps = *reinterpret_cast<FpsLds*>(s_perm);
-    const ItemInfo it = sample_item(a, &s_item, s_slots, s_fps, s_sel, s_asg);
+    GangLds& s_gang = *reinterpret_cast<GangLds*>(s_perm);
+    const ItemInfo it = sample_item(a, &s_item, s_slots, s_gang, s_sel, s_asg);
     if (it.b < 0) return;
     const int64_t b = it.b;
     const int64_t off = it.off;
@@ -1461,19 +1685,34 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         pool_slots_sorted(pa, b, off, P, s_perm, s_off);
         return;
     }
-    // gang: publish this shard's member lists
-    int32_t* __restrict__ gperm = pa.perm + off;
-    int32_t* __restrict__ cells = a.shard_cells + (size_t)(it.item0 + it.g) * (P + 1);
-    for (int m = tid; m < it.cnt; m += kFpsT) gperm[it.lo + m] = it.lo + s_perm[m];
-    for (int j = tid; j <= P; j += kFpsT) cells[j] = s_off[j];
+    // gang: this shard's float64 partial sums per slot (members in ascending
+    // order), published with a flag; then the G partials of each slot are
+    // added in shard order
+    const int C1 = C + 1;
+    double* __restrict__ part = a.gang_part + (size_t)(it.item0 + it.g) * P * C1;
+    int32_t* __restrict__ cnts = a.shard_cells + (size_t)(it.item0 + it.g) * (P + 1);
+    for (int j = tid; j < P; j += kFpsT) {
+        const int beg = s_off[j], end = s_off[j + 1];
+        cnts[j] = end - beg;
+        double* __restrict__ pj = part + (size_t)j * C1;
+        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+            const int nc = min(kPoolCols, C - c0);
+            double W, Sx[kPoolCols];
+            pool_slot(pa, off, beg, end, c0, nc, [&](int m) { return it.lo + s_perm[m]; }, W, Sx);
+            if (c0 == 0) pj[0] = W;
+#pragma unroll
+            for (int q = 0; q < kPoolCols; ++q)
+                if (q < nc) pj[1 + c0 + q] = Sx[q];
+        }
+    }
     __threadfence();
     __syncthreads();
-    // the flag is word 0 of this shard's record of parity (P-1)&1, tag P+1:
-    // every exchange of the FPS loop has completed, so that buffer is free
-    unsigned long long* rec = a.gang_rec + (size_t)it.item0 * 2 * kRecWords;
-    const int par = (P - 1) & 1;
+    // the flag is word 0 of this shard's record of the parity no exchange
+    // reads any more, tag P+1 (exchange tags are at most P-1)
+    unsigned long long* rec = a.gang_rec + (size_t)it.item0 * 2 * kGangRecWords;
+    const int par = it.par;
     if (tid == 0)
-        __hip_atomic_store(rec + ((size_t)it.g * 2 + par) * kRecWords, tagged(P, 0u),
+        __hip_atomic_store(rec + ((size_t)it.g * 2 + par) * kGangRecWords, rec_word(P + 1, 0, 0),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
         const int lane = lane_id();
@@ -1482,9 +1721,9 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
             bool ok = true;
             for (int q = lane; q < it.G; q += 64) {
                 const unsigned long long w = __hip_atomic_load(
-                    rec + ((size_t)q * 2 + par) * kRecWords, __ATOMIC_RELAXED,
+                    rec + ((size_t)q * 2 + par) * kGangRecWords, __ATOMIC_RELAXED,
                     __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && (uint32_t)(w >> 32) == want;
+                ok = ok && rec_ok(w, (int)want);
             }
             if (ballot(!ok) == 0) break;
             if (spin >= kSpinLimit) {
@@ -1496,26 +1735,49 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         }
     }
     __threadfence();
-    const int32_t* __restrict__ cells0 = a.shard_cells + (size_t)it.item0 * (P + 1);
-    const int S = (it.n + it.G - 1) / it.G;  // shard size; shard sh starts at sh*S
-    for (int j = it.g + it.G * tid; j < P; j += it.G * kFpsT) {
-        int count = 0;
-        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-            const int nc = min(kPoolCols, C - c0);
-            double W = 0.0, Sx[kPoolCols];
+    // this workgroup's slots j = g, g+G, ...; one thread per (slot, column)
+    // and one per slot for the member count; shard partials read 8 at a time
+    const double* __restrict__ part0 = a.gang_part + (size_t)it.item0 * P * C1;
+    const int32_t* __restrict__ cnts0 = a.shard_cells + (size_t)it.item0 * (P + 1);
+    const int G = it.G;
+    const int nmine = (P - it.g + G - 1) / G;
+    for (int t = tid; t < nmine * C1; t += kFpsT) {
+        const int js = t / C1;
+        const int c = t - js * C1;
+        const int j = it.g + G * js;
+        if (c < C) {
+            double W = 0.0, Sc = 0.0;
+            for (int sh0 = 0; sh0 < G; sh0 += kBatch) {
+                double w8[kBatch], s8[kBatch];
 #pragma unroll
-            for (int q = 0; q < kPoolCols; ++q) Sx[q] = 0.0;
-            count = 0;
-            for (int sh = 0; sh < it.G; ++sh) {
-                const int32_t* cs = cells0 + (size_t)sh * (P + 1);
-                const int beg = cs[j], end = cs[j + 1];
-                count += end - beg;
-                const int32_t* __restrict__ sp = gperm + sh * S;
-                pool_slot_acc(pa, off, beg, end, c0, nc, [&](int m) { return sp[m]; }, W, Sx);
+                for (int q = 0; q < kBatch; ++q) {
+                    if (sh0 + q < G) {
+                        const double* pj = part0 + ((size_t)(sh0 + q) * P + j) * C1;
+                        w8[q] = pj[0];
+                        s8[q] = pj[1 + c];
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    if (sh0 + q < G) {
+                        W += w8[q];
+                        Sc += s8[q];
+                    }
+                }
             }
-            pool_write(pa, b, j, c0, nc, W, Sx);
+            pa.pooled[(b * P + j) * (int64_t)C + c] = W != 0.0 ? (float)(Sc / W) : 0.0f;
+        } else if (pa.cell_count) {
+            int count = 0;
+            for (int sh0 = 0; sh0 < G; sh0 += kBatch) {
+                int c8[kBatch];
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q)
+                    c8[q] = sh0 + q < G ? cnts0[(size_t)(sh0 + q) * (P + 1) + j] : 0;
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) count += c8[q];
+            }
+            pa.cell_count[b * P + j] = count;
         }
-        if (pa.cell_count) pa.cell_count[b * P + j] = count;
     }
 }
 

@@ -822,8 +822,12 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
             const int vm = wave_max_i(v);
             const int Lg = (int)__builtin_ctzll(ballot(has && v == vm));
             if (lane == Lg) {
+                // the winner's coordinates are fetched now, overlapping the
+                // list construction below
+                const int wi = min(rec_idx(bw0), n - 1);
                 L.gwin.v = __int_as_float(v);
-                L.gwin.i = rec_idx(bw0);
+                L.gwin.i = wi;
+                L.gwin.c = p[wi];
             }
             if (lane == 0) L.gU = Ug;
         }
@@ -878,11 +882,10 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
                 ct = readlane_f(q.w, 0);
             } else {
                 s = min(max((int)__builtin_amdgcn_readfirstlane(L.gwin.i), 0), n - 1);
-                const float4 q = p[s];
-                cx = readlane_f(q.x, 0);
-                cy = readlane_f(q.y, 0);
-                cz = readlane_f(q.z, 0);
-                ct = readlane_f(q.w, 0);
+                cx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(L.gwin.c.x)));
+                cy = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(L.gwin.c.y)));
+                cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(L.gwin.c.z)));
+                ct = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(L.gwin.c.w)));
             }
         }
         const int Cl = min(Cg, kGangCap);
@@ -1410,6 +1413,98 @@ __device__ __forceinline__ void block_sort_by_token(const int32_t* __restrict__ 
     }
 }
 
+constexpr int kSmallSlot = 64;  // largest slot block_sort_small handles
+constexpr int kRankPer = kLdsPerm / kSortT;  // members one thread ranks at most
+
+// The same stable sort, for the usual case of small slots and an LDS input
+// that may be overwritten: counts and positions with LDS atomics (any order
+// inside a slot, into `tmp`), then every member's rank inside its slot (the
+// members of the slot with a lower pulse index) counted in parallel, and the
+// members written to their final places -- into `asg` itself.  Returns
+// false, with asg untouched, if some slot holds more than kSmallSlot pulses.
+//   asg: LDS int[n] (n <= kLdsPerm);  tmp: LDS int[n];  s_cnt: LDS int[T];
+//   s_off: LDS int[T + 1]
+__device__ __forceinline__ bool block_sort_small(int* asg, int n, int T, int* tmp, int* s_cnt,
+                                                 int* s_off) {
+    __shared__ int s_ws[kSortW], s_wm[kSortW];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    for (int q = tid; q < T; q += kSortT) s_cnt[q] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSortT) {
+        const int k = asg[i];
+        if (k >= 0 && k < T) atomicAdd(&s_cnt[k], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the counts (thread t: slots t*per .. t*per+per-1),
+    // and the largest count
+    const int per = (T + kSortT - 1) / kSortT;
+    int loc[kMaxP / kSortT];
+    int local = 0, mx = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        const int c = r < per && jj < T ? s_cnt[jj] : 0;
+        loc[r] = c;
+        local += c;
+        mx = max(mx, c);
+    }
+    const int incl = wave_incl_scan(local);
+    const int wmx = wave_max_i(mx);
+    if (lane == 63) s_ws[wave] = incl;
+    if (lane == 0) s_wm[wave] = wmx;
+    __syncthreads();
+    int run = incl - local, total = 0, gmax = 0;
+#pragma unroll
+    for (int w = 0; w < kSortW; ++w) {
+        const int v = s_ws[w];
+        run += w < wave ? v : 0;
+        total += v;
+        gmax = max(gmax, s_wm[w]);
+    }
+    __syncthreads();
+    if (gmax > kSmallSlot || n > kLdsPerm) return false;
+#pragma unroll
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        if (r < per && jj < T) {
+            s_off[jj] = run;
+            s_cnt[jj] = run;
+        }
+        run += loc[r];
+    }
+    if (tid == 0) s_off[T] = total;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSortT) {
+        const int k = asg[i];
+        if (k >= 0 && k < T) tmp[atomicAdd(&s_cnt[k], 1)] = i;
+    }
+    __syncthreads();
+    int dst[kRankPer], val[kRankPer];
+#pragma unroll
+    for (int r = 0; r < kRankPer; ++r) {
+        const int x = tid + r * kSortT;
+        dst[r] = -1;
+        val[r] = 0;
+        if (x < total) {
+            const int v = tmp[x];
+            const int j = asg[v];
+            const int b0 = s_off[j], e0 = s_off[j + 1];
+            int rank = 0;
+            for (int y = b0; y < e0; ++y) rank += tmp[y] < v ? 1 : 0;
+            dst[r] = b0 + rank;
+            val[r] = v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRankPer; ++r)
+        if (dst[r] >= 0) asg[dst[r]] = val[r];
+    __syncthreads();
+    return true;
+}
+
 // ------------------------------------------------------------ Lloyd update
 
 // New centroids of one event's slots j = tid, tid+256, ... < T: the
@@ -1680,9 +1775,15 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         return;
     }
     __syncthreads();
-    block_sort_by_token(s_asg, it.cnt, P, s_perm, s_cnt, s_off);
+    // the shard's pulses sorted by slot: in s_asg itself when every slot is
+    // small, else in s_perm
+    const int* sorted = s_asg;
+    if (!block_sort_small(s_asg, it.cnt, P, s_perm, s_cnt, s_off)) {
+        block_sort_by_token(s_asg, it.cnt, P, s_perm, s_cnt, s_off);
+        sorted = s_perm;
+    }
     if (it.kind == 1) {
-        pool_slots_sorted(pa, b, off, P, s_perm, s_off);
+        pool_slots_sorted(pa, b, off, P, sorted, s_off);
         return;
     }
     // gang: this shard's float64 partial sums per slot (members in ascending
@@ -1698,7 +1799,7 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         for (int c0 = 0; c0 < C; c0 += kPoolCols) {
             const int nc = min(kPoolCols, C - c0);
             double W, Sx[kPoolCols];
-            pool_slot(pa, off, beg, end, c0, nc, [&](int m) { return it.lo + s_perm[m]; }, W, Sx);
+            pool_slot(pa, off, beg, end, c0, nc, [&](int m) { return it.lo + sorted[m]; }, W, Sx);
             if (c0 == 0) pj[0] = W;
 #pragma unroll
             for (int q = 0; q < kPoolCols; ++q)

@@ -254,8 +254,9 @@ def main():
     # call = the work-list kernel + tokenize_kernel) in Voronoi mode without
     # Lloyd, else fpstok_sample
     roof = fps_roofline(st, step_gpu if fused else per_call["sample"],
-                        "tokenize_kernel (FPS + fused Voronoi pooling)" if fused
-                        else "sample_kernel (FPS)")
+                        "fpstok_tokenize call: plan_fps_kernel + tokenize_kernel (FPS + fused "
+                        "Voronoi pooling)" if fused else "fpstok_sample call: plan_fps_kernel + "
+                        "sample_kernel (FPS)")
     log("per-step GPU %.1f us; per call (stepwise) %s" % (
         step_gpu * 1e6, {c: round(v * 1e6, 1) for c, v in per_call.items()}))
 

@@ -159,6 +159,32 @@ def identical_events(ns, seed, C=6):
     return _pack(ns, coords, _features(rng, int(ns.sum()), C))
 
 
+def seed_copies_events(ns, seed, C=6, strides=None):
+    """Clouds where most pulses are exact copies of pulse 0 (the default FPS
+    seed) and every stride-th pulse (positions stride-1, 2*stride-1, ...)
+    lies on a far shell of radius 2..3.  After the first selection every
+    copy has distance 0, so when the stride equals the number of pulses a
+    lane holds, every lane's second-farthest distance is 0 while its
+    farthest is large: many more candidates than a candidate list holds,
+    and, once the far pulses are used up, the all-zero case."""
+    rng = np.random.default_rng(seed)
+    ns = np.asarray(ns, dtype=np.int64)
+    strides = np.ones_like(ns) if strides is None else np.asarray(strides, dtype=np.int64)
+    parts = []
+    for n, st in zip(ns, strides):
+        base = rng.uniform(-1.0, 1.0, 4)
+        c = np.repeat(base[None, :], n, axis=0)
+        far = np.arange(n) % st == st - 1
+        far[0] = False
+        k = int(far.sum())
+        d = rng.standard_normal((k, 4))
+        d /= np.linalg.norm(d, axis=1, keepdims=True)
+        c[far] = base + d * rng.uniform(2.0, 3.0, (k, 1))
+        parts.append(c)
+    coords = np.concatenate(parts) if parts else np.zeros((0, 4))
+    return _pack(ns, coords, _features(rng, int(ns.sum()), C))
+
+
 def make_batch(name: str, seed: int | None = None) -> dict:
     """A batch of the named workload: coords, features, offsets and the
     tokenizer parameters (P, mode, k, L, weighted, charge_col)."""

@@ -132,6 +132,20 @@ def test_gang_and_streaming_paths(oracle_mod):
     check_pipeline(oracle_mod, b, P=64, mode=0, label="streaming")
 
 
+@pytest.mark.parametrize("P", [128, 300])
+def test_candidate_list_overflow(oracle_mod, P):
+    """More candidates above the bound than the lists hold: a workgroup's
+    64-entry list, a shard's 63 published entries, the gang's 256 entries.
+    Every lane holds one far pulse and copies of the seed (stride = pulses
+    per lane).  With P = 300 the far pulses run out and the all-zero rule
+    takes over, in single workgroups and in gangs."""
+    ns = [200, 256, 512, 1024, 2048, 4096, 8192, 20000]
+    strides = [2, 2, 2, 4, 8, 16, 16, 16]
+    b = synth.seed_copies_events(ns, 31 + P, C=6, strides=strides)
+    check_pipeline(oracle_mod, b, P=P, mode=0, label="overflow P=%d" % P)
+    _tokenize_vs_oracle(oracle_mod, b, P, label="overflow fused P=%d" % P)
+
+
 def test_graph_replay_matches_eager(oracle_mod):
     """The whole tokenizer captured in a HIP graph: every replay (with eager
     work and synchronizations in between) equals the eager result."""

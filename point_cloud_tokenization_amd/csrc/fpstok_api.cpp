@@ -53,6 +53,10 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     at += align256((size_t)L.max_chunks * sizeof(int32_t));
     L.chunk_beg = at;
     at += align256((size_t)L.max_chunks * sizeof(int32_t));
+    L.chunk_part = at;
+    at += align256((size_t)L.max_chunks * sizeof(int32_t));
+    L.ev_cnt = at;
+    at += align256((size_t)B * sizeof(int32_t));
     L.mind = at;
     at += align256((size_t)nn * sizeof(float));
     L.near = at;
@@ -68,8 +72,9 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     at += align256((size_t)L.max_items * 2 * kGangRecWords * sizeof(unsigned long long));
     L.shard_cells = at;
     at += align256((size_t)L.max_items * (size_t)(P + 1) * sizeof(int32_t));
-    L.gang_part = at;
-    at += align256((size_t)(nn / kGangPulsesPerShard + 1) * (size_t)P * (size_t)(C + 1) * sizeof(double));
+    L.max_parts = nn / kGangPulsesPerShard + 1;
+    L.part = at;
+    at += align256((size_t)L.max_parts * (size_t)P * (size_t)(C + 2) * sizeof(double));
     L.total = at;
     return L;
 }
@@ -181,7 +186,7 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
     a.item_g = at<int32_t>(ws, L.item_g);
     a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
     a.shard_cells = at<int32_t>(ws, L.shard_cells);
-    a.gang_part = at<double>(ws, L.gang_part);
+    a.gang_part = at<double>(ws, L.part);
     hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
     return ok();
@@ -200,7 +205,8 @@ FPSTOK_API fpstok_status fpstok_assign(const fpstok_batch* bt, const fpstok_para
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
+    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, kChunk, false,
+                               s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
     AssignArgs a{};
     a.coords = (const float4*)bt->coords;
@@ -260,7 +266,8 @@ FPSTOK_API fpstok_status fpstok_lloyd(const fpstok_batch* bt, const fpstok_param
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
+    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, kChunk, false,
+                               s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
     LloydArgs u{};
     u.coords = (const float4*)bt->coords;
@@ -323,9 +330,21 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
     a.pooled = pooled;
     a.cell_count = cell_count;
     a.perm = at<int32_t>(ws, L.perm);
-    hipError_t e = pr->assign_mode == FPSTOK_VORONOI
-                       ? launch_pool_voronoi(a, bt->num_events, (hipStream_t)stream)
-                       : launch_pool_knn(a, bt->num_events, (hipStream_t)stream);
+    a.header = at<int32_t>(ws, L.header);
+    a.chunk_ev = at<int32_t>(ws, L.chunk_ev);
+    a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
+    a.chunk_part = at<int32_t>(ws, L.chunk_part);
+    a.ev_cnt = at<int32_t>(ws, L.ev_cnt);
+    a.part = at<double>(ws, L.part);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (pr->assign_mode == FPSTOK_VORONOI) {
+        e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, kPoolChunk, true, s);
+        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+        e = launch_pool_voronoi(a, L.max_chunks, s);
+    } else {
+        e = launch_pool_knn(a, bt->num_events, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
     return ok();
 }
@@ -379,7 +398,7 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     a.item_g = at<int32_t>(ws, L.item_g);
     a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
     a.shard_cells = at<int32_t>(ws, L.shard_cells);
-    a.gang_part = at<double>(ws, L.gang_part);
+    a.gang_part = at<double>(ws, L.part);
     PoolArgs p{};
     p.features = bt->features;
     p.offsets = bt->offsets;

@@ -13,6 +13,10 @@ namespace fpstok {
 // 256-thread workgroup.
 constexpr int kChunk = 256;
 
+// Pulses per chunk of the chunked Voronoi pooling: the largest slot sort one
+// workgroup does in LDS.
+constexpr int kPoolChunk = 4096;
+
 // 64-bit words of one gang exchange record (one shard, one parity): 64
 // candidate entries of one word each, the shard's bound, padding.
 constexpr int kGangRecWords = 64 + 8;
@@ -22,6 +26,8 @@ struct WorkspaceLayout {
     size_t header;      // int32[64]: [0] = number of chunks
     size_t chunk_ev;    // int32[max_chunks]: event of each chunk
     size_t chunk_beg;   // int32[max_chunks]: first event-local pulse of each chunk
+    size_t chunk_part;  // int32[max_chunks]: partial-sum record of each chunk (pooling)
+    size_t ev_cnt;      // int32[B]: chunks of each event done so far (pooling)
     size_t mind;        // float[N]: running min distance (large-event FPS)
     size_t near;        // int32[N]: running nearest slot (large-event FPS, no assign out)
     size_t perm;        // int32[N]: pulses sorted by token (Lloyd, pool)
@@ -29,15 +35,20 @@ struct WorkspaceLayout {
     size_t item_g;      // int32[max_items]: FPS work items (shard)
     size_t gang_rec;    // uint64[max_items][2][kGangRecWords]: gang exchange records
     size_t shard_cells; // int32[max_items][P+1]: per-shard slot sizes (fused pooling)
-    size_t gang_part;   // double[max_gang_items][P][C+1]: per-shard partial sums (fused pooling)
+    size_t part;        // double[max_parts][P][C+2]: partial sums per shard (fused pooling,
+                        // stride C+1) or per chunk (chunked pooling, stride C+2)
     size_t total;
     int64_t max_chunks;
     int64_t max_items;
+    int64_t max_parts;
 };
 
 // A gang event of n pulses has at most n / kGangPulsesPerShard shards, so
-// all gangs together have at most N / kGangPulsesPerShard.
+// all gangs together have at most N / kGangPulsesPerShard.  The same bound
+// holds for the pooling chunks of events of more than one chunk (at most
+// 2 n / kPoolChunk of them).
 constexpr int64_t kGangPulsesPerShard = 2048;
+static_assert(kPoolChunk >= 2 * kGangPulsesPerShard, "pooling chunks would outgrow the records");
 
 WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C);
 int64_t sample_max_items(int64_t B, int64_t N);
@@ -115,16 +126,26 @@ struct PoolArgs {
     float* pooled;
     int32_t* cell_count;
     int32_t* perm;
+    const int32_t* header;      // chunked pooling: [0] = number of chunks
+    const int32_t* chunk_ev;    // chunked pooling: event of each chunk
+    const int32_t* chunk_beg;   // chunked pooling: first event-local pulse of each chunk
+    const int32_t* chunk_part;  // chunked pooling: record of each chunk (-1: one-chunk event)
+    int32_t* ev_cnt;            // chunked pooling: finished chunks per event
+    double* part;               // chunked pooling: [max_parts][P][C+2] partial sums
+    int stage_cap;              // fused pooling: feature floats an event may stage in LDS
 };
 
+// Chunk list of every event: `chunk` pulses per chunk (kChunk for assign,
+// kPoolChunk for pooling).  With `pool` set, also the partial-sum records of
+// the chunks and zeroed per-event chunk counters.
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                       const WorkspaceLayout& L, hipStream_t s);
+                       const WorkspaceLayout& L, int chunk, bool pool, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s);
 hipError_t launch_assign(const AssignArgs& a, int64_t max_chunks, hipStream_t s);
 hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s);
-hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s);
 hipError_t launch_pool_knn(const PoolArgs& a, int64_t B, hipStream_t s);
 
 }  // namespace fpstok

@@ -128,19 +128,24 @@ __device__ __forceinline__ void mark_selected(uint32_t& selbits, int s) {
 
 // ------------------------------------------------------------------- planner
 
-// One workgroup of 1024 threads: split every event into chunks of kChunk
+// One workgroup of 1024 threads: split every event into chunks of `chunk`
 // pulses (an empty event gets one chunk so per-event work still runs) and
-// write the chunk list.
+// write the chunk list.  With `chunk_part` given (pooling), the chunks of
+// every event of more than one chunk also get consecutive partial-sum
+// records (-1: the event is one chunk), and `ev_cnt` is cleared.
 __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ offsets,
-                                                    int64_t B, int64_t N, int64_t max_chunks,
+                                                    int64_t B, int64_t N, int chunk,
+                                                    int64_t max_chunks, int64_t max_parts,
                                                     int32_t* __restrict__ header,
                                                     int32_t* __restrict__ chunk_ev,
-                                                    int32_t* __restrict__ chunk_beg) {
-    __shared__ int s_wsum[16];
+                                                    int32_t* __restrict__ chunk_beg,
+                                                    int32_t* __restrict__ chunk_part,
+                                                    int32_t* __restrict__ ev_cnt) {
+    __shared__ int s_wsum[16], s_psum[16];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
-    int carry = 0;
+    int64_t carry = 0, pcarry = 0;
     for (int64_t base = 0; base < B; base += 1024) {
         const int64_t b = base + tid;
         int nch = 0;
@@ -148,28 +153,44 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ 
             int64_t off;
             int n;
             event_range(offsets, N, b, off, n);
-            nch = n > 0 ? (n + kChunk - 1) / kChunk : 1;
+            nch = n > 0 ? (n + chunk - 1) / chunk : 1;
+            if (ev_cnt) ev_cnt[b] = 0;
         }
-        int incl = wave_incl_scan(nch);
-        if (lane == 63) s_wsum[wave] = incl;
+        const int np = nch > 1 ? nch : 0;
+        const int incl = wave_incl_scan(nch);
+        const int pincl = wave_incl_scan(np);
+        if (lane == 63) {
+            s_wsum[wave] = incl;
+            s_psum[wave] = pincl;
+        }
         __syncthreads();
-        int wbase = 0, total = 0;
+        int wbase = 0, total = 0, pbase = 0, ptotal = 0;
         for (int w = 0; w < 16; ++w) {
-            int v = s_wsum[w];
-            if (w < wave) wbase += v;
+            const int v = s_wsum[w], u = s_psum[w];
+            if (w < wave) {
+                wbase += v;
+                pbase += u;
+            }
             total += v;
+            ptotal += u;
         }
-        // malformed (overlapping) offsets can ask for more chunks than the
-        // list holds; those are dropped rather than written out of bounds
-        const int64_t pos = (int64_t)carry + wbase + incl - nch;
+        // malformed (overlapping) offsets can ask for more chunks or records
+        // than the lists hold; extra chunks are dropped and an event without
+        // room for its records is marked -2 (pooled whole by its first
+        // chunk), never written out of bounds
+        const int64_t pos = carry + wbase + incl - nch;
+        const int64_t ppos = pcarry + pbase + pincl - np;
+        const bool room = ppos + np <= max_parts;
         for (int c = 0; c < nch && pos + c < max_chunks; ++c) {
             chunk_ev[pos + c] = (int32_t)b;
-            chunk_beg[pos + c] = c * kChunk;
+            chunk_beg[pos + c] = c * chunk;
+            if (chunk_part) chunk_part[pos + c] = nch == 1 ? -1 : (room ? (int)(ppos + c) : -2);
         }
-        carry = (int)min((int64_t)carry + total, max_chunks);
+        carry = min(carry + total, max_chunks);
+        pcarry += ptotal;
         __syncthreads();
     }
-    if (tid == 0) header[0] = carry;
+    if (tid == 0) header[0] = (int)carry;
 }
 
 // ---------------------------------------------------------------------- FPS
@@ -215,6 +236,19 @@ __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
 }
 
 // ------------------------------------ single-workgroup FPS, candidate list
+
+constexpr int kStage = 6144;              // feature floats an event may stage in LDS
+constexpr int kStageR = kStage / kFpsT;   // staged floats per thread
+
+// Feature rows of a single-workgroup event, copied to LDS while its FPS
+// runs (nf = 0: none).  The loads are issued once the pulses are in
+// registers; the FPS loop itself issues no global loads, so they complete
+// in its shadow and are written to `dst` after the last iteration.
+struct Stage {
+    const float* src;  // the event's first feature row
+    int nf;            // floats to copy (n * C), at most kStage
+    float* dst;        // LDS
+};
 
 constexpr int kListCap = 64;  // entries of the candidate list (one per lane)
 constexpr int kNoEntry = (int)0xBF800000;  // bit pattern of -1.0f: an empty entry
@@ -284,7 +318,8 @@ __device__ __forceinline__ int first_unselected_lds(uint32_t* bm, const int* s_s
 // j) and flushed to LDS by wave 0 every 64 iterations.
 template <int M>
 __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64_t off, int n,
-                                           int s0, FpsLds& L, int* s_sel, int* s_asg) {
+                                           int s0, FpsLds& L, int* s_sel, int* s_asg,
+                                           const Stage& st) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -321,6 +356,11 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
         cz = readlane_f(q.z, 0);
         ct = readlane_f(q.w, 0);
     }
+    float fr[kStageR];
+    const int sr = __builtin_amdgcn_readfirstlane((st.nf + kFpsT - 1) / kFpsT);
+#pragma unroll
+    for (int r = 0; r < kStageR; ++r)
+        if (r < sr) fr[r] = st.src[min(tid + kFpsT * r, st.nf - 1)];
     int j = 0;
     for (;;) {
         // ---- a run of iterations decided by the list
@@ -490,24 +530,28 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             if (i < n) s_asg[i] = nr[k];
         }
     }
+#pragma unroll
+    for (int r = 0; r < kStageR; ++r)
+        if (r < sr && tid + kFpsT * r < st.nf) st.dst[tid + kFpsT * r] = fr[r];
     write_selection(a, b, p, s_sel);
 }
 
 __device__ __forceinline__ void fps_single_dispatch(const SampleArgs& a, int64_t b, int64_t off,
-                                                    int n, int s0, FpsLds& L, int* ss, int* sa) {
+                                                    int n, int s0, FpsLds& L, int* ss, int* sa,
+                                                    const Stage& st) {
     switch ((n + kFpsT - 1) / kFpsT) {
-        case 1: fps_single<1>(a, b, off, n, s0, L, ss, sa); break;
-        case 2: fps_single<2>(a, b, off, n, s0, L, ss, sa); break;
-        case 3: fps_single<3>(a, b, off, n, s0, L, ss, sa); break;
-        case 4: fps_single<4>(a, b, off, n, s0, L, ss, sa); break;
-        case 5: fps_single<5>(a, b, off, n, s0, L, ss, sa); break;
-        case 6: fps_single<6>(a, b, off, n, s0, L, ss, sa); break;
-        case 7: fps_single<7>(a, b, off, n, s0, L, ss, sa); break;
-        case 8: fps_single<8>(a, b, off, n, s0, L, ss, sa); break;
-        case 9: case 10: fps_single<10>(a, b, off, n, s0, L, ss, sa); break;
-        case 11: case 12: fps_single<12>(a, b, off, n, s0, L, ss, sa); break;
-        case 13: case 14: fps_single<14>(a, b, off, n, s0, L, ss, sa); break;
-        default: fps_single<16>(a, b, off, n, s0, L, ss, sa); break;
+        case 1: fps_single<1>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 2: fps_single<2>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 3: fps_single<3>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 4: fps_single<4>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 5: fps_single<5>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 6: fps_single<6>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 7: fps_single<7>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 8: fps_single<8>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 9: case 10: fps_single<10>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 11: case 12: fps_single<12>(a, b, off, n, s0, L, ss, sa, st); break;
+        case 13: case 14: fps_single<14>(a, b, off, n, s0, L, ss, sa, st); break;
+        default: fps_single<16>(a, b, off, n, s0, L, ss, sa, st); break;
     }
 }
 
@@ -1072,15 +1116,19 @@ struct ItemInfo {
     int lo, cnt;  // the shard's pulses
     int item0;    // work item of shard 0 (gangs)
     int par;      // gang record parity no shard reads any more (gangs)
+    bool staged;  // the event's feature rows were staged in LDS (single workgroup)
 };
 
 // Claim one work item and run FPS (or pass-through) for it.  s_asg, when not
 // null, receives the shard's Voronoi slots (register-resident paths only).
+// With `feats` given, a single-workgroup event of at most stage_cap feature
+// floats also gets its C-column feature rows copied to s_feat.
 __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item,
                                                 FpsSlot (*s_slots)[kFpsW], GangLds& s_gang,
-                                                int* s_sel, int* s_asg) {
+                                                int* s_sel, int* s_asg, const float* feats, int C,
+                                                int stage_cap, float* s_feat) {
     const int tid = threadIdx.x;
-    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0};
+    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0, false};
     // items are claimed in list order, so the shards of one gang go to
     // workgroups that start one after another: a gang whose workgroups wait
     // for a partner only ever waits for a workgroup that will start once
@@ -1121,7 +1169,9 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     int s0 = a.start_idx ? a.start_idx[b] : 0;
     if (s0 < 0 || s0 >= n) s0 = 0;
     if (n <= kFpsCap) {
-        fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg);
+        it.staged = feats != nullptr && (int64_t)(n + 1) * C <= stage_cap;
+        const Stage st{it.staged ? feats + off * C : nullptr, it.staged ? n * C : 0, s_feat};
+        fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg, st);
         it.kind = 1;
         it.cnt = n;
     } else if (n <= kGangMax * kFpsCap) {
@@ -1149,7 +1199,7 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
     __shared__ GangLds s_gang;
-    sample_item(a, &s_item, s_slots, s_gang, s_sel, nullptr);
+    sample_item(a, &s_item, s_slots, s_gang, s_sel, nullptr, nullptr, 0, 0, nullptr);
 }
 
 // ------------------------------------------------------------------- assign
@@ -1664,33 +1714,131 @@ __device__ __forceinline__ void pool_identity(const PoolArgs& a, int64_t b, int6
     }
 }
 
-// Voronoi pooling, one workgroup per event.  An event whose slots are the
-// identity (every pass-through event) pools each pulse on its own; otherwise
-// a stable sort by slot (permutation in LDS when it fits) and, for every
-// slot, the (weighted) mean of its members in ascending pulse order.
+constexpr int kCombU = 4;  // chunk records whose loads are issued together
+
+// Voronoi pooling over the chunk list of kPoolChunk pulses per chunk.
+//  * An event of one chunk (every event of up to kPoolChunk pulses) is
+//    pooled whole by its workgroup: identity events pulse by pulse, others
+//    by a stable sort by slot in LDS and every slot's (weighted) mean of its
+//    members in ascending pulse order.
+//  * A chunk of a larger event sorts its own pulses the same way and writes
+//    float64 partial sums per slot (weight, every column, member count) to
+//    its record.  The workgroup that finishes the event's last chunk (a
+//    counter per event) adds the records in chunk order and writes the
+//    means: each record is an ascending sum, so only the grouping at chunk
+//    boundaries differs from one ascending sum.
+//  * An event the records have no room for (malformed offsets only) is
+//    pooled whole by its first chunk's workgroup through device memory.
 __global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
     __shared__ int s_cnt[kSortW * kMaxP];
     __shared__ int s_off[kMaxP + 1];
-    __shared__ int s_perm[kLdsPerm];
-    const int64_t b = blockIdx.x;
+    __shared__ int s_asg[kPoolChunk];
+    __shared__ int s_tmp[kPoolChunk];
+    __shared__ int s_last;
+    static_assert(kPoolChunk == kLdsPerm, "the slot sorts hold one chunk in LDS");
+    const int c = blockIdx.x;
+    if (c >= a.header[0]) return;
+    const int64_t b = a.chunk_ev[c];
+    const int beg = a.chunk_beg[c];
+    const int part = a.chunk_part[c];
     int64_t off;
     int n;
     event_range(a.offsets, a.N, b, off, n);
     int T = a.token_count[b];
     T = T < 0 ? 0 : (T > a.P ? a.P : T);
     const int tid = threadIdx.x;
-    bool ident = n == T;
-    for (int i = tid; ident && i < n; i += kSortT) ident = a.assign[off + i] == i;
-    if (__syncthreads_and(ident)) {
-        pool_identity(a, b, off, T);
-        return;
-    }
-    if (n <= kLdsPerm) {
-        block_sort_by_token(a.assign + off, n, T, s_perm, s_cnt, s_off);
-        pool_slots_sorted(a, b, off, T, s_perm, s_off);
-    } else {
+    const int P = a.P;
+    const int C = a.C;
+    if (part == -2) {
+        if (beg != 0) return;
         block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
         pool_slots_sorted(a, b, off, T, a.perm + off, s_off);
+        return;
+    }
+    if (part == -1) {
+        bool ident = n == T;
+        for (int i = tid; ident && i < n; i += kSortT) ident = a.assign[off + i] == i;
+        if (__syncthreads_and(ident)) {
+            pool_identity(a, b, off, T);
+            return;
+        }
+    }
+    const int len = max(0, min(n - beg, kPoolChunk));
+    for (int i = tid; i < len; i += kSortT) s_asg[i] = a.assign[off + beg + i];
+    __syncthreads();
+    const int* perm = s_asg;
+    if (!block_sort_small(s_asg, len, T, s_tmp, s_cnt, s_off)) {
+        block_sort_by_token(s_asg, len, T, s_tmp, s_cnt, s_off);
+        perm = s_tmp;
+    }
+    if (part == -1) {
+        pool_slots_sorted(a, b, off, T, perm, s_off);
+        return;
+    }
+    // this chunk's record: per slot j < T, [W, S_0 .. S_{C-1}, count]
+    const int C2 = C + 2;
+    double* __restrict__ rec = a.part + (size_t)part * P * C2;
+    for (int j = tid; j < T; j += kSortT) {
+        const int mb = s_off[j], me = s_off[j + 1];
+        double W = 0.0;
+        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+            const int nc = min(kPoolCols, C - c0);
+            double S[kPoolCols];
+            pool_slot(a, off, mb, me, c0, nc, [&](int m) { return beg + perm[m]; }, W, S);
+#pragma unroll
+            for (int q = 0; q < kPoolCols; ++q)
+                if (q < nc) rec[(size_t)j * C2 + 1 + c0 + q] = S[q];
+        }
+        rec[(size_t)j * C2] = W;
+        rec[(size_t)j * C2 + C + 1] = (double)(me - mb);
+    }
+    // publish the record; the last chunk of the event to finish combines
+    __threadfence();
+    __syncthreads();
+    const int K = (n + kPoolChunk - 1) / kPoolChunk;
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(a.ev_cnt + b, 1, __ATOMIC_ACQ_REL,
+                                        __HIP_MEMORY_SCOPE_AGENT) == K - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    // one thread per slot: the records of the event's K chunks added in
+    // chunk order, kCombU chunks' loads in flight
+    const double* __restrict__ rec0 = a.part + (size_t)(part - beg / kPoolChunk) * P * C2;
+    const size_t stride = (size_t)P * C2;
+    for (int j = tid; j < P; j += kSortT) {
+        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+            const int nc = min(kPoolCols, C - c0);
+            double W = 0.0, M = 0.0, S[kPoolCols];
+#pragma unroll
+            for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
+            for (int k0 = 0; j < T && k0 < K; k0 += kCombU) {
+                double w4[kCombU], m4[kCombU], s4[kCombU][kPoolCols];
+#pragma unroll
+                for (int u = 0; u < kCombU; ++u) {
+                    if (k0 + u < K) {
+                        const double* __restrict__ r = rec0 + (k0 + u) * stride + (size_t)j * C2;
+                        w4[u] = r[0];
+                        m4[u] = r[C + 1];
+#pragma unroll
+                        for (int q = 0; q < kPoolCols; ++q)
+                            if (q < nc) s4[u][q] = r[1 + c0 + q];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kCombU; ++u) {
+                    if (k0 + u < K) {
+                        W += w4[u];
+                        M += m4[u];
+#pragma unroll
+                        for (int q = 0; q < kPoolCols; ++q)
+                            if (q < nc) S[q] += s4[u][q];
+                    }
+                }
+            }
+            pool_write(a, b, j, c0, nc, W, S);
+            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = (int)M;
+        }
     }
 }
 
@@ -1728,6 +1876,160 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
 
 // ------------------------------------------- fused FPS + Voronoi pooling
 
+constexpr int kBmW4 = 8;  // 128-bit words per bitmap row: events of up to 1024 pulses
+
+// Stable sort of a small event's pulses by slot through per-slot bitmaps
+// (bit i of row k: pulse i has slot k).  A pulse's rank among its slot's
+// members is the number of set bits of the row below its own, read from a
+// prefix of popcounts per 128-bit word plus one masked word, so the order
+// is ascending by construction, with no atomics on the order and no
+// per-member loops.  perm[s_off[k] + r] = r-th member of slot k.
+//   bm: LDS uint32[T * W4 * 4], W4 = ceil(n / 128) <= kBmW4;  pre4: LDS
+//   int[T * W4];  s_off: LDS int[T + 1];  perm: LDS int[n]
+__device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, int n, int T,
+                                                  uint32_t* bm, int* pre4, int* s_off,
+                                                  int* perm) {
+    __shared__ int s_ws[kSortW];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int W4 = (n + 127) >> 7;
+    uint4* bm4 = reinterpret_cast<uint4*>(bm);
+    for (int q = tid; q < T * W4; q += kSortT) bm4[q] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    for (int i = tid; i < n; i += kSortT) {
+        const int k = asg[i];
+        if ((unsigned)k < (unsigned)T) atomicOr(&bm[k * W4 * 4 + (i >> 5)], 1u << (i & 31));
+    }
+    __syncthreads();
+    // slot jj (threads own `per` consecutive slots): prefix popcounts of its
+    // row and its member count; then the exclusive scan of the counts
+    const int per = (T + kSortT - 1) / kSortT;
+    int loc[kMaxP / kSortT];
+    int local = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        int c = 0;
+        if (r < per && jj < T) {
+#pragma unroll
+            for (int w4 = 0; w4 < kBmW4; ++w4) {
+                if (w4 < W4) {
+                    const uint4 q = bm4[jj * W4 + w4];
+                    pre4[jj * W4 + w4] = c;
+                    c += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
+                }
+            }
+        }
+        loc[r] = c;
+        local += c;
+    }
+    const int incl = wave_incl_scan(local);
+    if (lane == 63) s_ws[wave] = incl;
+    __syncthreads();
+    int run = incl - local, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSortW; ++w) {
+        const int v = s_ws[w];
+        run += w < wave ? v : 0;
+        total += v;
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        if (r < per && jj < T) s_off[jj] = run;
+        run += loc[r];
+    }
+    if (tid == 0) s_off[T] = total;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kBmW4 * 128 / kSortT; ++r) {
+        const int i = tid + kSortT * r;
+        const int k = i < n ? asg[i] : -1;
+        if ((unsigned)k < (unsigned)T) {
+            const int w4 = i >> 7;
+            const uint4 q = bm4[k * W4 + w4];
+            const int sh = i & 127;  // bits of this 128-bit word below bit i
+            const uint32_t m0 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
+            const uint32_t m1 = sh >= 64 ? 0xFFFFFFFFu : (sh <= 32 ? 0u : (1u << (sh - 32)) - 1u);
+            const uint32_t m2 = sh >= 96 ? 0xFFFFFFFFu : (sh <= 64 ? 0u : (1u << (sh - 64)) - 1u);
+            const uint32_t m3 = sh <= 96 ? 0u : (1u << (sh - 96)) - 1u;
+            const int rank = pre4[k * W4 + w4] + __popc(q.x & m0) + __popc(q.y & m1) +
+                             __popc(q.z & m2) + __popc(q.w & m3);
+            perm[s_off[k] + rank] = i;
+        }
+    }
+    __syncthreads();
+}
+
+// Slot j's (weighted) mean of columns c0 .. c0+NC-1 from LDS rows, members
+// perm[beg .. end) in that order, kBatch at a time.  A batch is padded with
+// row n, which is all zero: adding 0.0 * 0.0 leaves a sum that started at
+// +0.0 unchanged, so the result is the same float64 sequence as
+// pool_slot_acc's.  The products of two floats are exact in float64, so the
+// fused multiply-add rounds once, like the separate add.
+template <int NC>
+__device__ __forceinline__ void pool_lds_cols(const PoolArgs& a, int64_t b, int j, int beg,
+                                              int end, int n, int c0,
+                                              const int* __restrict__ perm,
+                                              const float* __restrict__ rows) {
+    const int C = a.C;
+    const int wcol = a.weight_col;
+    double W = 0.0, S[NC];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) S[q] = 0.0;
+    for (int m0 = beg; m0 < end; m0 += kBatch) {
+        int idx[kBatch];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) idx[t] = m0 + t < end ? perm[m0 + t] : n;
+        float wv[kBatch], fv[kBatch][NC];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+            const float* __restrict__ row = rows + idx[t] * C;
+            wv[t] = wcol >= 0 ? row[wcol] : (idx[t] < n ? 1.0f : 0.0f);
+#pragma unroll
+            for (int q = 0; q < NC; ++q) fv[t][q] = row[c0 + q];
+        }
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+            const double wd = (double)wv[t];
+            W += wd;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[t][q], S[q]);
+        }
+    }
+    float* __restrict__ out = a.pooled + (b * a.P + j) * (int64_t)C + c0;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) out[q] = W != 0.0 ? (float)(S[q] / W) : 0.0f;
+}
+
+// Pooling of a single-workgroup event of n pulses whose members are sorted
+// by slot in LDS (perm, s_off) and whose feature rows are staged in LDS
+// (rows[i * C + c], followed by a zero row): every slot's (weighted) mean
+// in ascending member order, float64, from LDS instead of device memory.
+__device__ __forceinline__ void pool_slots_lds(const PoolArgs& a, int64_t b, int n,
+                                               const int* __restrict__ perm, const int* s_off,
+                                               const float* __restrict__ rows) {
+    const int P = a.P;
+    const int C = a.C;
+    for (int j = threadIdx.x; j < P; j += kFpsT) {
+        const int beg = s_off[j], end = s_off[j + 1];
+        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+            switch (min(kPoolCols, C - c0)) {
+                case 1: pool_lds_cols<1>(a, b, j, beg, end, n, c0, perm, rows); break;
+                case 2: pool_lds_cols<2>(a, b, j, beg, end, n, c0, perm, rows); break;
+                case 3: pool_lds_cols<3>(a, b, j, beg, end, n, c0, perm, rows); break;
+                case 4: pool_lds_cols<4>(a, b, j, beg, end, n, c0, perm, rows); break;
+                case 5: pool_lds_cols<5>(a, b, j, beg, end, n, c0, perm, rows); break;
+                case 6: pool_lds_cols<6>(a, b, j, beg, end, n, c0, perm, rows); break;
+                case 7: pool_lds_cols<7>(a, b, j, beg, end, n, c0, perm, rows); break;
+                default: pool_lds_cols<8>(a, b, j, beg, end, n, c0, perm, rows); break;
+            }
+        }
+        if (a.cell_count) a.cell_count[b * P + j] = end - beg;
+    }
+}
+
 // Tokenizer in one launch for Voronoi mode without Lloyd: every workgroup
 // claims a work item, runs FPS (or pass-through) and then pools its event
 // while other workgroups are still sampling.
@@ -1758,7 +2060,9 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
     int* s_cnt = s_asg + kFpsCap;
     int* s_off = s_cnt + kSortW * P;
     GangLds& s_gang = *reinterpret_cast<GangLds*>(s_perm);
-    const ItemInfo it = sample_item(a, &s_item, s_slots, s_gang, s_sel, s_asg);
+    float* s_feat = reinterpret_cast<float*>(s_off + P + 1);
+    const ItemInfo it = sample_item(a, &s_item, s_slots, s_gang, s_sel, s_asg, pa.features, pa.C,
+                                    pa.stage_cap, s_feat);
     if (it.b < 0) return;
     const int64_t b = it.b;
     const int64_t off = it.off;
@@ -1774,7 +2078,21 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         pool_slots_sorted(pa, b, off, P, pa.perm + off, s_off);
         return;
     }
+    if (it.staged)
+        for (int q = tid; q < C; q += kFpsT) s_feat[it.n * C + q] = 0.0f;  // the zero row
     __syncthreads();
+    if (it.kind == 1 && it.staged) {
+        // small event, rows in LDS: bitmap sort into s_asg[1024 ..), pooling
+        // from LDS (s_asg holds at most 1024 slots here)
+        const int W4 = (it.n + 127) >> 7;
+        if (it.n <= kBmW4 * 128 && P * W4 <= kFpsCap / 4) {
+            int* perm = s_asg + kBmW4 * 128;
+            block_sort_bitmap(s_asg, it.n, P, reinterpret_cast<uint32_t*>(s_perm),
+                              s_asg + 2 * kBmW4 * 128, s_off, perm);
+            pool_slots_lds(pa, b, it.n, perm, s_off, s_feat);
+            return;
+        }
+    }
     // the shard's pulses sorted by slot: in s_asg itself when every slot is
     // small, else in s_perm
     const int* sorted = s_asg;
@@ -1887,11 +2205,13 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
 static inline unsigned grid1(int64_t x) { return (unsigned)(x < 1 ? 1 : x); }
 
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                       const WorkspaceLayout& L, hipStream_t s) {
+                       const WorkspaceLayout& L, int chunk, bool pool, hipStream_t s) {
     char* base = (char*)ws;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N, L.max_chunks,
-                       (int32_t*)(base + L.header), (int32_t*)(base + L.chunk_ev),
-                       (int32_t*)(base + L.chunk_beg));
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N, chunk, L.max_chunks,
+                       L.max_parts, (int32_t*)(base + L.header), (int32_t*)(base + L.chunk_ev),
+                       (int32_t*)(base + L.chunk_beg),
+                       pool ? (int32_t*)(base + L.chunk_part) : nullptr,
+                       pool ? (int32_t*)(base + L.ev_cnt) : nullptr);
     return hipGetLastError();
 }
 
@@ -1909,9 +2229,14 @@ hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, h
     hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(1024), 0, s, a, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = sizeof(int) * ((size_t)kSortW * a.P + a.P + 1 + 2 * (size_t)kFpsCap);
+    // feature rows of small single-workgroup events are staged in LDS when
+    // that leaves two workgroups per CU their room
+    PoolArgs p = pa;
+    p.stage_cap = a.P <= 512 ? kStage : 0;
+    const size_t lds = sizeof(int) * ((size_t)kSortW * a.P + a.P + 1 + 2 * (size_t)kFpsCap) +
+                       sizeof(float) * (size_t)p.stage_cap;
     hipLaunchKernelGGL(tokenize_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), lds, s,
-                       a, pa);
+                       a, p);
     return hipGetLastError();
 }
 
@@ -1931,8 +2256,8 @@ hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(pool_voronoi_kernel, dim3(grid1(B)), dim3(kSortT), 0, s, a);
+hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s) {
+    hipLaunchKernelGGL(pool_voronoi_kernel, dim3(grid1(max_chunks)), dim3(kSortT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -225,6 +225,24 @@ def test_tokenize_workloads(oracle_mod, name):
                         label=name)
 
 
+def test_fused_lds_pooling(oracle_mod):
+    """Single-workgroup events whose feature rows are staged in LDS during
+    FPS: the bitmap slot sort and the LDS pooling, on both sides of their
+    limits (1024 pulses; (n + 1) * C staged floats of at most 6144) and for
+    every column count the LDS pooling specialises (1..8, more in passes),
+    charge-weighted, unit-charge and plain mean."""
+    ns = [129, 255, 256, 257, 640, 1023, 1024, 1025]
+    for C in (1, 3, 6, 8, 9, 13):
+        b = synth.icecube_events(ns, 300 + C, C=C)
+        cc = synth.CHARGE_COL if C > synth.CHARGE_COL else -1
+        _tokenize_vs_oracle(oracle_mod, b, 128, charge_col=cc, label="lds C=%d" % C)
+        _tokenize_vs_oracle(oracle_mod, b, 128, weighted=False, charge_col=cc,
+                            label="lds mean C=%d" % C)
+    b = synth.icecube_events([1024, 700, 65, 513], 331, C=6)
+    _tokenize_vs_oracle(oracle_mod, b, 64, charge_col=-1, label="lds P=64 unit charge")
+    _tokenize_vs_oracle(oracle_mod, b, 256, label="lds P=256")
+
+
 def test_tokenize_fused_edges(oracle_mod):
     """The fused Voronoi kernel on every path: pass-through, one workgroup,
     gangs (cooperative pooling across shards) and the streaming fallback."""

@@ -57,6 +57,8 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     at += align256((size_t)L.max_chunks * sizeof(int32_t));
     L.ev_cnt = at;
     at += align256((size_t)B * sizeof(int32_t));
+    L.big_ev = at;
+    at += align256(2 * (size_t)B * sizeof(int32_t));
     L.mind = at;
     at += align256((size_t)nn * sizeof(float));
     L.near = at;
@@ -205,8 +207,7 @@ FPSTOK_API fpstok_status fpstok_assign(const fpstok_batch* bt, const fpstok_para
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, kChunk, false,
-                               s);
+    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
     AssignArgs a{};
     a.coords = (const float4*)bt->coords;
@@ -266,8 +267,7 @@ FPSTOK_API fpstok_status fpstok_lloyd(const fpstok_batch* bt, const fpstok_param
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, kChunk, false,
-                               s);
+    hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
     LloydArgs u{};
     u.coords = (const float4*)bt->coords;
@@ -335,13 +335,18 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
     a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
     a.chunk_part = at<int32_t>(ws, L.chunk_part);
     a.ev_cnt = at<int32_t>(ws, L.ev_cnt);
+    a.big_ev = at<int32_t>(ws, L.big_ev);
+    a.B = bt->num_events;
+    // the combine kernel's blocks hold one thread per (field, slot)
+    a.comb_last = bt->num_features + 2 <= 256 ? kCombLast : (1 << 30);
     a.part = at<double>(ws, L.part);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (pr->assign_mode == FPSTOK_VORONOI) {
-        e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, kPoolChunk, true, s);
+        e = launch_plan_pool(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
         if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
         e = launch_pool_voronoi(a, L.max_chunks, s);
+        if (e == hipSuccess) e = launch_pool_combine(a, s);
     } else {
         e = launch_pool_knn(a, bt->num_events, s);
     }

@@ -17,6 +17,10 @@ constexpr int kChunk = 256;
 // workgroup does in LDS.
 constexpr int kPoolChunk = 4096;
 
+// Events of at most this many pooling chunks are finished by the workgroup
+// of their last chunk; larger ones by a separate combine kernel.
+constexpr int kCombLast = 4;
+
 // 64-bit words of one gang exchange record (one shard, one parity): 64
 // candidate entries of one word each, the shard's bound, padding.
 constexpr int kGangRecWords = 64 + 8;
@@ -28,6 +32,8 @@ struct WorkspaceLayout {
     size_t chunk_beg;   // int32[max_chunks]: first event-local pulse of each chunk
     size_t chunk_part;  // int32[max_chunks]: partial-sum record of each chunk (pooling)
     size_t ev_cnt;      // int32[B]: chunks of each event done so far (pooling)
+    size_t big_ev;      // int32[2][B]: events of more than kCombLast chunks and their first
+                        // record (pooling)
     size_t mind;        // float[N]: running min distance (large-event FPS)
     size_t near;        // int32[N]: running nearest slot (large-event FPS, no assign out)
     size_t perm;        // int32[N]: pulses sorted by token (Lloyd, pool)
@@ -126,26 +132,34 @@ struct PoolArgs {
     float* pooled;
     int32_t* cell_count;
     int32_t* perm;
-    const int32_t* header;      // chunked pooling: [0] = number of chunks
+    const int32_t* header;      // chunked pooling: [0] chunks, [4] events of > kCombLast chunks
     const int32_t* chunk_ev;    // chunked pooling: event of each chunk
     const int32_t* chunk_beg;   // chunked pooling: first event-local pulse of each chunk
     const int32_t* chunk_part;  // chunked pooling: record of each chunk (-1: one-chunk event)
     int32_t* ev_cnt;            // chunked pooling: finished chunks per event
+    const int32_t* big_ev;      // chunked pooling: [m] event, [B + m] first record, m < header[4]
+    int64_t B;                  // chunked pooling: events
+    int comb_last;              // chunked pooling: events of at most this many chunks are
+                                // finished by their last chunk's workgroup
     double* part;               // chunked pooling: [max_parts][P][C+2] partial sums
     int stage_cap;              // fused pooling: feature floats an event may stage in LDS
 };
 
-// Chunk list of every event: `chunk` pulses per chunk (kChunk for assign,
-// kPoolChunk for pooling).  With `pool` set, also the partial-sum records of
-// the chunks and zeroed per-event chunk counters.
+// Chunk list of every event, kChunk pulses per chunk (assign).
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                       const WorkspaceLayout& L, int chunk, bool pool, hipStream_t s);
+                       const WorkspaceLayout& L, hipStream_t s);
+// Pooling chunk list (kPoolChunk pulses per chunk, largest first), the
+// chunks' partial-sum records, cleared per-event counters and the list of
+// events for the combine kernel.
+hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
+                            const WorkspaceLayout& L, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s);
 hipError_t launch_assign(const AssignArgs& a, int64_t max_chunks, hipStream_t s);
 hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s);
+hipError_t launch_pool_combine(const PoolArgs& a, hipStream_t s);
 hipError_t launch_pool_knn(const PoolArgs& a, int64_t B, hipStream_t s);
 
 }  // namespace fpstok

@@ -128,24 +128,19 @@ __device__ __forceinline__ void mark_selected(uint32_t& selbits, int s) {
 
 // ------------------------------------------------------------------- planner
 
-// One workgroup of 1024 threads: split every event into chunks of `chunk`
+// One workgroup of 1024 threads: split every event into chunks of kChunk
 // pulses (an empty event gets one chunk so per-event work still runs) and
-// write the chunk list.  With `chunk_part` given (pooling), the chunks of
-// every event of more than one chunk also get consecutive partial-sum
-// records (-1: the event is one chunk), and `ev_cnt` is cleared.
+// write the chunk list.
 __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ offsets,
-                                                    int64_t B, int64_t N, int chunk,
-                                                    int64_t max_chunks, int64_t max_parts,
+                                                    int64_t B, int64_t N, int64_t max_chunks,
                                                     int32_t* __restrict__ header,
                                                     int32_t* __restrict__ chunk_ev,
-                                                    int32_t* __restrict__ chunk_beg,
-                                                    int32_t* __restrict__ chunk_part,
-                                                    int32_t* __restrict__ ev_cnt) {
-    __shared__ int s_wsum[16], s_psum[16];
+                                                    int32_t* __restrict__ chunk_beg) {
+    __shared__ int s_wsum[16];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
-    int64_t carry = 0, pcarry = 0;
+    int carry = 0;
     for (int64_t base = 0; base < B; base += 1024) {
         const int64_t b = base + tid;
         int nch = 0;
@@ -153,44 +148,112 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ 
             int64_t off;
             int n;
             event_range(offsets, N, b, off, n);
-            nch = n > 0 ? (n + chunk - 1) / chunk : 1;
-            if (ev_cnt) ev_cnt[b] = 0;
+            nch = n > 0 ? (n + kChunk - 1) / kChunk : 1;
         }
-        const int np = nch > 1 ? nch : 0;
-        const int incl = wave_incl_scan(nch);
-        const int pincl = wave_incl_scan(np);
-        if (lane == 63) {
-            s_wsum[wave] = incl;
-            s_psum[wave] = pincl;
-        }
+        int incl = wave_incl_scan(nch);
+        if (lane == 63) s_wsum[wave] = incl;
         __syncthreads();
-        int wbase = 0, total = 0, pbase = 0, ptotal = 0;
+        int wbase = 0, total = 0;
         for (int w = 0; w < 16; ++w) {
-            const int v = s_wsum[w], u = s_psum[w];
-            if (w < wave) {
-                wbase += v;
-                pbase += u;
-            }
+            int v = s_wsum[w];
+            if (w < wave) wbase += v;
             total += v;
-            ptotal += u;
         }
-        // malformed (overlapping) offsets can ask for more chunks or records
-        // than the lists hold; extra chunks are dropped and an event without
-        // room for its records is marked -2 (pooled whole by its first
-        // chunk), never written out of bounds
-        const int64_t pos = carry + wbase + incl - nch;
-        const int64_t ppos = pcarry + pbase + pincl - np;
-        const bool room = ppos + np <= max_parts;
+        // malformed (overlapping) offsets can ask for more chunks than the
+        // list holds; those are dropped rather than written out of bounds
+        const int64_t pos = (int64_t)carry + wbase + incl - nch;
         for (int c = 0; c < nch && pos + c < max_chunks; ++c) {
             chunk_ev[pos + c] = (int32_t)b;
-            chunk_beg[pos + c] = c * chunk;
-            if (chunk_part) chunk_part[pos + c] = nch == 1 ? -1 : (room ? (int)(ppos + c) : -2);
+            chunk_beg[pos + c] = c * kChunk;
         }
-        carry = min(carry + total, max_chunks);
-        pcarry += ptotal;
+        carry = (int)min((int64_t)carry + total, max_chunks);
         __syncthreads();
     }
-    if (tid == 0) header[0] = (int)carry;
+    if (tid == 0) header[0] = carry;
+}
+
+// The pooling chunk list (kPoolChunk pulses per chunk), one workgroup of
+// 1024 threads, largest first: every event's full chunks, then every
+// event's last, partial chunk (an empty event gets one empty chunk), so that
+// the long chunks start before the short ones.  The chunks of an event of
+// more than one chunk get consecutive partial-sum records (-1: the event is
+// one chunk), ev_cnt is cleared, and the events of more than kCombLast
+// chunks are listed in big_ev with their first record (count in header[4]).
+// Malformed (overlapping) offsets can ask for more chunks or records than
+// the lists hold: extra chunks are dropped, an event without room for its
+// records is marked -2 (summed whole by its first chunk), and a listed event
+// without room is listed as -1; nothing is written out of bounds.
+__global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restrict__ offsets,
+                                                         int64_t B, int64_t N, int64_t max_chunks,
+                                                         int64_t max_parts,
+                                                         int32_t* __restrict__ header,
+                                                         int32_t* __restrict__ chunk_ev,
+                                                         int32_t* __restrict__ chunk_beg,
+                                                         int32_t* __restrict__ chunk_part,
+                                                         int32_t* __restrict__ ev_cnt,
+                                                         int32_t* __restrict__ big_ev) {
+    __shared__ int s_sum[3][16];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    int64_t carry = 0;
+    int bcarry = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        int64_t pcarry = 0;
+        for (int64_t base = 0; base < B; base += 1024) {
+            const int64_t b = base + tid;
+            int nf = 0, tl = 0;
+            if (b < B) {
+                int64_t off;
+                int n;
+                event_range(offsets, N, b, off, n);
+                nf = n / kPoolChunk;
+                tl = n % kPoolChunk != 0 || n == 0 ? 1 : 0;
+                if (pass == 0) ev_cnt[b] = 0;
+            }
+            const int nch = nf + tl;
+            const int cnt = pass == 0 ? nf : tl;  // chunks this pass places
+            const int np = nch > 1 ? nch : 0;
+            const int nb = pass == 0 && nch > kCombLast ? 1 : 0;
+            const int v[3] = {cnt, np, nb};
+            int incl[3], pre[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                incl[q] = wave_incl_scan(v[q]);
+                if (lane == 63) s_sum[q][wave] = incl[q];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                for (int w = 0; w < 16; ++w) {
+                    const int x = s_sum[q][w];
+                    pre[q] += w < wave ? x : 0;
+                    tot[q] += x;
+                }
+            const int64_t pos = carry + pre[0] + incl[0] - cnt;
+            const int64_t ppos = pcarry + pre[1] + incl[1] - np;
+            const bool room = ppos + np <= max_parts;
+            for (int c = 0; c < cnt && pos + c < max_chunks; ++c) {
+                const int k = pass == 0 ? c : nf;  // chunk number inside the event
+                chunk_ev[pos + c] = (int32_t)b;
+                chunk_beg[pos + c] = k * kPoolChunk;
+                chunk_part[pos + c] = nch == 1 ? -1 : (room ? (int)(ppos + k) : -2);
+            }
+            if (nb) {
+                const int m = bcarry + pre[2] + incl[2] - 1;
+                big_ev[m] = room ? (int32_t)b : -1;
+                big_ev[B + m] = (int32_t)ppos;
+            }
+            carry = min(carry + tot[0], max_chunks);
+            pcarry += tot[1];
+            bcarry += tot[2];
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        header[0] = (int)carry;
+        header[4] = bcarry;
+    }
 }
 
 // ---------------------------------------------------------------------- FPS
@@ -1555,6 +1618,92 @@ __device__ __forceinline__ bool block_sort_small(int* asg, int n, int T, int* tm
     return true;
 }
 
+constexpr int kBmW4 = 8;  // 128-bit words per bitmap row: events of up to 1024 pulses
+
+// Stable sort of a small event's pulses by slot through per-slot bitmaps
+// (bit i of row k: pulse i has slot k).  A pulse's rank among its slot's
+// members is the number of set bits of the row below its own, read from a
+// prefix of popcounts per 128-bit word plus one masked word, so the order
+// is ascending by construction, with no atomics on the order and no
+// per-member loops.  perm[s_off[k] + r] = r-th member of slot k.
+//   bm: LDS uint32[T * W4 * 4], W4 = ceil(n / 128) <= kBmW4;  pre4: LDS
+//   int[T * W4];  s_off: LDS int[T + 1];  perm: LDS int[n]
+__device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, int n, int T,
+                                                  uint32_t* bm, int* pre4, int* s_off,
+                                                  int* perm) {
+    __shared__ int s_ws[kSortW];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int W4 = (n + 127) >> 7;
+    uint4* bm4 = reinterpret_cast<uint4*>(bm);
+    for (int q = tid; q < T * W4; q += kSortT) bm4[q] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    for (int i = tid; i < n; i += kSortT) {
+        const int k = asg[i];
+        if ((unsigned)k < (unsigned)T) atomicOr(&bm[k * W4 * 4 + (i >> 5)], 1u << (i & 31));
+    }
+    __syncthreads();
+    // slot jj (threads own `per` consecutive slots): prefix popcounts of its
+    // row and its member count; then the exclusive scan of the counts
+    const int per = (T + kSortT - 1) / kSortT;
+    int loc[kMaxP / kSortT];
+    int local = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        int c = 0;
+        if (r < per && jj < T) {
+#pragma unroll
+            for (int w4 = 0; w4 < kBmW4; ++w4) {
+                if (w4 < W4) {
+                    const uint4 q = bm4[jj * W4 + w4];
+                    pre4[jj * W4 + w4] = c;
+                    c += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
+                }
+            }
+        }
+        loc[r] = c;
+        local += c;
+    }
+    const int incl = wave_incl_scan(local);
+    if (lane == 63) s_ws[wave] = incl;
+    __syncthreads();
+    int run = incl - local, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSortW; ++w) {
+        const int v = s_ws[w];
+        run += w < wave ? v : 0;
+        total += v;
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        if (r < per && jj < T) s_off[jj] = run;
+        run += loc[r];
+    }
+    if (tid == 0) s_off[T] = total;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kBmW4 * 128 / kSortT; ++r) {
+        const int i = tid + kSortT * r;
+        const int k = i < n ? asg[i] : -1;
+        if ((unsigned)k < (unsigned)T) {
+            const int w4 = i >> 7;
+            const uint4 q = bm4[k * W4 + w4];
+            const int sh = i & 127;  // bits of this 128-bit word below bit i
+            const uint32_t m0 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
+            const uint32_t m1 = sh >= 64 ? 0xFFFFFFFFu : (sh <= 32 ? 0u : (1u << (sh - 32)) - 1u);
+            const uint32_t m2 = sh >= 96 ? 0xFFFFFFFFu : (sh <= 64 ? 0u : (1u << (sh - 64)) - 1u);
+            const uint32_t m3 = sh <= 96 ? 0u : (1u << (sh - 96)) - 1u;
+            const int rank = pre4[k * W4 + w4] + __popc(q.x & m0) + __popc(q.y & m1) +
+                             __popc(q.z & m2) + __popc(q.w & m3);
+            perm[s_off[k] + rank] = i;
+        }
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------------ Lloyd update
 
 // New centroids of one event's slots j = tid, tid+256, ... < T: the
@@ -1716,6 +1865,53 @@ __device__ __forceinline__ void pool_identity(const PoolArgs& a, int64_t b, int6
 
 constexpr int kCombU = 4;  // chunk records whose loads are issued together
 
+// The means of event b from the records of its K chunks (first record
+// p0): one thread per slot adds the records in chunk order, kCombU chunks'
+// loads in flight.
+__device__ __forceinline__ void pool_combine_records(const PoolArgs& a, int64_t b, int T, int K,
+                                                     int p0) {
+    const int tid = threadIdx.x;
+    const int P = a.P;
+    const int C = a.C;
+    const int C2 = C + 2;
+    const double* __restrict__ rec0 = a.part + (size_t)p0 * P * C2;
+    const size_t stride = (size_t)P * C2;
+    for (int j = tid; j < P; j += kSortT) {
+        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+            const int nc = min(kPoolCols, C - c0);
+            double W = 0.0, M = 0.0, S[kPoolCols];
+#pragma unroll
+            for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
+            for (int k0 = 0; j < T && k0 < K; k0 += kCombU) {
+                double w4[kCombU], m4[kCombU], s4[kCombU][kPoolCols];
+#pragma unroll
+                for (int u = 0; u < kCombU; ++u) {
+                    if (k0 + u < K) {
+                        const double* __restrict__ r = rec0 + (k0 + u) * stride + (size_t)j * C2;
+                        w4[u] = r[0];
+                        m4[u] = r[C + 1];
+#pragma unroll
+                        for (int q = 0; q < kPoolCols; ++q)
+                            if (q < nc) s4[u][q] = r[1 + c0 + q];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kCombU; ++u) {
+                    if (k0 + u < K) {
+                        W += w4[u];
+                        M += m4[u];
+#pragma unroll
+                        for (int q = 0; q < kPoolCols; ++q)
+                            if (q < nc) S[q] += s4[u][q];
+                    }
+                }
+            }
+            pool_write(a, b, j, c0, nc, W, S);
+            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = (int)M;
+        }
+    }
+}
+
 // Voronoi pooling over the chunk list of kPoolChunk pulses per chunk.
 //  * An event of one chunk (every event of up to kPoolChunk pulses) is
 //    pooled whole by its workgroup: identity events pulse by pulse, others
@@ -1793,51 +1989,260 @@ __global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
         rec[(size_t)j * C2 + C + 1] = (double)(me - mb);
     }
     // publish the record; the last chunk of the event to finish combines
+    // (events of more than comb_last chunks: the combine kernel)
+    const int K = (n + kPoolChunk - 1) / kPoolChunk;
+    if (K > a.comb_last) return;
     __threadfence();
     __syncthreads();
-    const int K = (n + kPoolChunk - 1) / kPoolChunk;
     if (tid == 0)
         s_last = __hip_atomic_fetch_add(a.ev_cnt + b, 1, __ATOMIC_ACQ_REL,
                                         __HIP_MEMORY_SCOPE_AGENT) == K - 1;
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    // one thread per slot: the records of the event's K chunks added in
-    // chunk order, kCombU chunks' loads in flight
-    const double* __restrict__ rec0 = a.part + (size_t)(part - beg / kPoolChunk) * P * C2;
-    const size_t stride = (size_t)P * C2;
-    for (int j = tid; j < P; j += kSortT) {
-        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-            const int nc = min(kPoolCols, C - c0);
-            double W = 0.0, M = 0.0, S[kPoolCols];
+    pool_combine_records(a, b, T, K, part - beg / kPoolChunk);
+}
+
+// ------------------------------------ chunked pooling through LDS (P <= 256)
+
+constexpr int kPoolLdsMaxP = kSortT;  // one thread per slot
+
+constexpr int kPreRows = 24;  // feature floats per thread held for the next piece
+constexpr int kLdsBatch = 4;  // members whose LDS rows are read together
+constexpr int kPreSlots = 4;  // slots per thread held for the next piece (pieces <= 1024)
+
+// Per-slot running sums of one chunk [beg, hi) of event b (thread j <-> slot
+// j < T), over the columns c0 .. c0+NC-1: the chunk is taken `sub` pulses
+// at a time; each piece's slots and feature rows are copied to LDS, sorted
+// by slot through bitmaps, and every slot's members of the piece are added
+// in ascending order from LDS, so each sum is one ascending sequence over
+// the chunk.  The next piece's loads are issued into registers before the
+// current piece is sorted and summed (sub * C <= 256 * kPreRows).
+//   s_asg: int[sub];  s_rows: float[(sub + 1) * C];  bm: uint32[T * sub / 32];
+//   pre4: int[T * sub / 128];  s_off: int[T + 1];  perm: int[sub]
+template <int NC>
+__device__ __forceinline__ void chunk_slot_sums(const PoolArgs& a, int64_t off, int beg, int hi,
+                                                int T, int c0, int sub, int* s_asg,
+                                                float* s_rows, uint32_t* bm, int* pre4,
+                                                int* s_off, int* perm, double& W,
+                                                double (&S)[NC], int& cnt) {
+    const int tid = threadIdx.x;
+    const int C = a.C;
+    const int wcol = a.weight_col;
+    W = 0.0;
+    cnt = 0;
 #pragma unroll
-            for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
-            for (int k0 = 0; j < T && k0 < K; k0 += kCombU) {
-                double w4[kCombU], m4[kCombU], s4[kCombU][kPoolCols];
+    for (int q = 0; q < NC; ++q) S[q] = 0.0;
+    int na[kPreSlots];
+    float nr[kPreRows];
+    // loads of the piece at s0 (indices clamped into the piece; only the
+    // first ns slots and ns * C floats are kept)
+    auto fetch = [&](int s0) {
+        const int ns = min(sub, hi - s0);
+        const int32_t* __restrict__ ag = a.assign + off + s0;
+        const float* __restrict__ fg = a.features + (off + s0) * (int64_t)C;
 #pragma unroll
-                for (int u = 0; u < kCombU; ++u) {
-                    if (k0 + u < K) {
-                        const double* __restrict__ r = rec0 + (k0 + u) * stride + (size_t)j * C2;
-                        w4[u] = r[0];
-                        m4[u] = r[C + 1];
+        for (int r = 0; r < kPreSlots; ++r) na[r] = ag[min(tid + kSortT * r, ns - 1)];
 #pragma unroll
-                        for (int q = 0; q < kPoolCols; ++q)
-                            if (q < nc) s4[u][q] = r[1 + c0 + q];
-                    }
+        for (int r = 0; r < kPreRows; ++r) nr[r] = fg[min(tid + kSortT * r, ns * C - 1)];
+    };
+    if (beg < hi) fetch(beg);
+    for (int s0 = beg; s0 < hi; s0 += sub) {
+        const int ns = min(sub, hi - s0);
+#pragma unroll
+        for (int r = 0; r < kPreSlots; ++r)
+            if (tid + kSortT * r < ns) s_asg[tid + kSortT * r] = na[r];
+#pragma unroll
+        for (int r = 0; r < kPreRows; ++r)
+            if (tid + kSortT * r < ns * C) s_rows[tid + kSortT * r] = nr[r];
+        for (int q = tid; q < C; q += kSortT) s_rows[ns * C + q] = 0.0f;
+        __syncthreads();
+        if (s0 + sub < hi) fetch(s0 + sub);
+        block_sort_bitmap(s_asg, ns, T, bm, pre4, s_off, perm);
+        if (tid < T) {
+            const int mb = s_off[tid], me = s_off[tid + 1];
+            cnt += me - mb;
+            for (int m0 = mb; m0 < me; m0 += kLdsBatch) {
+                int idx[kLdsBatch];
+#pragma unroll
+                for (int t = 0; t < kLdsBatch; ++t) idx[t] = m0 + t < me ? perm[m0 + t] : ns;
+                float wv[kLdsBatch], fv[kLdsBatch][NC];
+#pragma unroll
+                for (int t = 0; t < kLdsBatch; ++t) {
+                    const float* __restrict__ row = s_rows + idx[t] * C;
+                    wv[t] = wcol >= 0 ? row[wcol] : (idx[t] < ns ? 1.0f : 0.0f);
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) fv[t][q] = row[c0 + q];
                 }
 #pragma unroll
-                for (int u = 0; u < kCombU; ++u) {
-                    if (k0 + u < K) {
-                        W += w4[u];
-                        M += m4[u];
+                for (int t = 0; t < kLdsBatch; ++t) {
+                    const double wd = (double)wv[t];
+                    W += wd;
 #pragma unroll
-                        for (int q = 0; q < kPoolCols; ++q)
-                            if (q < nc) S[q] += s4[u][q];
-                    }
+                    for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[t][q], S[q]);
                 }
             }
-            pool_write(a, b, j, c0, nc, W, S);
-            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = (int)M;
+        }
+        __syncthreads();
+    }
+}
+
+// One column pass of a chunk: its sums, then either the means of a
+// one-chunk event (slots j < P, zeros beyond T) or the chunk's record.
+template <int NC>
+__device__ __forceinline__ void chunk_pass(const PoolArgs& a, int64_t b, int64_t off, int beg,
+                                           int hi, int T, int c0, int sub, int part, int* s_asg,
+                                           float* s_rows, uint32_t* bm, int* pre4, int* s_off,
+                                           int* perm) {
+    double W, S[NC];
+    int cnt;
+    chunk_slot_sums<NC>(a, off, beg, hi, T, c0, sub, s_asg, s_rows, bm, pre4, s_off, perm, W, S,
+                        cnt);
+    const int j = threadIdx.x;
+    const int P = a.P;
+    const int C = a.C;
+    if (part < 0) {
+        if (j < P) {
+            float* __restrict__ out = a.pooled + (b * P + j) * (int64_t)C + c0;
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+                out[q] = j < T && W != 0.0 ? (float)(S[q] / W) : 0.0f;
+            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = j < T ? cnt : 0;
+        }
+    } else if (j < T) {
+        const int C2 = C + 2;
+        double* __restrict__ r = a.part + ((size_t)part * P + j) * C2;
+        r[0] = W;
+#pragma unroll
+        for (int q = 0; q < NC; ++q) r[1 + c0 + q] = S[q];
+        if (c0 == 0) r[C + 1] = (double)cnt;
+    }
+}
+
+// Voronoi pooling over the chunk list (kPoolChunk pulses per chunk) for
+// P <= 256, every chunk summed through LDS in pieces of `sub` pulses:
+//  * an event of one chunk gets its means directly (identity events pulse
+//    by pulse);
+//  * a chunk of a larger event writes its record (weight, every column,
+//    member count per slot); the workgroup finishing the event's last chunk
+//    adds the records in chunk order;
+//  * an event without record space (malformed offsets only) is summed whole
+//    by its first chunk's workgroup.
+// Dynamic LDS: int s_asg[sub], int perm[sub], int s_off[P + 1], int
+// pre4[P * sub / 128], uint32 bm[P * sub / 32], float s_rows[(sub + 1) * C].
+__global__ __launch_bounds__(kSortT) void pool_voronoi_lds_kernel(PoolArgs a, int sub) {
+    extern __shared__ __align__(16) int s_dyn[];
+    __shared__ int s_last;
+    const int c = blockIdx.x;
+    if (c >= a.header[0]) return;
+    const int64_t b = a.chunk_ev[c];
+    const int beg = a.chunk_beg[c];
+    const int part = a.chunk_part[c];
+    int64_t off;
+    int n;
+    event_range(a.offsets, a.N, b, off, n);
+    int T = a.token_count[b];
+    T = T < 0 ? 0 : (T > a.P ? a.P : T);
+    const int tid = threadIdx.x;
+    const int P = a.P;
+    const int C = a.C;
+    if (part == -2 && beg != 0) return;
+    if (part == -1) {
+        bool ident = n == T;
+        for (int i = tid; ident && i < n; i += kSortT) ident = a.assign[off + i] == i;
+        if (__syncthreads_and(ident)) {
+            pool_identity(a, b, off, T);
+            return;
+        }
+    }
+    const int W4 = sub >> 7;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(s_dyn);       // P * W4 * 4
+    int* pre4 = s_dyn + P * W4 * 4;                           // P * W4
+    int* s_asg = pre4 + P * W4;                               // sub
+    int* perm = s_asg + sub;                                  // sub
+    int* s_off = perm + sub;                                  // P + 1
+    float* s_rows = reinterpret_cast<float*>(s_off + P + 1);  // (sub + 1) * C
+    const int hi = part == -2 ? n : min(n, beg + kPoolChunk);
+    const int rpart = part == -2 ? -1 : part;
+    for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+        switch (min(kPoolCols, C - c0)) {
+#define FPSTOK_CHUNK_PASS(NC)                                                                  \
+    case NC:                                                                                 \
+        chunk_pass<NC>(a, b, off, beg, hi, T, c0, sub, rpart, s_asg, s_rows, bm, pre4, s_off, \
+                       perm);                                                                \
+        break;
+            FPSTOK_CHUNK_PASS(1)
+            FPSTOK_CHUNK_PASS(2)
+            FPSTOK_CHUNK_PASS(3)
+            FPSTOK_CHUNK_PASS(4)
+            FPSTOK_CHUNK_PASS(5)
+            FPSTOK_CHUNK_PASS(6)
+            FPSTOK_CHUNK_PASS(7)
+            default: FPSTOK_CHUNK_PASS(8)
+#undef FPSTOK_CHUNK_PASS
+        }
+    }
+    if (rpart < 0) return;
+    // publish the record; the last chunk of the event to finish combines
+    // (events of more than comb_last chunks: the combine kernel)
+    const int K = (n + kPoolChunk - 1) / kPoolChunk;
+    if (K > a.comb_last) return;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(a.ev_cnt + b, 1, __ATOMIC_ACQ_REL,
+                                        __HIP_MEMORY_SCOPE_AGENT) == K - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    pool_combine_records(a, b, T, K, part - beg / kPoolChunk);
+}
+
+// Means of the events of more than comb_last chunks from their chunks'
+// records: block (event m, slot group) with threads (field f, slot js);
+// field 0 is the weight, 1..C the columns, C+1 the member count; every
+// thread adds its value over the K records in chunk order, 16 loads in
+// flight.
+__global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a) {
+    __shared__ double s_W[256];
+    const int m = blockIdx.x;
+    if (m >= a.header[4]) return;
+    const int b = a.big_ev[m];
+    if (b < 0) return;
+    const int p0 = a.big_ev[a.B + m];
+    int64_t off;
+    int n;
+    event_range(a.offsets, a.N, b, off, n);
+    const int K = (n + kPoolChunk - 1) / kPoolChunk;
+    int T = a.token_count[b];
+    T = T < 0 ? 0 : (T > a.P ? a.P : T);
+    const int P = a.P;
+    const int C = a.C;
+    const int C2 = C + 2;
+    const int f = threadIdx.x;
+    const int js = threadIdx.y;
+    const int j = blockIdx.y * blockDim.y + js;
+    double t = 0.0;
+    if (j < T) {
+        const double* __restrict__ r = a.part + ((size_t)p0 * P + j) * C2 + f;
+        const size_t stride = (size_t)P * C2;
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            double v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = k0 + u < K ? r[(size_t)(k0 + u) * stride] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (k0 + u < K) t += v[u];
+        }
+    }
+    if (f == 0) s_W[js] = t;
+    __syncthreads();
+    if (j < P) {
+        if (f >= 1 && f <= C) {
+            const double W = s_W[js];
+            a.pooled[((int64_t)b * P + j) * C + f - 1] = j < T && W != 0.0 ? (float)(t / W) : 0.0f;
+        } else if (f == C + 1 && a.cell_count) {
+            a.cell_count[(int64_t)b * P + j] = j < T ? (int)t : 0;
         }
     }
 }
@@ -1875,92 +2280,6 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
 }
 
 // ------------------------------------------- fused FPS + Voronoi pooling
-
-constexpr int kBmW4 = 8;  // 128-bit words per bitmap row: events of up to 1024 pulses
-
-// Stable sort of a small event's pulses by slot through per-slot bitmaps
-// (bit i of row k: pulse i has slot k).  A pulse's rank among its slot's
-// members is the number of set bits of the row below its own, read from a
-// prefix of popcounts per 128-bit word plus one masked word, so the order
-// is ascending by construction, with no atomics on the order and no
-// per-member loops.  perm[s_off[k] + r] = r-th member of slot k.
-//   bm: LDS uint32[T * W4 * 4], W4 = ceil(n / 128) <= kBmW4;  pre4: LDS
-//   int[T * W4];  s_off: LDS int[T + 1];  perm: LDS int[n]
-__device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, int n, int T,
-                                                  uint32_t* bm, int* pre4, int* s_off,
-                                                  int* perm) {
-    __shared__ int s_ws[kSortW];
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid >> 6;
-    const int W4 = (n + 127) >> 7;
-    uint4* bm4 = reinterpret_cast<uint4*>(bm);
-    for (int q = tid; q < T * W4; q += kSortT) bm4[q] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    for (int i = tid; i < n; i += kSortT) {
-        const int k = asg[i];
-        if ((unsigned)k < (unsigned)T) atomicOr(&bm[k * W4 * 4 + (i >> 5)], 1u << (i & 31));
-    }
-    __syncthreads();
-    // slot jj (threads own `per` consecutive slots): prefix popcounts of its
-    // row and its member count; then the exclusive scan of the counts
-    const int per = (T + kSortT - 1) / kSortT;
-    int loc[kMaxP / kSortT];
-    int local = 0;
-#pragma unroll
-    for (int r = 0; r < kMaxP / kSortT; ++r) {
-        const int jj = tid * per + r;
-        int c = 0;
-        if (r < per && jj < T) {
-#pragma unroll
-            for (int w4 = 0; w4 < kBmW4; ++w4) {
-                if (w4 < W4) {
-                    const uint4 q = bm4[jj * W4 + w4];
-                    pre4[jj * W4 + w4] = c;
-                    c += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
-                }
-            }
-        }
-        loc[r] = c;
-        local += c;
-    }
-    const int incl = wave_incl_scan(local);
-    if (lane == 63) s_ws[wave] = incl;
-    __syncthreads();
-    int run = incl - local, total = 0;
-#pragma unroll
-    for (int w = 0; w < kSortW; ++w) {
-        const int v = s_ws[w];
-        run += w < wave ? v : 0;
-        total += v;
-    }
-#pragma unroll
-    for (int r = 0; r < kMaxP / kSortT; ++r) {
-        const int jj = tid * per + r;
-        if (r < per && jj < T) s_off[jj] = run;
-        run += loc[r];
-    }
-    if (tid == 0) s_off[T] = total;
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kBmW4 * 128 / kSortT; ++r) {
-        const int i = tid + kSortT * r;
-        const int k = i < n ? asg[i] : -1;
-        if ((unsigned)k < (unsigned)T) {
-            const int w4 = i >> 7;
-            const uint4 q = bm4[k * W4 + w4];
-            const int sh = i & 127;  // bits of this 128-bit word below bit i
-            const uint32_t m0 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
-            const uint32_t m1 = sh >= 64 ? 0xFFFFFFFFu : (sh <= 32 ? 0u : (1u << (sh - 32)) - 1u);
-            const uint32_t m2 = sh >= 96 ? 0xFFFFFFFFu : (sh <= 64 ? 0u : (1u << (sh - 64)) - 1u);
-            const uint32_t m3 = sh <= 96 ? 0u : (1u << (sh - 96)) - 1u;
-            const int rank = pre4[k * W4 + w4] + __popc(q.x & m0) + __popc(q.y & m1) +
-                             __popc(q.z & m2) + __popc(q.w & m3);
-            perm[s_off[k] + rank] = i;
-        }
-    }
-    __syncthreads();
-}
 
 // Slot j's (weighted) mean of columns c0 .. c0+NC-1 from LDS rows, members
 // perm[beg .. end) in that order, kBatch at a time.  A batch is padded with
@@ -2205,13 +2524,34 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
 static inline unsigned grid1(int64_t x) { return (unsigned)(x < 1 ? 1 : x); }
 
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                       const WorkspaceLayout& L, int chunk, bool pool, hipStream_t s) {
+                       const WorkspaceLayout& L, hipStream_t s) {
     char* base = (char*)ws;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N, chunk, L.max_chunks,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N, L.max_chunks,
+                       (int32_t*)(base + L.header), (int32_t*)(base + L.chunk_ev),
+                       (int32_t*)(base + L.chunk_beg));
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
+                            const WorkspaceLayout& L, hipStream_t s) {
+    char* base = (char*)ws;
+    hipLaunchKernelGGL(plan_pool_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N, L.max_chunks,
                        L.max_parts, (int32_t*)(base + L.header), (int32_t*)(base + L.chunk_ev),
-                       (int32_t*)(base + L.chunk_beg),
-                       pool ? (int32_t*)(base + L.chunk_part) : nullptr,
-                       pool ? (int32_t*)(base + L.ev_cnt) : nullptr);
+                       (int32_t*)(base + L.chunk_beg), (int32_t*)(base + L.chunk_part),
+                       (int32_t*)(base + L.ev_cnt), (int32_t*)(base + L.big_ev));
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_combine(const PoolArgs& a, hipStream_t s) {
+    if (a.comb_last >= (1 << 30)) return hipSuccess;
+    // events of more than comb_last chunks hold more than comb_last *
+    // kPoolChunk pulses
+    const int64_t big = std::min<int64_t>(a.B, a.N / ((int64_t)a.comb_last * kPoolChunk + 1));
+    if (big <= 0) return hipSuccess;
+    const int C2 = a.C + 2;
+    const int spg = 256 / C2;
+    hipLaunchKernelGGL(pool_combine_kernel, dim3((unsigned)big, (unsigned)((a.P + spg - 1) / spg)),
+                       dim3(C2, spg), 0, s, a);
     return hipGetLastError();
 }
 
@@ -2256,7 +2596,29 @@ hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Dynamic LDS of pool_voronoi_lds_kernel for pieces of `sub` pulses.
+static size_t pool_lds_bytes(int P, int C, int sub) {
+    const size_t w4 = (size_t)sub / 128;
+    return sizeof(int) * ((size_t)P * w4 * 5 + 2 * (size_t)sub + P + 1) +
+           sizeof(float) * ((size_t)sub + 1) * C;
+}
+
 hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s) {
+    if (a.P <= kPoolLdsMaxP) {
+        // the largest piece (at most 1024 pulses, a multiple of 128) whose
+        // rows the threads can hold in registers and whose LDS leaves room
+        // for two workgroups per CU
+        // 1024-pulse pieces, when the threads can hold a piece's rows in
+        // registers and two workgroups per CU fit in LDS; otherwise (wide
+        // rows) gathering members from device memory is faster
+        const int sub = 1024;
+        if ((int64_t)sub * a.C <= (int64_t)kSortT * kPreRows &&
+            pool_lds_bytes(a.P, a.C, sub) <= 80 * 1024) {
+            hipLaunchKernelGGL(pool_voronoi_lds_kernel, dim3(grid1(max_chunks)), dim3(kSortT),
+                               pool_lds_bytes(a.P, a.C, sub), s, a, sub);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL(pool_voronoi_kernel, dim3(grid1(max_chunks)), dim3(kSortT), 0, s, a);
     return hipGetLastError();
 }

@@ -243,6 +243,20 @@ def test_fused_lds_pooling(oracle_mod):
     _tokenize_vs_oracle(oracle_mod, b, 256, label="lds P=256")
 
 
+def test_pool_chunk_combines(oracle_mod):
+    """Standalone Voronoi pooling over 4096-pulse chunks: one-chunk events
+    summed in pieces through LDS, events of 2..4 chunks finished by their
+    last chunk's workgroup, larger ones by the combine kernel; P <= 256 (LDS
+    pieces, narrow and wide rows) and P > 256 (the sort path)."""
+    ns = [4096, 4097, 8192, 12289, 16384, 16385, 40000, 300]
+    for C, P in ((6, 128), (6, 256), (16, 128), (3, 300)):
+        b = synth.icecube_events(ns, 400 + C + P, C=C)
+        cc = synth.CHARGE_COL if C > synth.CHARGE_COL else -1
+        check_pipeline(oracle_mod, b, P=P, charge_col=cc, label="pool chunks C=%d P=%d" % (C, P))
+    b = synth.icecube_events([70000, 20000], 431, C=6)
+    check_pipeline(oracle_mod, b, P=256, weighted=False, label="pool chunks plain mean")
+
+
 def test_tokenize_fused_edges(oracle_mod):
     """The fused Voronoi kernel on every path: pass-through, one workgroup,
     gangs (cooperative pooling across shards) and the streaming fallback."""

@@ -37,6 +37,17 @@ VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12
 # (the float32 squared distance), 1 running-min update, 1 fused Voronoi
 # select, 1 argmax compare
 FPS_OPS_PER_POINT_ITER = 14
+# HBM bytes of one fpstok_tokenize call on the headline workload
+# (plan_fps_kernel + tokenize_kernel), from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE per dispatch, each scaled by its reading for a plain
+# device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
+# 2 * (439.9 + 4.0) KiB, writes 418.6 + 0.5 KiB.  Valid only for the kernel
+# source it was taken on; reported as null for any other.
+MEASURED_TRAFFIC = {
+    "workload": HEADLINE,
+    "kernels_sha256": "bb0b5717ed77550956d9723be0b48ca01763b6c315036d3e54b7f725ee4479b8",
+    "bytes": int(round((2 * (439.9 + 4.0) + (418.6 + 0.5)) * 1024)),
+}
 
 
 def log(msg):
@@ -192,12 +203,25 @@ def cpu_baseline(b, budget_s):
                     reps, B, el))
 
 
-def fps_roofline(st, seconds, kernel):
+def measured_traffic(workload):
+    """HBM bytes per call from the committed counter runs, when they were taken
+    on this workload and on the kernel source now in the package; else None."""
+    import hashlib
+
+    src = os.path.join(ROOT, "point_cloud_tokenization_amd", "csrc", "fpstok_kernels.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if workload != MEASURED_TRAFFIC["workload"] or sha != MEASURED_TRAFFIC["kernels_sha256"]:
+        return None
+    return MEASURED_TRAFFIC["bytes"]
+
+
+def fps_roofline(st, seconds, kernel, traffic=None):
     """FPS algorithmic VALU lane-ops per launch over the launch duration."""
     ops = st["point_iters"] * FPS_OPS_PER_POINT_ITER
     ach = ops / seconds / 1e12
     return dict(bound="alu", achieved=ach, peak=VALU_PEAK_TOPS, unit="TOP/s",
-                frac=ach / VALU_PEAK_TOPS, traffic=None, kernel=kernel)
+                frac=ach / VALU_PEAK_TOPS, traffic=traffic, kernel=kernel)
 
 
 def main():
@@ -256,7 +280,8 @@ def main():
     roof = fps_roofline(st, step_gpu if fused else per_call["sample"],
                         "fpstok_tokenize call: plan_fps_kernel + tokenize_kernel (FPS + fused "
                         "Voronoi pooling)" if fused else "fpstok_sample call: plan_fps_kernel + "
-                        "sample_kernel (FPS)")
+                        "sample_kernel (FPS)",
+                        measured_traffic(args.workload) if fused else None)
     log("per-step GPU %.1f us; per call (stepwise) %s" % (
         step_gpu * 1e6, {c: round(v * 1e6, 1) for c, v in per_call.items()}))
 

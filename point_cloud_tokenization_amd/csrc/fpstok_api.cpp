@@ -53,8 +53,13 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     at += align256((size_t)L.max_chunks * sizeof(int32_t));
     L.chunk_beg = at;
     at += align256((size_t)L.max_chunks * sizeof(int32_t));
+    L.max_pool_chunks = nn / kPoolChunk + B;
+    L.pool_ev = at;
+    at += align256((size_t)L.max_pool_chunks * sizeof(int32_t));
+    L.pool_beg = at;
+    at += align256((size_t)L.max_pool_chunks * sizeof(int32_t));
     L.chunk_part = at;
-    at += align256((size_t)L.max_chunks * sizeof(int32_t));
+    at += align256((size_t)L.max_pool_chunks * sizeof(int32_t));
     L.ev_cnt = at;
     at += align256((size_t)B * sizeof(int32_t));
     L.big_ev = at;
@@ -145,6 +150,108 @@ static T* at(void* ws, size_t off) {
     return (T*)((char*)ws + off);
 }
 
+static SampleArgs sample_args(const fpstok_batch* bt, const fpstok_params* pr,
+                              const int32_t* start_idx, int32_t* centroid_idx, float* centroids,
+                              int32_t* token_count, int32_t* assign, void* ws,
+                              const WorkspaceLayout& L) {
+    SampleArgs a{};
+    a.coords = (const float4*)bt->coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.start_idx = start_idx;
+    a.centroid_idx = centroid_idx;
+    a.centroids = (float4*)centroids;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.ws_mind = at<float>(ws, L.mind);
+    a.ws_near = at<int32_t>(ws, L.near);
+    a.header = at<int32_t>(ws, L.header);
+    a.item_ev = at<int32_t>(ws, L.item_ev);
+    a.item_g = at<int32_t>(ws, L.item_g);
+    a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
+    a.shard_cells = at<int32_t>(ws, L.shard_cells);
+    a.gang_part = at<double>(ws, L.part);
+    return a;
+}
+
+static PoolArgs pool_args(const fpstok_batch* bt, const fpstok_params* pr,
+                          const int32_t* token_count, const int32_t* assign,
+                          const int32_t* knn_idx, float* pooled, int32_t* cell_count, void* ws,
+                          const WorkspaceLayout& L) {
+    PoolArgs a{};
+    a.features = bt->features;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.C = bt->num_features;
+    a.weight_col = pr->pool_weighted ? bt->charge_col : -1;
+    a.P = pr->num_patches;
+    a.k = pr->k;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.knn_idx = knn_idx;
+    a.pooled = pooled;
+    a.cell_count = cell_count;
+    a.perm = at<int32_t>(ws, L.perm);
+    a.header = at<int32_t>(ws, L.header);
+    a.chunk_ev = at<int32_t>(ws, L.pool_ev);
+    a.chunk_beg = at<int32_t>(ws, L.pool_beg);
+    a.chunk_part = at<int32_t>(ws, L.chunk_part);
+    a.ev_cnt = at<int32_t>(ws, L.ev_cnt);
+    a.big_ev = at<int32_t>(ws, L.big_ev);
+    a.B = bt->num_events;
+    // the combine kernel's blocks hold one thread per (field, slot)
+    a.comb_last = bt->num_features + 2 <= 256 ? kCombLast : (1 << 30);
+    a.part = at<double>(ws, L.part);
+    return a;
+}
+
+// The Lloyd rounds once the assign chunk list is planned.
+static hipError_t run_lloyd(const fpstok_batch* bt, const fpstok_params* pr, float* centroids,
+                            const int32_t* token_count, int32_t* assign, void* ws,
+                            const WorkspaceLayout& L, hipStream_t s) {
+    LloydArgs u{};
+    u.coords = (const float4*)bt->coords;
+    u.features = bt->features;
+    u.offsets = bt->offsets;
+    u.N = bt->num_points;
+    u.C = bt->num_features;
+    u.charge_col = bt->charge_col;
+    u.P = pr->num_patches;
+    u.centroids = (float4*)centroids;
+    u.token_count = token_count;
+    u.assign = assign;
+    u.perm = at<int32_t>(ws, L.perm);
+    AssignArgs a{};
+    a.coords = u.coords;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.P = pr->num_patches;
+    a.centroids = (const float4*)centroids;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.header = at<int32_t>(ws, L.header);
+    a.chunk_ev = at<int32_t>(ws, L.chunk_ev);
+    a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
+    a.skip_small = 1;
+    for (int it = 0; it < pr->lloyd_iters; ++it) {
+        hipError_t e = launch_lloyd_update(u, bt->num_events, s);
+        if (e != hipSuccess) return e;
+        e = launch_assign(a, L.max_chunks, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// The pooling kernels once the pooling chunk list is planned.
+static hipError_t run_pool(const fpstok_batch* bt, const fpstok_params* pr, const PoolArgs& a,
+                           const WorkspaceLayout& L, hipStream_t s) {
+    if (pr->assign_mode != FPSTOK_VORONOI) return launch_pool_knn(a, bt->num_events, s);
+    hipError_t e = launch_pool_voronoi(a, L.max_pool_chunks, s);
+    if (e == hipSuccess) e = launch_pool_combine(a, s);
+    return e;
+}
+
 }  // namespace fpstok
 
 using namespace fpstok;
@@ -171,24 +278,8 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
-    SampleArgs a{};
-    a.coords = (const float4*)bt->coords;
-    a.offsets = bt->offsets;
-    a.N = bt->num_points;
-    a.P = pr->num_patches;
-    a.start_idx = start_idx;
-    a.centroid_idx = centroid_idx;
-    a.centroids = (float4*)centroids;
-    a.token_count = token_count;
-    a.assign = assign;
-    a.ws_mind = at<float>(ws, L.mind);
-    a.ws_near = at<int32_t>(ws, L.near);
-    a.header = at<int32_t>(ws, L.header);
-    a.item_ev = at<int32_t>(ws, L.item_ev);
-    a.item_g = at<int32_t>(ws, L.item_g);
-    a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
-    a.shard_cells = at<int32_t>(ws, L.shard_cells);
-    a.gang_part = at<double>(ws, L.part);
+    const SampleArgs a = sample_args(bt, pr, start_idx, centroid_idx, centroids, token_count,
+                                     assign, ws, L);
     hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
     return ok();
@@ -269,36 +360,8 @@ FPSTOK_API fpstok_status fpstok_lloyd(const fpstok_batch* bt, const fpstok_param
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
-    LloydArgs u{};
-    u.coords = (const float4*)bt->coords;
-    u.features = bt->features;
-    u.offsets = bt->offsets;
-    u.N = bt->num_points;
-    u.C = bt->num_features;
-    u.charge_col = bt->charge_col;
-    u.P = pr->num_patches;
-    u.centroids = (float4*)centroids;
-    u.token_count = token_count;
-    u.assign = assign;
-    u.perm = at<int32_t>(ws, L.perm);
-    AssignArgs a{};
-    a.coords = u.coords;
-    a.offsets = bt->offsets;
-    a.N = bt->num_points;
-    a.P = pr->num_patches;
-    a.centroids = (const float4*)centroids;
-    a.token_count = token_count;
-    a.assign = assign;
-    a.header = at<int32_t>(ws, L.header);
-    a.chunk_ev = at<int32_t>(ws, L.chunk_ev);
-    a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
-    a.skip_small = 1;
-    for (int it = 0; it < pr->lloyd_iters; ++it) {
-        e = launch_lloyd_update(u, bt->num_events, s);
-        if (e != hipSuccess) return hip_fail(e, "lloyd update kernel launch");
-        e = launch_assign(a, L.max_chunks, s);
-        if (e != hipSuccess) return hip_fail(e, "assign kernel launch");
-    }
+    e = run_lloyd(bt, pr, centroids, token_count, assign, ws, L, s);
+    if (e != hipSuccess) return hip_fail(e, "lloyd kernel launch");
     return ok();
 }
 
@@ -316,40 +379,14 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
         return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
-    PoolArgs a{};
-    a.features = bt->features;
-    a.offsets = bt->offsets;
-    a.N = bt->num_points;
-    a.C = bt->num_features;
-    a.weight_col = pr->pool_weighted ? bt->charge_col : -1;
-    a.P = pr->num_patches;
-    a.k = pr->k;
-    a.token_count = token_count;
-    a.assign = assign;
-    a.knn_idx = knn_idx;
-    a.pooled = pooled;
-    a.cell_count = cell_count;
-    a.perm = at<int32_t>(ws, L.perm);
-    a.header = at<int32_t>(ws, L.header);
-    a.chunk_ev = at<int32_t>(ws, L.chunk_ev);
-    a.chunk_beg = at<int32_t>(ws, L.chunk_beg);
-    a.chunk_part = at<int32_t>(ws, L.chunk_part);
-    a.ev_cnt = at<int32_t>(ws, L.ev_cnt);
-    a.big_ev = at<int32_t>(ws, L.big_ev);
-    a.B = bt->num_events;
-    // the combine kernel's blocks hold one thread per (field, slot)
-    a.comb_last = bt->num_features + 2 <= 256 ? kCombLast : (1 << 30);
-    a.part = at<double>(ws, L.part);
+    const PoolArgs a = pool_args(bt, pr, token_count, assign, knn_idx, pooled, cell_count, ws, L);
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
+    hipError_t e = hipSuccess;
     if (pr->assign_mode == FPSTOK_VORONOI) {
         e = launch_plan_pool(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
         if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
-        e = launch_pool_voronoi(a, L.max_chunks, s);
-        if (e == hipSuccess) e = launch_pool_combine(a, s);
-    } else {
-        e = launch_pool_knn(a, bt->num_events, s);
     }
+    e = run_pool(bt, pr, a, L, s);
     if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
     return ok();
 }
@@ -372,53 +409,29 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     if (!voronoi && !knn_idx) return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    const SampleArgs a = sample_args(bt, pr, start_idx, centroid_idx, centroids, token_count,
+                                     assign, ws, L);
+    hipStream_t s = (hipStream_t)stream;
     if (!voronoi || pr->lloyd_iters > 0) {
-        // the calls one after another on the same stream and workspace
-        if ((st = fpstok_sample(bt, pr, start_idx, centroid_idx, centroids, token_count, assign,
-                                ws, ws_bytes, stream)) != FPSTOK_OK)
-            return st;
-        if ((st = fpstok_lloyd(bt, pr, centroids, token_count, assign, ws, ws_bytes, stream)) !=
-            FPSTOK_OK)
-            return st;
+        // sample -> Lloyd -> [kNN] -> pool on the same stream and workspace,
+        // every work list planned by one launch
+        const PoolArgs p = pool_args(bt, pr, token_count, assign, knn_idx, pooled, cell_count, ws,
+                                     L);
+        hipError_t e = launch_plan_all(a, bt->num_events, ws, L, p, pr->lloyd_iters > 0, voronoi, s);
+        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+        e = launch_sample_items(a, bt->num_events, s);
+        if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
+        e = run_lloyd(bt, pr, centroids, token_count, assign, ws, L, s);
+        if (e != hipSuccess) return hip_fail(e, "lloyd kernel launch");
         if (!voronoi && (st = fpstok_knn(bt, pr, centroids, token_count, knn_idx, ws, ws_bytes,
                                          stream)) != FPSTOK_OK)
             return st;
-        return fpstok_pool(bt, pr, token_count, assign, knn_idx, pooled, cell_count, ws, ws_bytes,
-                           stream);
+        e = run_pool(bt, pr, p, L, s);
+        if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+        return ok();
     }
-    SampleArgs a{};
-    a.coords = (const float4*)bt->coords;
-    a.offsets = bt->offsets;
-    a.N = bt->num_points;
-    a.P = pr->num_patches;
-    a.start_idx = start_idx;
-    a.centroid_idx = centroid_idx;
-    a.centroids = (float4*)centroids;
-    a.token_count = token_count;
-    a.assign = assign;
-    a.ws_mind = at<float>(ws, L.mind);
-    a.ws_near = at<int32_t>(ws, L.near);
-    a.header = at<int32_t>(ws, L.header);
-    a.item_ev = at<int32_t>(ws, L.item_ev);
-    a.item_g = at<int32_t>(ws, L.item_g);
-    a.gang_rec = at<unsigned long long>(ws, L.gang_rec);
-    a.shard_cells = at<int32_t>(ws, L.shard_cells);
-    a.gang_part = at<double>(ws, L.part);
-    PoolArgs p{};
-    p.features = bt->features;
-    p.offsets = bt->offsets;
-    p.N = bt->num_points;
-    p.C = bt->num_features;
-    p.weight_col = pr->pool_weighted ? bt->charge_col : -1;
-    p.P = pr->num_patches;
-    p.k = pr->k;
-    p.token_count = token_count;
-    p.assign = assign;
-    p.knn_idx = nullptr;
-    p.pooled = pooled;
-    p.cell_count = cell_count;
-    p.perm = at<int32_t>(ws, L.perm);
-    hipError_t e = launch_tokenize(a, p, bt->num_events, (hipStream_t)stream);
+    const PoolArgs p = pool_args(bt, pr, token_count, assign, nullptr, pooled, cell_count, ws, L);
+    hipError_t e = launch_tokenize(a, p, bt->num_events, s);
     if (e != hipSuccess) return hip_fail(e, "tokenize kernel launch");
     return ok();
 }

@@ -30,7 +30,9 @@ struct WorkspaceLayout {
     size_t header;      // int32[64]: [0] = number of chunks
     size_t chunk_ev;    // int32[max_chunks]: event of each chunk
     size_t chunk_beg;   // int32[max_chunks]: first event-local pulse of each chunk
-    size_t chunk_part;  // int32[max_chunks]: partial-sum record of each chunk (pooling)
+    size_t pool_ev;     // int32[max_pool_chunks]: event of each pooling chunk
+    size_t pool_beg;    // int32[max_pool_chunks]: first event-local pulse of each pooling chunk
+    size_t chunk_part;  // int32[max_pool_chunks]: partial-sum record of each pooling chunk
     size_t ev_cnt;      // int32[B]: chunks of each event done so far (pooling)
     size_t big_ev;      // int32[2][B]: events of more than kCombLast chunks and their first
                         // record (pooling)
@@ -45,6 +47,7 @@ struct WorkspaceLayout {
                         // stride C+1) or per chunk (chunked pooling, stride C+2)
     size_t total;
     int64_t max_chunks;
+    int64_t max_pool_chunks;
     int64_t max_items;
     int64_t max_parts;
 };
@@ -132,7 +135,7 @@ struct PoolArgs {
     float* pooled;
     int32_t* cell_count;
     int32_t* perm;
-    const int32_t* header;      // chunked pooling: [0] chunks, [4] events of > kCombLast chunks
+    int32_t* header;            // chunked pooling: [4] events of > kCombLast chunks, [6] chunks
     const int32_t* chunk_ev;    // chunked pooling: event of each chunk
     const int32_t* chunk_beg;   // chunked pooling: first event-local pulse of each chunk
     const int32_t* chunk_part;  // chunked pooling: record of each chunk (-1: one-chunk event)
@@ -154,6 +157,12 @@ hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
 hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
                             const WorkspaceLayout& L, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
+// The work lists of a sample -> Lloyd (`chunks`) -> Voronoi pool (`pool`)
+// sequence in one launch; then launch_sample_items runs the FPS without
+// planning again.
+hipError_t launch_plan_all(const SampleArgs& a, int64_t B, void* ws, const WorkspaceLayout& L,
+                           const PoolArgs& pa, bool chunks, bool pool, hipStream_t s);
+hipError_t launch_sample_items(const SampleArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s);
 hipError_t launch_assign(const AssignArgs& a, int64_t max_chunks, hipStream_t s);
 hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s);

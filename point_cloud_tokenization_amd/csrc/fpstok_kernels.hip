@@ -131,7 +131,7 @@ __device__ __forceinline__ void mark_selected(uint32_t& selbits, int s) {
 // One workgroup of 1024 threads: split every event into chunks of kChunk
 // pulses (an empty event gets one chunk so per-event work still runs) and
 // write the chunk list.
-__global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ offsets,
+__device__ __forceinline__ void plan_chunks(const int64_t* __restrict__ offsets,
                                                     int64_t B, int64_t N, int64_t max_chunks,
                                                     int32_t* __restrict__ header,
                                                     int32_t* __restrict__ chunk_ev,
@@ -178,12 +178,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ 
 // the long chunks start before the short ones.  The chunks of an event of
 // more than one chunk get consecutive partial-sum records (-1: the event is
 // one chunk), ev_cnt is cleared, and the events of more than kCombLast
-// chunks are listed in big_ev with their first record (count in header[4]).
+// chunks are listed in big_ev with their first record (count in header[4];
+// the chunk count goes to header[6]).
 // Malformed (overlapping) offsets can ask for more chunks or records than
 // the lists hold: extra chunks are dropped, an event without room for its
 // records is marked -2 (summed whole by its first chunk), and a listed event
 // without room is listed as -1; nothing is written out of bounds.
-__global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restrict__ offsets,
+__device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                                                          int64_t B, int64_t N, int64_t max_chunks,
                                                          int64_t max_parts,
                                                          int32_t* __restrict__ header,
@@ -251,9 +252,30 @@ __global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restri
         }
     }
     if (tid == 0) {
-        header[0] = (int)carry;
         header[4] = bcarry;
+        header[6] = (int)carry;
     }
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ offsets, int64_t B,
+                                                    int64_t N, int64_t max_chunks,
+                                                    int32_t* __restrict__ header,
+                                                    int32_t* __restrict__ chunk_ev,
+                                                    int32_t* __restrict__ chunk_beg) {
+    plan_chunks(offsets, B, N, max_chunks, header, chunk_ev, chunk_beg);
+}
+
+__global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restrict__ offsets,
+                                                         int64_t B, int64_t N, int64_t max_chunks,
+                                                         int64_t max_parts,
+                                                         int32_t* __restrict__ header,
+                                                         int32_t* __restrict__ chunk_ev,
+                                                         int32_t* __restrict__ chunk_beg,
+                                                         int32_t* __restrict__ chunk_part,
+                                                         int32_t* __restrict__ ev_cnt,
+                                                         int32_t* __restrict__ big_ev) {
+    plan_pool(offsets, B, N, max_chunks, max_parts, header, chunk_ev, chunk_beg, chunk_part,
+              ev_cnt, big_ev);
 }
 
 // ---------------------------------------------------------------------- FPS
@@ -1116,7 +1138,7 @@ __device__ __forceinline__ void fps_streaming(const SampleArgs& a, int64_t b, in
 // first every shard of every event that needs a gang (kFpsCap < n <=
 // kGangMax*kFpsCap; shards of one event consecutive), then one item per other
 // event.  Zeroes the gang records and the claim counter.
-__global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B) {
+__device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
     __shared__ int s_wsum[16];
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -1165,6 +1187,33 @@ __global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B)
         a.header[1] = (int)min((int64_t)carry, B + a.N / kFpsCap);  // items
         a.header[2] = 0;      // claim counter
         a.header[3] = 0;      // device error word
+    }
+}
+
+__global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B) {
+    plan_fps(a, B);
+}
+
+// The work lists of a call that runs sample, then Lloyd (assign chunks,
+// when `chunks`) and Voronoi pooling (pooling chunks, when `pool`), in one
+// launch.
+__global__ __launch_bounds__(1024) void plan_all_kernel(SampleArgs a, int64_t B,
+                                                        int32_t* __restrict__ chunk_ev,
+                                                        int32_t* __restrict__ chunk_beg,
+                                                        int64_t max_chunks, PoolArgs pa,
+                                                        int64_t max_pool_chunks,
+                                                        int64_t max_parts, int chunks, int pool) {
+    plan_fps(a, B);
+    if (chunks) {
+        __syncthreads();
+        plan_chunks(a.offsets, B, a.N, max_chunks, a.header, chunk_ev, chunk_beg);
+    }
+    if (pool) {
+        __syncthreads();
+        plan_pool(a.offsets, B, a.N, max_pool_chunks, max_parts, pa.header,
+                  const_cast<int32_t*>(pa.chunk_ev), const_cast<int32_t*>(pa.chunk_beg),
+                  const_cast<int32_t*>(pa.chunk_part), pa.ev_cnt,
+                  const_cast<int32_t*>(pa.big_ev));
     }
 }
 
@@ -1933,7 +1982,7 @@ __global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
     __shared__ int s_last;
     static_assert(kPoolChunk == kLdsPerm, "the slot sorts hold one chunk in LDS");
     const int c = blockIdx.x;
-    if (c >= a.header[0]) return;
+    if (c >= a.header[6]) return;
     const int64_t b = a.chunk_ev[c];
     const int beg = a.chunk_beg[c];
     const int part = a.chunk_part[c];
@@ -2134,7 +2183,7 @@ __global__ __launch_bounds__(kSortT) void pool_voronoi_lds_kernel(PoolArgs a, in
     extern __shared__ __align__(16) int s_dyn[];
     __shared__ int s_last;
     const int c = blockIdx.x;
-    if (c >= a.header[0]) return;
+    if (c >= a.header[6]) return;
     const int64_t b = a.chunk_ev[c];
     const int beg = a.chunk_beg[c];
     const int part = a.chunk_part[c];
@@ -2535,9 +2584,10 @@ hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
 hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
                             const WorkspaceLayout& L, hipStream_t s) {
     char* base = (char*)ws;
-    hipLaunchKernelGGL(plan_pool_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N, L.max_chunks,
-                       L.max_parts, (int32_t*)(base + L.header), (int32_t*)(base + L.chunk_ev),
-                       (int32_t*)(base + L.chunk_beg), (int32_t*)(base + L.chunk_part),
+    hipLaunchKernelGGL(plan_pool_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N,
+                       L.max_pool_chunks, L.max_parts, (int32_t*)(base + L.header),
+                       (int32_t*)(base + L.pool_ev), (int32_t*)(base + L.pool_beg),
+                       (int32_t*)(base + L.chunk_part),
                        (int32_t*)(base + L.ev_cnt), (int32_t*)(base + L.big_ev));
     return hipGetLastError();
 }
@@ -2556,6 +2606,20 @@ hipError_t launch_pool_combine(const PoolArgs& a, hipStream_t s) {
 }
 
 int64_t sample_max_items(int64_t B, int64_t N) { return B + N / kFpsCap; }
+
+hipError_t launch_plan_all(const SampleArgs& a, int64_t B, void* ws, const WorkspaceLayout& L,
+                           const PoolArgs& pa, bool chunks, bool pool, hipStream_t s) {
+    char* base = (char*)ws;
+    hipLaunchKernelGGL(plan_all_kernel, dim3(1), dim3(1024), 0, s, a, B,
+                       (int32_t*)(base + L.chunk_ev), (int32_t*)(base + L.chunk_beg), L.max_chunks,
+                       pa, L.max_pool_chunks, L.max_parts, chunks ? 1 : 0, pool ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_sample_items(const SampleArgs& a, int64_t B, hipStream_t s) {
+    hipLaunchKernelGGL(sample_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s) {
     hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(1024), 0, s, a, B);

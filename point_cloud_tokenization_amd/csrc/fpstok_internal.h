@@ -9,9 +9,9 @@
 
 namespace fpstok {
 
-// Pulses per chunk of the chunked kernels (assign): one per thread of a
+// Pulses per chunk of the assign kernel: four threads per pulse in a
 // 256-thread workgroup.
-constexpr int kChunk = 256;
+constexpr int kChunk = 64;
 
 // Pulses per chunk of the chunked Voronoi pooling: the largest slot sort one
 // workgroup does in LDS.

@@ -1317,10 +1317,15 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
 // ------------------------------------------------------------------- assign
 
 constexpr int kAsgT = 256;
-constexpr int kAsgR = kChunk / kAsgT;  // pulses per thread
+constexpr int kAsgQ = 4;  // threads per pulse, each over a quarter of the centroids
+static_assert(kChunk * kAsgQ == kAsgT, "one chunk per workgroup");
 
-// Nearest centroid of every pulse of one chunk; centroids staged in LDS and
-// read as broadcasts; each thread keeps kAsgR pulses in registers.
+// Nearest centroid of every pulse of one chunk (kChunk pulses), lowest slot
+// on ties.  Centroids are staged in LDS.  The kAsgQ threads of a pulse (a
+// quad of lanes) each scan a contiguous quarter of the centroids in
+// ascending order with a strict comparison, then merge across the quad
+// (two DPP steps): the lower quarter wins ties, so the result is the first
+// minimum over all centroids.
 __global__ __launch_bounds__(kAsgT) void assign_kernel(AssignArgs a) {
     __shared__ float4 s_c[1024];
     const int w = blockIdx.x;
@@ -1337,41 +1342,38 @@ __global__ __launch_bounds__(kAsgT) void assign_kernel(AssignArgs a) {
     const int tid = threadIdx.x;
     for (int j = tid; j < T; j += kAsgT) s_c[j] = a.centroids[b * a.P + j];
     __syncthreads();
+    const int q = tid & (kAsgQ - 1);
+    const int i = beg + (tid >> 2);
     const int end = min(n, beg + kChunk);
-    float qx[kAsgR], qy[kAsgR], qz[kAsgR], qt[kAsgR], bd[kAsgR];
-    int bj[kAsgR];
-#pragma unroll
-    for (int r = 0; r < kAsgR; ++r) {
-        const int i = beg + tid + r * kAsgT;
-        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < end) q = a.coords[off + i];
-        qx[r] = q.x;
-        qy[r] = q.y;
-        qz[r] = q.z;
-        qt[r] = q.w;
-        bd[r] = INFINITY;
-        bj[r] = 0;
-    }
-    {
-        const float4 c = s_c[0];
-#pragma unroll
-        for (int r = 0; r < kAsgR; ++r) bd[r] = sqd(qx[r], qy[r], qz[r], qt[r], c.x, c.y, c.z, c.w);
-    }
-    for (int j = 1; j < T; ++j) {
+    float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < end) p = a.coords[off + i];
+    const int T4 = (T + kAsgQ - 1) >> 2;
+    const int j0 = min(T, q * T4), j1 = min(T, j0 + T4);
+    float bd = INFINITY;
+    int bj = j0;
+    for (int j = j0; j < j1; ++j) {
         const float4 c = s_c[j];
-#pragma unroll
-        for (int r = 0; r < kAsgR; ++r) {
-            const float d = sqd(qx[r], qy[r], qz[r], qt[r], c.x, c.y, c.z, c.w);
-            const bool u = d < bd[r];
-            bd[r] = u ? d : bd[r];
-            bj[r] = u ? j : bj[r];
-        }
+        const float d = sqd(p.x, p.y, p.z, p.w, c.x, c.y, c.z, c.w);
+        const bool u = d < bd;
+        bd = u ? d : bd;
+        bj = u ? j : bj;
     }
+    // merge the quad: partner q^1, then q^2; the lower quarter comes first
 #pragma unroll
-    for (int r = 0; r < kAsgR; ++r) {
-        const int i = beg + tid + r * kAsgT;
-        if (i < end) a.assign[off + i] = bj[r];
+    for (int step = 0; step < 2; ++step) {
+        const int od = step == 0 ? dpp_i<kQuadSwap1, 0xF>(__float_as_int(bd), 0)
+                                 : dpp_i<kQuadSwap2, 0xF>(__float_as_int(bd), 0);
+        const int oj = step == 0 ? dpp_i<kQuadSwap1, 0xF>(bj, 0) : dpp_i<kQuadSwap2, 0xF>(bj, 0);
+        const bool lower = ((q >> step) & 1) == 0;  // this lane holds the lower range
+        const float ad = lower ? bd : __int_as_float(od);
+        const int aj = lower ? bj : oj;
+        const float xd = lower ? __int_as_float(od) : bd;
+        const int xj = lower ? oj : bj;
+        const bool tb = xd < ad;
+        bd = tb ? xd : ad;
+        bj = tb ? xj : aj;
     }
+    if (q == 0 && i < end) a.assign[off + i] = bj;
 }
 
 // ---------------------------------------------------------------------- kNN

@@ -1799,12 +1799,56 @@ __device__ __forceinline__ void lloyd_slot_means(const LloydArgs& a, int64_t b, 
     }
 }
 
-// One workgroup per event with n > P: stable sort by slot (permutation in
-// LDS when it fits), then every slot's charge-weighted mean.
+// lloyd_slot_means from LDS: coordinates rows[i] and weights wts[i] of the
+// event's pulses, row n all zero (a batch is padded with it: adding 0.0 * 0.0
+// leaves a sum that started at +0.0 unchanged, and the fused multiply-add of
+// an exact float64 product rounds once, like the separate add).
+__device__ __forceinline__ void lloyd_slot_means_lds(const LloydArgs& a, int64_t b, int n, int T,
+                                                     const int* __restrict__ perm,
+                                                     const int* s_off,
+                                                     const float4* __restrict__ rows,
+                                                     const float* __restrict__ wts) {
+    for (int j = threadIdx.x; j < T; j += kSortT) {
+        double W = 0.0, sx = 0.0, sy = 0.0, sz = 0.0, st = 0.0;
+        const int e = s_off[j + 1];
+        for (int m0 = s_off[j]; m0 < e; m0 += kBatch) {
+            int idx[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) idx[q] = m0 + q < e ? perm[m0 + q] : n;
+            float4 x[kBatch];
+            float w[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                x[q] = rows[idx[q]];
+                w[q] = wts[idx[q]];
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const double wd = (double)w[q];
+                W += wd;
+                sx = __builtin_fma(wd, (double)x[q].x, sx);
+                sy = __builtin_fma(wd, (double)x[q].y, sy);
+                sz = __builtin_fma(wd, (double)x[q].z, sz);
+                st = __builtin_fma(wd, (double)x[q].w, st);
+            }
+        }
+        if (W > 0.0)
+            a.centroids[b * a.P + j] =
+                make_float4((float)(sx / W), (float)(sy / W), (float)(sz / W), (float)(st / W));
+    }
+}
+
+// One workgroup per event with n > P: every slot's charge-weighted mean of
+// its members in ascending pulse order.  An event of up to kLdsPerm pulses
+// first copies its coordinates and weights to LDS (dynamic: float4
+// rows[kLdsPerm + 1], float wts[kLdsPerm + 1]) and sorts by slot in LDS
+// (through bitmaps when n <= 1024, else the ballot-match sort); larger
+// events sort into device memory and gather their members from it.
 __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
-    __shared__ int s_cnt[kSortW * kMaxP];
+    __shared__ __align__(16) int s_cnt[kSortW * kMaxP];
     __shared__ int s_off[kMaxP + 1];
-    __shared__ int s_perm[kLdsPerm];
+    __shared__ __align__(16) int s_perm[kLdsPerm];
+    extern __shared__ __align__(16) float4 s_rows[];
     const int64_t b = blockIdx.x;
     int64_t off;
     int n;
@@ -1813,12 +1857,34 @@ __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
     int T = a.token_count[b];
     T = T > a.P ? a.P : T;
     if (T < 1) return;
-    if (n <= kLdsPerm) {
-        block_sort_by_token(a.assign + off, n, T, s_perm, s_cnt, s_off);
-        lloyd_slot_means(a, b, off, T, s_perm, s_off);
-    } else {
+    const int tid = threadIdx.x;
+    if (n > kLdsPerm) {
         block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
         lloyd_slot_means(a, b, off, T, a.perm + off, s_off);
+        return;
+    }
+    float* s_w = reinterpret_cast<float*>(s_rows + kLdsPerm + 1);
+    for (int i = tid; i < n; i += kSortT) {
+        s_rows[i] = a.coords[off + i];
+        s_w[i] = a.charge_col >= 0 ? a.features[(off + i) * (int64_t)a.C + a.charge_col] : 1.0f;
+    }
+    if (tid == 0) {
+        s_rows[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s_w[n] = 0.0f;
+    }
+    const int W4 = (n + 127) >> 7;
+    if (n <= kBmW4 * 128 && T * W4 <= kLdsPerm / 4) {
+        // slots copied to s_perm[0, n); permutation in s_perm[1024, 2048);
+        // prefix table in s_perm[2048, 3072); bitmaps in s_cnt
+        for (int i = tid; i < n; i += kSortT) s_perm[i] = a.assign[off + i];
+        __syncthreads();
+        int* perm = s_perm + kBmW4 * 128;
+        block_sort_bitmap(s_perm, n, T, reinterpret_cast<uint32_t*>(s_cnt),
+                          s_perm + 2 * kBmW4 * 128, s_off, perm);
+        lloyd_slot_means_lds(a, b, n, T, perm, s_off, s_rows, s_w);
+    } else {
+        block_sort_by_token(a.assign + off, n, T, s_perm, s_cnt, s_off);
+        lloyd_slot_means_lds(a, b, n, T, s_perm, s_off, s_rows, s_w);
     }
 }
 
@@ -2658,7 +2724,8 @@ hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s) {
 }
 
 hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(lloyd_update_kernel, dim3(grid1(B)), dim3(kSortT), 0, s, a);
+    const size_t lds = (sizeof(float4) + sizeof(float)) * (size_t)(kLdsPerm + 1);
+    hipLaunchKernelGGL(lloyd_update_kernel, dim3(grid1(B)), dim3(kSortT), lds, s, a);
     return hipGetLastError();
 }
 

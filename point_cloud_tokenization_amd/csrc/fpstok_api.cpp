@@ -158,6 +158,7 @@ static SampleArgs sample_args(const fpstok_batch* bt, const fpstok_params* pr,
     a.coords = (const float4*)bt->coords;
     a.offsets = bt->offsets;
     a.N = bt->num_points;
+    a.B = bt->num_events;
     a.P = pr->num_patches;
     a.start_idx = start_idx;
     a.centroid_idx = centroid_idx;

@@ -66,6 +66,7 @@ struct SampleArgs {
     const float4* coords;
     const int64_t* offsets;
     int64_t N;
+    int64_t B;
     int P;
     const int32_t* start_idx;
     int32_t* centroid_idx;
@@ -74,7 +75,8 @@ struct SampleArgs {
     int32_t* assign;
     float* ws_mind;
     int32_t* ws_near;
-    int32_t* header;                // [1] items, [2] claim counter, [3] error word
+    int32_t* header;                // [1] items, [2] claim counter, [3] error word,
+                                    // [5] gang items (0: item i is event i)
     int32_t* item_ev;               // [max_items] event of each work item
     int32_t* item_g;                // [max_items] shard of each work item
     unsigned long long* gang_rec;   // [max_items][2][kGangRecWords] gang records

@@ -1137,56 +1137,96 @@ __device__ __forceinline__ void fps_streaming(const SampleArgs& a, int64_t b, in
 // Work list of the sample call, built by one workgroup of 1024 threads:
 // first every shard of every event that needs a gang (kFpsCap < n <=
 // kGangMax*kFpsCap; shards of one event consecutive), then one item per other
-// event.  Zeroes the gang records and the claim counter.
+// event.  Zeroes the gang records and the claim counter.  header[5] receives
+// the number of gang items: when it is 0, item i is event i and the sample
+// workgroups take their items by workgroup index instead of claiming them.
 __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
-    __shared__ int s_wsum[16];
+    __shared__ int s_wsum[2][16];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
-    int carry = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-        for (int64_t base = 0; base < B; base += 1024) {
-            const int64_t b = base + tid;
-            int cnt = 0;
-            if (b < B) {
-                int64_t off;
-                int n;
-                event_range(a.offsets, a.N, b, off, n);
-                const bool gang = n > kFpsCap && n <= kGangMax * kFpsCap && n > a.P;
-                if (pass == 0 && gang) cnt = (n + kFpsCap - 1) / kFpsCap;
-                if (pass == 1 && !gang) cnt = 1;
-            }
-            const int incl = wave_incl_scan(cnt);
-            if (lane == 63) s_wsum[wave] = incl;
-            __syncthreads();
-            int wb = 0, total = 0;
-            for (int w = 0; w < 16; ++w) {
-                const int v = s_wsum[w];
-                if (w < wave) wb += v;
-                total += v;
-            }
-            const int pos = carry + wb + incl - cnt;
-            // malformed (overlapping) offsets could ask for more items than
-            // the list holds; those are dropped, never written out of bounds
-            const int64_t max_items = B + a.N / kFpsCap;
-            for (int q = 0; q < cnt && pos + q < max_items; ++q) {
-                a.item_ev[pos + q] = (int32_t)b;
-                a.item_g[pos + q] = q;
-            }
-            carry += total;
-            __syncthreads();
+    const int64_t max_items = B + a.N / kFpsCap;
+    // malformed (overlapping) offsets could ask for more items than the list
+    // holds; those are dropped, never written out of bounds
+    auto put = [&](int64_t pos, int cnt, int64_t b) {
+        for (int q = 0; q < cnt && pos + q < max_items; ++q) {
+            a.item_ev[pos + q] = (int32_t)b;
+            a.item_g[pos + q] = q;
         }
-        // gang items are the first `carry` items after pass 0: clear their
-        // records (stale tags of an earlier call must not match)
-        if (pass == 0) {
-            const int64_t gw = (int64_t)min((int64_t)carry, B + a.N / kFpsCap) * 2 * kGangRecWords;
-            for (int64_t w = tid; w < gw; w += 1024) a.gang_rec[w] = 0ull;
+    };
+    int gang_items = 0, items = 0;
+    if (B <= 1024) {
+        // one pass: both counts of event `tid` and their two scans
+        int gc = 0, sc = 0;
+        if (tid < B) {
+            int64_t off;
+            int n;
+            event_range(a.offsets, a.N, tid, off, n);
+            const bool gang = n > kFpsCap && n <= kGangMax * kFpsCap && n > a.P;
+            gc = gang ? (n + kFpsCap - 1) / kFpsCap : 0;
+            sc = gang ? 0 : 1;
         }
+        const int gi = wave_incl_scan(gc);
+        const int si = wave_incl_scan(sc);
+        if (lane == 63) {
+            s_wsum[0][wave] = gi;
+            s_wsum[1][wave] = si;
+        }
+        __syncthreads();
+        int gb = 0, sb = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int g = s_wsum[0][w], v = s_wsum[1][w];
+            if (w < wave) {
+                gb += g;
+                sb += v;
+            }
+            gang_items += g;
+            items += v;
+        }
+        items += gang_items;
+        put(gb + gi - gc, gc, tid);
+        put(gang_items + sb + si - sc, sc, tid);
+    } else {
+        int carry = 0;
+        for (int pass = 0; pass < 2; ++pass) {
+            for (int64_t base = 0; base < B; base += 1024) {
+                const int64_t b = base + tid;
+                int cnt = 0;
+                if (b < B) {
+                    int64_t off;
+                    int n;
+                    event_range(a.offsets, a.N, b, off, n);
+                    const bool gang = n > kFpsCap && n <= kGangMax * kFpsCap && n > a.P;
+                    if (pass == 0 && gang) cnt = (n + kFpsCap - 1) / kFpsCap;
+                    if (pass == 1 && !gang) cnt = 1;
+                }
+                const int incl = wave_incl_scan(cnt);
+                if (lane == 63) s_wsum[0][wave] = incl;
+                __syncthreads();
+                int wb = 0, total = 0;
+                for (int w = 0; w < 16; ++w) {
+                    const int v = s_wsum[0][w];
+                    if (w < wave) wb += v;
+                    total += v;
+                }
+                put(carry + wb + incl - cnt, cnt, b);
+                carry += total;
+                __syncthreads();
+            }
+            if (pass == 0) gang_items = carry;
+        }
+        items = carry;
     }
+    // gang items come first: clear their records (stale tags of an earlier
+    // call must not match)
+    gang_items = (int)min((int64_t)gang_items, max_items);
+    const int64_t gw = (int64_t)gang_items * 2 * kGangRecWords;
+    for (int64_t w = tid; w < gw; w += 1024) a.gang_rec[w] = 0ull;
     if (tid == 0) {
-        a.header[1] = (int)min((int64_t)carry, B + a.N / kFpsCap);  // items
-        a.header[2] = 0;      // claim counter
-        a.header[3] = 0;      // device error word
+        a.header[1] = (int)min((int64_t)items, max_items);  // items
+        a.header[2] = 0;                                   // claim counter
+        a.header[3] = 0;                                   // device error word
+        a.header[5] = gang_items;
     }
 }
 
@@ -1241,20 +1281,36 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
                                                 int stage_cap, float* s_feat) {
     const int tid = threadIdx.x;
     ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0, false};
-    // items are claimed in list order, so the shards of one gang go to
-    // workgroups that start one after another: a gang whose workgroups wait
-    // for a partner only ever waits for a workgroup that will start once
-    // earlier, complete gangs or single events finish
-    if (tid == 0)
-        *s_item = __hip_atomic_fetch_add(a.header + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int item = *s_item;
-    if (item >= a.header[1]) return it;
-    const int64_t b = a.item_ev[item];
-    const int g = a.item_g[item];
+    // without gangs item i is event i: the event's range is read together
+    // with the header, and nothing is claimed
+    const int64_t bd = (int64_t)blockIdx.x < a.B ? (int64_t)blockIdx.x : a.B - 1;
     int64_t off;
     int n;
-    event_range(a.offsets, a.N, b, off, n);
+    event_range(a.offsets, a.N, bd, off, n);
+    const int nitems = a.header[1];
+    int item;
+    int64_t b;
+    int g;
+    if (a.header[5] == 0) {
+        item = (int)blockIdx.x;
+        if (item >= nitems) return it;
+        b = item;
+        g = 0;
+    } else {
+        // items are claimed in list order, so the shards of one gang go to
+        // workgroups that start one after another: a gang whose workgroups
+        // wait for a partner only ever waits for a workgroup that will start
+        // once earlier, complete gangs or single events finish
+        if (tid == 0)
+            *s_item = __hip_atomic_fetch_add(a.header + 2, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        item = *s_item;
+        if (item >= nitems) return it;
+        b = a.item_ev[item];
+        g = a.item_g[item];
+        event_range(a.offsets, a.N, b, off, n);
+    }
     it.b = b;
     it.off = off;
     it.n = n;

@@ -144,6 +144,31 @@ class Runner:
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
+    def timed_stream(self, steps, warmup):
+        """K host-launched steps back to back on one stream, with nothing
+        between them; returns wall seconds between the two synchronisations."""
+        import torch
+
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def timed_launch(self, steps, warmup, launch):
+        """Wall seconds of K steps in the chosen launch mode ("best": both,
+        the faster one); returns (seconds, mode, {mode: seconds})."""
+        walls = {}
+        if launch in ("graph", "best"):
+            walls["hipGraph"] = self.timed_graph(steps, warmup)
+        if launch in ("eager", "best"):
+            walls["eager"] = self.timed_stream(steps, warmup)
+        mode = min(walls, key=walls.get)
+        return walls[mode], mode, walls
+
     def timed(self, steps, warmup):
         """K host-launched steps with a HIP event pair around each (on the
         stream the kernels run on).  Returns (wall seconds, mean step seconds
@@ -236,9 +261,9 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times), "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters, and exit")
-    ap.add_argument("--launch", choices=["graph", "eager"], default="graph",
-                    help="graph: time replays of one captured step (default); eager: time "
-                         "host-launched steps")
+    ap.add_argument("--launch", choices=["best", "graph", "eager"], default="best",
+                    help="graph: time replays of one captured step; eager: time host-launched "
+                         "steps back to back; best (default): both, report the faster")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the tokenizer runs on a single MI355X and "
@@ -268,8 +293,8 @@ def main():
     r = Runner(b)
     # per-step GPU time: a HIP event pair around each of K host-launched
     # steps, on the stream the kernels run on
-    wall_eager, step_gpu = r.timed(args.steps, args.warmup)
-    wall = r.timed_graph(args.steps, args.warmup) if args.launch == "graph" else wall_eager
+    _, step_gpu = r.timed(args.steps, args.warmup)
+    wall, mode, walls = r.timed_launch(args.steps, args.warmup, args.launch)
     ms = wall / args.steps * 1e3
     value = st["B"] * args.steps / wall
     per_call = r.per_call(max(10, args.steps // 4))
@@ -294,12 +319,11 @@ def main():
             s2 = workload_stats(bb)
             steps = 20 if s2["N"] > 1_000_000 else 100
             rr = Runner(bb)
-            w2, g2 = rr.timed(steps, 5)
-            if args.launch == "graph":
-                w2 = rr.timed_graph(steps, 5)
+            _, g2 = rr.timed(steps, 5)
+            w2, mode2, _ = rr.timed_launch(steps, 5, args.launch)
             pc2 = rr.per_call(max(5, steps // 4))
             secondary[name] = dict(
-                events_per_s=s2["B"] * steps / w2, ms_per_step=w2 / steps * 1e3,
+                events_per_s=s2["B"] * steps / w2, ms_per_step=w2 / steps * 1e3, launch=mode2,
                 step_gpu_us=g2 * 1e6,
                 per_call_us={c: v * 1e6 for c, v in pc2.items()},
                 fps_point_iters_per_s=s2["point_iters"] / pc2["sample"],
@@ -325,8 +349,8 @@ def main():
                    "num_patches": st["P"], "features": st["C"],
                    "assign_mode": "knn" if b["mode"] == 1 else "voronoi",
                    "lloyd_iters": b["L"], "pool": "charge" if b["weighted"] else "mean",
-                   "seed": b["seed"], "launch": "hipGraph" if args.launch == "graph" else "eager"},
-        "eager_events_per_s": st["B"] * args.steps / wall_eager,
+                   "seed": b["seed"], "launch": mode},
+        "events_per_s_by_launch": {m: st["B"] * args.steps / w for m, w in walls.items()},
         "step_gpu_us": step_gpu * 1e6,
         "fps_point_iters_per_s": st["point_iters"] / step_gpu,
         "per_call_us": {c: v * 1e6 for c, v in per_call.items()},

@@ -465,14 +465,16 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
                 nr[k] = u ? j : nr[k];
                 md[k] = u ? d : md[k];
             }
-            if (j + 1 == P || wm <= U) break;
-            // the best listed pulse; lanes hold the list in pulse order
+            // the best listed pulse (lanes hold the list in pulse order),
+            // read before the test: when the run ends here the exchange
+            // replaces it
             const int Lw = (int)__builtin_ctzll(ballot(__float_as_int(lv) == wm));
             s = readlane_i(li, Lw);
             cx = readlane_f(lx, Lw);
             cy = readlane_f(ly, Lw);
             cz = readlane_f(lz, Lw);
             ct = readlane_f(lt, Lw);
+            if (j + 1 == P || wm <= U) break;
             ++j;
         }
         if (j + 1 == P) break;

@@ -45,8 +45,8 @@ FPS_OPS_PER_POINT_ITER = 14
 # source it was taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "bb0b5717ed77550956d9723be0b48ca01763b6c315036d3e54b7f725ee4479b8",
-    "bytes": int(round((2 * (439.9 + 4.0) + (418.6 + 0.5)) * 1024)),
+    "kernels_sha256": "5fddbb00a3916c547a7e302a2fca626e6e9bf62a3659deb31de80d1df793c9c5",
+    "bytes": int(round((2 * (386.8 + 4.3) + (419.3 + 0.5)) * 1024)),
 }
 
 

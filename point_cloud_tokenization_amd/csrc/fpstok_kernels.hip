@@ -47,6 +47,16 @@ __device__ __forceinline__ void event_range(const int64_t* offsets, int64_t N, i
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// Workgroup barrier that orders LDS accesses only: it waits for this wave's
+// LDS operations but leaves its global loads and stores in flight (a plain
+// __syncthreads also drains those).  For code whose threads communicate
+// through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // number of set bits of m in lanes below this one
@@ -312,7 +322,7 @@ struct Shard {
 // Write the selection order (and the selected coordinates) of one event.
 __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
                                                 const float4* __restrict__ p, const int* s_sel) {
-    __syncthreads();
+    lds_barrier();
     for (int j = threadIdx.x; j < a.P; j += blockDim.x) {
         const int s = s_sel[j];
         a.centroid_idx[b * a.P + j] = s;
@@ -328,11 +338,13 @@ constexpr int kStageR = kStage / kFpsT;   // staged floats per thread
 // Feature rows of a single-workgroup event, copied to LDS while its FPS
 // runs (nf = 0: none).  The loads are issued once the pulses are in
 // registers; the FPS loop itself issues no global loads, so they complete
-// in its shadow and are written to `dst` after the last iteration.
+// in its shadow and are written to `dst` after the last iteration, followed
+// by one all-zero row (the padding row of the pooling sums).
 struct Stage {
     const float* src;  // the event's first feature row
-    int nf;            // floats to copy (n * C), at most kStage
-    float* dst;        // LDS
+    int nf;            // floats to copy (n * C), at most kStage - C
+    int nz;            // floats written: nf + C (the zero row), 0 when none
+    float* dst;        // LDS, kStage floats
 };
 
 constexpr int kListCap = 64;  // entries of the candidate list (one per lane)
@@ -514,7 +526,7 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             L.wc[wave] = __popcll(ob);
             L.wb[wave] = wb2;
         }
-        __syncthreads();
+        lds_barrier();
         // every wave: U, this iteration's argmax (largest offer, then lowest
         // (wave, position) = lowest pulse index) and the list layout
         int Un = 0;
@@ -582,12 +594,12 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             const int d = wave_max_i(keep && pos >= kListCap ? b1 : INT32_MIN);
             // every wave needs the same U: combine the per-wave maxima
             if (lane == 0) L.wd[wave] = d;
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int w = 0; w < kFpsW; ++w)
                 Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wd[w]));
         }
-        __syncthreads();
+        lds_barrier();
         U = __builtin_amdgcn_readfirstlane(Un);
         if (lane < C) {
             const FpsSlot o = L.list[lane];
@@ -611,15 +623,22 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
         }
     }
     if (s_asg) {
+        // every lane's M entries (below 256 * M <= kFpsCap); the sort reads
+        // the first n
 #pragma unroll
-        for (int k = 0; k < M; ++k) {
-            const int i = lbase + k;
-            if (i < n) s_asg[i] = nr[k];
+        for (int k = 0; k < M; ++k) s_asg[lbase + k] = nr[k];
+    }
+    // the rows and the zero row, with no per-lane branches: a row r is
+    // written whole (uniform test) and its lanes beyond the rows store 0
+    // (they stay below kStage, inside dst)
+    const int sz = __builtin_amdgcn_readfirstlane((st.nz + kFpsT - 1) / kFpsT);
+#pragma unroll
+    for (int r = 0; r < kStageR; ++r) {
+        if (r < sz) {
+            const int q = tid + kFpsT * r;
+            st.dst[q] = q < st.nf ? fr[r] : 0.0f;
         }
     }
-#pragma unroll
-    for (int r = 0; r < kStageR; ++r)
-        if (r < sr && tid + kFpsT * r < st.nf) st.dst[tid + kFpsT * r] = fr[r];
     write_selection(a, b, p, s_sel);
 }
 
@@ -1340,7 +1359,8 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     if (s0 < 0 || s0 >= n) s0 = 0;
     if (n <= kFpsCap) {
         it.staged = feats != nullptr && (int64_t)(n + 1) * C <= stage_cap;
-        const Stage st{it.staged ? feats + off * C : nullptr, it.staged ? n * C : 0, s_feat};
+        const Stage st{it.staged ? feats + off * C : nullptr, it.staged ? n * C : 0,
+                       it.staged ? (n + 1) * C : 0, s_feat};
         fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg, st);
         it.kind = 1;
         it.cnt = n;
@@ -1747,12 +1767,12 @@ __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, i
     const int W4 = (n + 127) >> 7;
     uint4* bm4 = reinterpret_cast<uint4*>(bm);
     for (int q = tid; q < T * W4; q += kSortT) bm4[q] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < n; i += kSortT) {
         const int k = asg[i];
         if ((unsigned)k < (unsigned)T) atomicOr(&bm[k * W4 * 4 + (i >> 5)], 1u << (i & 31));
     }
-    __syncthreads();
+    lds_barrier();
     // slot jj (threads own `per` consecutive slots): prefix popcounts of its
     // row and its member count; then the exclusive scan of the counts
     const int per = (T + kSortT - 1) / kSortT;
@@ -1777,7 +1797,7 @@ __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, i
     }
     const int incl = wave_incl_scan(local);
     if (lane == 63) s_ws[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     int run = incl - local, total = 0;
 #pragma unroll
     for (int w = 0; w < kSortW; ++w) {
@@ -1792,7 +1812,7 @@ __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, i
         run += loc[r];
     }
     if (tid == 0) s_off[T] = total;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < kBmW4 * 128 / kSortT; ++r) {
         const int i = tid + kSortT * r;
@@ -1810,7 +1830,7 @@ __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, i
             perm[s_off[k] + rank] = i;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // ------------------------------------------------------------ Lloyd update
@@ -2572,9 +2592,7 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         pool_slots_sorted(pa, b, off, P, pa.perm + off, s_off);
         return;
     }
-    if (it.staged)
-        for (int q = tid; q < C; q += kFpsT) s_feat[it.n * C + q] = 0.0f;  // the zero row
-    __syncthreads();
+    lds_barrier();
     if (it.kind == 1 && it.staged) {
         // small event, rows in LDS: bitmap sort into s_asg[1024 ..), pooling
         // from LDS (s_asg holds at most 1024 slots here)

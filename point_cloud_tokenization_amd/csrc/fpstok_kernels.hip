@@ -1155,7 +1155,7 @@ __device__ __forceinline__ void fps_streaming(const SampleArgs& a, int64_t b, in
     write_selection(a, b, p, s_sel);
 }
 
-// Work list of the sample call, built by one workgroup of 1024 threads:
+// Work list of the sample call, built by one workgroup (up to 1024 threads):
 // first every shard of every event that needs a gang (kFpsCap < n <=
 // kGangMax*kFpsCap; shards of one event consecutive), then one item per other
 // event.  Zeroes the gang records and the claim counter.  header[5] receives
@@ -1166,6 +1166,8 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
+    const int nt = (int)blockDim.x;  // a multiple of 64, at most 1024
+    const int nw = nt >> 6;
     const int64_t max_items = B + a.N / kFpsCap;
     // malformed (overlapping) offsets could ask for more items than the list
     // holds; those are dropped, never written out of bounds
@@ -1176,7 +1178,7 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
         }
     };
     int gang_items = 0, items = 0;
-    if (B <= 1024) {
+    if (B <= nt) {
         // one pass: both counts of event `tid` and their two scans
         int gc = 0, sc = 0;
         if (tid < B) {
@@ -1195,7 +1197,7 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
         }
         __syncthreads();
         int gb = 0, sb = 0;
-        for (int w = 0; w < 16; ++w) {
+        for (int w = 0; w < nw; ++w) {
             const int g = s_wsum[0][w], v = s_wsum[1][w];
             if (w < wave) {
                 gb += g;
@@ -1210,7 +1212,7 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
     } else {
         int carry = 0;
         for (int pass = 0; pass < 2; ++pass) {
-            for (int64_t base = 0; base < B; base += 1024) {
+            for (int64_t base = 0; base < B; base += nt) {
                 const int64_t b = base + tid;
                 int cnt = 0;
                 if (b < B) {
@@ -1225,7 +1227,7 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
                 if (lane == 63) s_wsum[0][wave] = incl;
                 __syncthreads();
                 int wb = 0, total = 0;
-                for (int w = 0; w < 16; ++w) {
+                for (int w = 0; w < nw; ++w) {
                     const int v = s_wsum[0][w];
                     if (w < wave) wb += v;
                     total += v;
@@ -1242,7 +1244,7 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
     // call must not match)
     gang_items = (int)min((int64_t)gang_items, max_items);
     const int64_t gw = (int64_t)gang_items * 2 * kGangRecWords;
-    for (int64_t w = tid; w < gw; w += 1024) a.gang_rec[w] = 0ull;
+    for (int64_t w = tid; w < gw; w += nt) a.gang_rec[w] = 0ull;
     if (tid == 0) {
         a.header[1] = (int)min((int64_t)items, max_items);  // items
         a.header[2] = 0;                                   // claim counter
@@ -2765,8 +2767,13 @@ hipError_t launch_sample_items(const SampleArgs& a, int64_t B, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Threads of the FPS work-list kernel: one per event, whole waves, up to 1024.
+static unsigned plan_fps_threads(int64_t B) {
+    return (unsigned)(B >= 1024 ? 1024 : ((B + 63) / 64) * 64);
+}
+
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(1024), 0, s, a, B);
+    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(plan_fps_threads(B)), 0, s, a, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sample_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), 0, s, a);
@@ -2774,7 +2781,7 @@ hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s) {
 }
 
 hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(1024), 0, s, a, B);
+    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(plan_fps_threads(B)), 0, s, a, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // feature rows of small single-workgroup events are staged in LDS when

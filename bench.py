@@ -45,8 +45,8 @@ FPS_OPS_PER_POINT_ITER = 14
 # source it was taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "5fddbb00a3916c547a7e302a2fca626e6e9bf62a3659deb31de80d1df793c9c5",
-    "bytes": int(round((2 * (386.8 + 4.3) + (419.3 + 0.5)) * 1024)),
+    "kernels_sha256": "7178cc1f83693dcf4598c9d3600f12115ec84a92666a4a40ed39d47f26d9b8d4",
+    "bytes": int(round((2 * (413.3 + 4.5) + (419.3 + 0.5)) * 1024)),
 }
 
 

@@ -53,8 +53,13 @@ def _load():
         lib.oracle_pool.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
         lib.oracle_tokenize.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, i32, i32, P,
                                         P, P, P, P, P, P, P]
+        lib.oracle_pack.argtypes = [P, i64, i32, i32, P, P, P, P]
+        lib.oracle_unpack.argtypes = [P, i64, i32, i32, P, P, P]
+        lib.oracle_pool_backward.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P,
+                                             P, P, P]
         for f in ("oracle_sample", "oracle_assign", "oracle_knn", "oracle_lloyd",
-                  "oracle_pool", "oracle_tokenize"):
+                  "oracle_pool", "oracle_tokenize", "oracle_pack", "oracle_unpack",
+                  "oracle_pool_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -188,4 +193,58 @@ def tokenize(coords, features, offsets, P=128, mode=0, k=16, L=0, weighted=True,
         _ptr(out["centroid_idx"]), _ptr(out["centroids"]), _ptr(out["token_count"]),
         _ptr(out["assign"]), _ptr(out["knn_idx"]), _ptr(out["pooled"]),
         _ptr(out["cell_count"])), "tokenize")
+    return out
+
+
+def pack(token_count, rows):
+    """Tokens of every event packed event after event (next to the path:
+    variable-length attention).  rows [B,P,D]; returns (packed [sum T, D] f32,
+    doc_id [sum T] i32, cu_seqlens [B+1] i32)."""
+    r = np.ascontiguousarray(rows, dtype=np.float32)
+    if r.ndim != 3:
+        raise ValueError("rows must be [B,P,D]")
+    B, P, D = r.shape
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    total = int(np.clip(tc, 0, P).sum()) if B else 0
+    packed = np.empty((max(total, 0), D), np.float32)
+    doc = np.empty(max(total, 0), np.int32)
+    cu = np.empty(B + 1, np.int32)
+    _check(_load().oracle_pack(_ptr(tc), B, P, D, _ptr(r), _ptr(packed), _ptr(doc), _ptr(cu)),
+           "pack")
+    return packed, doc, cu
+
+
+def unpack(token_count, cu_seqlens, packed, P):
+    """Inverse of pack: rows [B,P,D], zero beyond each event's tokens."""
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    pk = np.ascontiguousarray(packed, dtype=np.float32)
+    B = tc.size
+    D = pk.shape[1] if pk.ndim == 2 else 0
+    rows = np.empty((B, P, D), np.float32)
+    _check(_load().oracle_unpack(_ptr(tc), B, P, D, _ptr(cu), _ptr(pk), _ptr(rows)), "unpack")
+    return rows
+
+
+def pool_backward(features, offsets, P, token_count, pooled, grad_pooled, mode=0, assign=None,
+                  knn_idx=None, k=1, weighted=True, charge_col=-1):
+    """Gradient of pool() with respect to the features ([N,C] f32), given the
+    gradient of the loss with respect to its output and the output itself."""
+    f = np.ascontiguousarray(features, dtype=np.float32)
+    o = _offs(offsets)
+    B = o.size - 1
+    C = f.shape[1]
+    tc = np.ascontiguousarray(token_count, dtype=np.int32)
+    a = None if assign is None else np.ascontiguousarray(assign, dtype=np.int32)
+    kn = None if knn_idx is None else np.ascontiguousarray(knn_idx, dtype=np.int32)
+    if mode == 0 and a is None:
+        raise ValueError("Voronoi mode needs assign")
+    if mode == 1 and kn is None:
+        raise ValueError("kNN mode needs knn_idx")
+    pm = np.ascontiguousarray(pooled, dtype=np.float32).reshape(B, P, C)
+    g = np.ascontiguousarray(grad_pooled, dtype=np.float32).reshape(B, P, C)
+    out = np.empty((f.shape[0], C), np.float32)
+    _check(_load().oracle_pool_backward(_ptr(f), _ptr(o), B, C, charge_col, P, mode, k,
+                                        int(weighted), _ptr(tc), _ptr(a), _ptr(kn), _ptr(pm),
+                                        _ptr(g), _ptr(out)), "pool_backward")
     return out

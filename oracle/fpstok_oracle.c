@@ -385,3 +385,144 @@ int oracle_tokenize(const float* coords, const float* features, const int64_t* o
     return oracle_pool(features, offsets, B, C, charge_col, P, mode, k, weighted, token_count,
                        assign, knn_idx, pooled, cell_count);
 }
+
+/* ------------------------------------------------- token packing (next) -- */
+
+/* Packing of the tokens of a batch into one variable-length sequence for
+ * block-diagonal attention ([PR] "What is added": models/utils.py pack /
+ * unpack / build_block_mask; the review thread on the packing helper: doc_id
+ * is the event index of every packed token and the packed length is the
+ * number of tokens).  Event b contributes its first T_b = token_count[b]
+ * slots, events in order.
+ *   rows      : [B,P,D] per-slot rows (pooled features, centroids, ...)
+ *   packed    : [sum T_b, D] the rows of the tokens, event after event
+ *   doc_id    : [sum T_b] event of every packed token (may be NULL)
+ *   cu_seqlens: [B+1] cu_seqlens[b] = T_0 + ... + T_{b-1}
+ * Returns 2 if some T_b is outside [0, P]. */
+int oracle_pack(const int32_t* token_count, int64_t B, int32_t P, int32_t D,
+                const float* rows, float* packed, int32_t* doc_id, int32_t* cu_seqlens)
+{
+    int64_t at = 0;
+    cu_seqlens[0] = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t T = token_count[b];
+        if (T < 0 || T > P) return 2;
+        for (int32_t j = 0; j < T; ++j) {
+            for (int32_t d = 0; d < D; ++d)
+                packed[(at + j) * D + d] = rows[(b * P + j) * (int64_t)D + d];
+            if (doc_id) doc_id[at + j] = (int32_t)b;
+        }
+        at += T;
+        cu_seqlens[b + 1] = (int32_t)at;
+    }
+    return 0;
+}
+
+/* The inverse: rows[b][j] = packed[cu_seqlens[b] + j] for j < T_b, 0 for
+ * T_b <= j < P.  cu_seqlens as oracle_pack writes it. */
+int oracle_unpack(const int32_t* token_count, int64_t B, int32_t P, int32_t D,
+                  const int32_t* cu_seqlens, const float* packed, float* rows)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t T = token_count[b];
+        if (T < 0 || T > P) return 2;
+        for (int32_t j = 0; j < P; ++j)
+            for (int32_t d = 0; d < D; ++d)
+                rows[(b * P + j) * (int64_t)D + d] =
+                    j < T ? packed[((int64_t)cu_seqlens[b] + j) * D + d] : 0.0f;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------- pooling backward (next) -- */
+
+/* Gradient of the pooling (oracle_pool) with respect to the features, given
+ * the gradient of the loss with respect to the pooled rows (training runs
+ * through the tokenizer: [PR] "Dependencies", time per training step, and
+ * "What is added", the gradient tests).  Token j of event b with members
+ * M_j (Voronoi: assign = j; kNN: the list entries != -1), weights w_i, weight
+ * sum W_j and output m_j = pooled[b][j]:
+ *     m_j[c] = sum_{i in M_j} w_i f_i[c] / W_j        (0 when W_j = 0)
+ * so, for i in M_j and W_j != 0,
+ *     d m_j[c] / d f_i[c'] = [c = c'] w_i / W_j
+ *                          + [c' = weight column] (f_i[c] - m_j[c]) / W_j,
+ * the second term only when the weights are a feature column (weighted
+ * pooling with charge_col >= 0); a token with W_j = 0 has a constant output
+ * and contributes nothing.  The mean m_j in that term is the forward's
+ * float32 output `pooled`, as an automatic differentiation of the forward
+ * would reuse it.  Per pulse the contributions are accumulated in float64 in
+ * ascending token order (a pulse is in one Voronoi cell, or in any number of
+ * kNN lists); within a token, g_j[c'] * w_i / W_j is formed left to right
+ * and the weight-column term as (sum over c ascending of
+ * g_j[c] * (f_i[c] - m_j[c])) / W_j.  W_j is the float64 sum of the members'
+ * weights in member order (ascending pulse index, or list order), as in
+ * oracle_pool.  Result rounded to float32.
+ *   grad_pooled  : [B,P,C] f32 (rows j >= T_b are ignored)
+ *   pooled       : [B,P,C] f32, the forward output
+ *   grad_features: [N,C] f32 out (0 for pulses in no token) */
+int oracle_pool_backward(const float* features, const int64_t* offsets, int64_t B, int32_t C,
+                         int32_t charge_col, int32_t P, int32_t mode, int32_t k,
+                         int32_t weighted, const int32_t* token_count, const int32_t* assign,
+                         const int32_t* knn_idx, const float* pooled, const float* grad_pooled,
+                         float* grad_features)
+{
+    int32_t wcol = weighted != 0 ? charge_col : -1;
+    int64_t N = offsets[B];
+    double* W = (double*)malloc((size_t)(P > 0 ? P : 1) * sizeof(double));
+    double* G = (double*)malloc((size_t)(N > 0 ? N : 1) * (size_t)C * sizeof(double));
+    if (!W || !G) { free(W); free(G); return 1; }
+    memset(G, 0, (size_t)(N > 0 ? N : 1) * (size_t)C * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t off = offsets[b];
+        int64_t n = offsets[b + 1] - off;
+        int32_t T = token_count[b];
+        if (T < 0 || T > P) { free(W); free(G); return 2; }
+        /* weight sums, in member order */
+        for (int32_t j = 0; j < P; ++j) W[j] = 0.0;
+        if (mode == 0) {
+            for (int64_t i = 0; i < n; ++i) {
+                int32_t j = assign[off + i];
+                if (j < 0 || j >= T) { free(W); free(G); return 2; }
+                W[j] += weight_of(features, C, wcol, off + i);
+            }
+        } else {
+            for (int32_t j = 0; j < T; ++j)
+                for (int32_t e = 0; e < k; ++e) {
+                    int32_t i = knn_idx[(b * (int64_t)P + j) * k + e];
+                    if (i < 0) continue;
+                    if (i >= n) { free(W); free(G); return 2; }
+                    W[j] += weight_of(features, C, wcol, off + i);
+                }
+        }
+        /* contributions of token j to its member i, tokens in ascending order */
+        for (int32_t j = 0; j < T; ++j) {
+            if (W[j] == 0.0) continue;
+            const float* g = grad_pooled + (b * (int64_t)P + j) * C;
+            const float* m = pooled + (b * (int64_t)P + j) * C;
+            int64_t cnt = mode == 0 ? n : k;
+            for (int64_t e = 0; e < cnt; ++e) {
+                int64_t i;
+                if (mode == 0) {
+                    if (assign[off + e] != j) continue;
+                    i = e;
+                } else {
+                    int32_t q = knn_idx[(b * (int64_t)P + j) * k + e];
+                    if (q < 0) continue;
+                    i = q;
+                }
+                const float* f = features + (off + i) * (int64_t)C;
+                double w = weight_of(features, C, wcol, off + i);
+                double* gi = G + (off + i) * (int64_t)C;
+                for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] * w / W[j];
+                if (wcol >= 0) {
+                    double s = 0.0;
+                    for (int32_t c = 0; c < C; ++c) s += (double)g[c] * ((double)f[c] - (double)m[c]);
+                    gi[wcol] += s / W[j];
+                }
+            }
+        }
+    }
+    for (int64_t q = 0; q < N * (int64_t)C; ++q) grad_features[q] = (float)G[q];
+    free(W); free(G);
+    return 0;
+}

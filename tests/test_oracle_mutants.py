@@ -12,6 +12,7 @@ import sys
 import numpy as np
 import pytest
 
+import tests.test_oracle_next as nxt
 import tests.test_oracle_pins as pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -37,9 +38,31 @@ MUTANTS = [
     ("pool_drops_last_knn_entry", "for (int32_t e = 0; e < k; ++e) {\n                    int32_t i = lst[e];",
      "for (int32_t e = 0; e + 1 < k; ++e) {\n                    int32_t i = lst[e];"),
     ("passthrough_threshold_off_by_one", "        if (n <= P) {\n            /* small events", "        if (n < P) {\n            /* small events"),
+    ("pack_doc_id_shifted", "            if (doc_id) doc_id[at + j] = (int32_t)b;",
+     "            if (doc_id) doc_id[at + j] = (int32_t)(b + 1 < B ? b + 1 : b);"),
+    ("pack_drops_last_token", "        for (int32_t j = 0; j < T; ++j) {\n            for (int32_t d = 0; d < D; ++d)\n                packed",
+     "        for (int32_t j = 0; j + 1 < T; ++j) {\n            for (int32_t d = 0; d < D; ++d)\n                packed"),
+    ("unpack_no_zero_padding", "                    j < T ? packed[((int64_t)cu_seqlens[b] + j) * D + d] : 0.0f;",
+     "                    j < T ? packed[((int64_t)cu_seqlens[b] + j) * D + d] : 1.0f;"),
+    ("backward_ignores_weight", "    int32_t wcol = weighted != 0 ? charge_col : -1;", "    int32_t wcol = -1;"),
+    ("backward_drops_weight_term", "                    gi[wcol] += s / W[j];", "                    (void)s;"),
+    ("backward_unit_weight", "for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] * w / W[j];",
+     "for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] / W[j];"),
+    ("backward_sign_of_weight_term", "s += (double)g[c] * ((double)f[c] - (double)m[c]);",
+     "s += (double)g[c] * ((double)m[c] - (double)f[c]);"),
+    ("backward_overwrites_instead_of_adding", "for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] * w / W[j];",
+     "for (int32_t c = 0; c < C; ++c) gi[c] = (double)g[c] * w / W[j];"),
 ]
 
 PIN_CALLS = [
+    lambda m: nxt.test_pack_worked_example(m),
+    lambda m: [nxt.test_pack_counts_and_round_trip(m, s) for s in (0, 1)],
+    lambda m: nxt.test_pack_rejects_bad_counts(m),
+    lambda m: [nxt.test_pool_backward_finite_differences(m, mode, w, 0)
+               for mode in (0, 1) for w in (False, True)],
+    lambda m: nxt.test_pool_backward_worked_example(m),
+    lambda m: nxt.test_pool_backward_plain_mean_and_passthrough(m),
+    lambda m: nxt.test_pool_backward_zero_weight_token_and_linearity(m),
     lambda m: [pins.test_closed_forms(m, c) for c in pins._cases()],
     lambda m: pins.test_identical_cloud_knn_pool_lloyd(m),
     lambda m: [pins.test_fps_and_assign_brute_force(m, s) for s in (1, 2, 3)],

@@ -1,0 +1,219 @@
+"""Pins of the oracle's functions for the steps next to the path: token
+packing (pack / unpack) and the gradient of the pooling (pool_backward).
+
+Each is checked against something other than itself:
+  * hand-worked examples (tests/golden/next_forms.json);
+  * for packing: numpy's cumulative sum and bincount for cu_seqlens and
+    doc_id, the pack/unpack round trip, and rejection of counts outside
+    [0, P];
+  * for the gradient: central finite differences of the pooled means
+    computed in exact rational arithmetic (fractions.Fraction), in Voronoi
+    and kNN mode (pulses in several lists), weighted and unweighted; the
+    plain-mean special case (gradient = g / member count); pass-through
+    tokens (gradient = g); tokens of zero weight (no gradient); linearity in
+    the incoming gradient.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "next_forms.json")
+
+
+def _golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)
+
+
+# ---------------------------------------------------------------- packing
+
+def test_pack_worked_example(oracle_mod):
+    g = _golden()["pack"]
+    tc = np.array(g["token_count"], np.int32)
+    B, P, D = tc.size, g["P"], g["D"]
+    rows = np.arange(B * P * D, dtype=np.float32).reshape(B, P, D)
+    packed, doc, cu = oracle_mod.pack(tc, rows)
+    np.testing.assert_array_equal(packed, np.array(g["packed"], np.float32))
+    np.testing.assert_array_equal(doc, g["doc_id"])
+    np.testing.assert_array_equal(cu, g["cu_seqlens"])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_pack_counts_and_round_trip(oracle_mod, seed):
+    rng = np.random.default_rng(seed)
+    B, P, D = 37, 16, 5
+    tc = rng.integers(0, P + 1, B).astype(np.int32)
+    tc[::7] = 0
+    tc[3] = P
+    rows = rng.standard_normal((B, P, D)).astype(np.float32)
+    packed, doc, cu = oracle_mod.pack(tc, rows)
+    np.testing.assert_array_equal(cu, np.concatenate([[0], np.cumsum(tc)]))
+    np.testing.assert_array_equal(np.bincount(doc, minlength=B), tc)
+    assert packed.shape == (int(tc.sum()), D)
+    back = oracle_mod.unpack(tc, cu, packed, P)
+    mask = np.arange(P)[None, :] < tc[:, None]
+    np.testing.assert_array_equal(back[mask], rows[mask])
+    assert np.all(back[~mask] == 0)
+
+
+def test_pack_rejects_bad_counts(oracle_mod):
+    rows = np.zeros((2, 4, 1), np.float32)
+    for bad in ([5, 0], [-1, 2]):
+        with pytest.raises(RuntimeError):
+            oracle_mod.pack(np.array(bad, np.int32), rows)
+
+
+# --------------------------------------------------------- pooling gradient
+
+def _members(mode, n, T, assign, knn, k):
+    if mode == 0:
+        return [[i for i in range(n) if assign[i] == j] for j in range(T)]
+    return [[int(q) for q in knn[j * k:(j + 1) * k] if q >= 0] for j in range(T)]
+
+
+def _exact_pool(f, members, wcol):
+    """Pooled means of one event in exact rational arithmetic."""
+    out = []
+    for mem in members:
+        W = sum((f[i][wcol] if wcol >= 0 else Fraction(1)) for i in mem)
+        if W == 0:
+            out.append([Fraction(0)] * len(f[0]))
+            continue
+        row = []
+        for c in range(len(f[0])):
+            row.append(sum((f[i][wcol] if wcol >= 0 else Fraction(1)) * f[i][c] for i in mem) / W)
+        out.append(row)
+    return out
+
+
+def _fd_grad(fl, members, wcol, g):
+    """Central differences of sum_j g_j . m_j with respect to every feature."""
+    h = Fraction(1, 1 << 22)
+    f = [[Fraction(float(v)) for v in row] for row in fl]
+    grad = np.zeros((len(f), len(f[0])))
+    for i in range(len(f)):
+        for c in range(len(f[0])):
+            vals = []
+            for s in (1, -1):
+                f2 = [row[:] for row in f]
+                f2[i][c] += s * h
+                m = _exact_pool(f2, members, wcol)
+                vals.append(sum(Fraction(float(g[j][q])) * m[j][q]
+                                for j in range(len(m)) for q in range(len(m[0]))))
+            grad[i, c] = float((vals[0] - vals[1]) / (2 * h))
+    return grad
+
+
+def _case(seed, mode, weighted):
+    rng = np.random.default_rng(seed)
+    n, P, C, k = 11, 4, 3, 4
+    f = rng.integers(-8, 9, (n, C)).astype(np.float32) / 4
+    if weighted:
+        f[:, 1] = rng.integers(1, 9, n).astype(np.float32) / 2  # positive charges
+    T = P
+    assign = rng.integers(0, T, n).astype(np.int32)
+    assign[:T] = np.arange(T)  # no empty cell
+    knn = np.full((P, k), -1, np.int32)
+    for j in range(T):
+        kk = int(rng.integers(1, k + 1))
+        knn[j, :kk] = rng.choice(n, kk, replace=False)
+    return f, P, C, k, T, assign, knn
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_pool_backward_finite_differences(oracle_mod, mode, weighted, seed):
+    f, P, C, k, T, assign, knn = _case(seed, mode, weighted)
+    n = f.shape[0]
+    wcol = 1 if weighted else -1
+    off = np.array([0, n], np.int64)
+    tc = np.array([T], np.int32)
+    kw = dict(mode=mode, assign=assign if mode == 0 else None,
+              knn_idx=knn[None] if mode == 1 else None, k=k, weighted=weighted, charge_col=1)
+    pooled, _ = oracle_mod.pool(f, off, P, tc, **kw)
+    g = np.random.default_rng(seed + 10).standard_normal((1, P, C)).astype(np.float32)
+    got = oracle_mod.pool_backward(f, off, P, tc, pooled, g, **kw)
+    mem = _members(mode, n, T, assign, knn.reshape(-1), k)
+    want = _fd_grad(f, mem, wcol, g[0])
+    scale = np.abs(want).max()
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-5 * scale)
+
+
+def test_pool_backward_worked_example(oracle_mod):
+    g = _golden()["pool_backward"]
+    f = np.array(g["features"], np.float32)
+    out = oracle_mod.pool_backward(
+        f, np.array(g["offsets"]), g["P"], np.array(g["token_count"], np.int32),
+        np.array(g["pooled"], np.float32)[None], np.array(g["grad_pooled"], np.float32)[None],
+        mode=0, assign=np.array(g["assign"], np.int32), weighted=True, charge_col=g["charge_col"])
+    np.testing.assert_array_equal(out, np.array(g["grad_features"], np.float32))
+
+
+def test_pool_backward_plain_mean_and_passthrough(oracle_mod):
+    rng = np.random.default_rng(5)
+    n, P, C = 40, 8, 4
+    f = rng.standard_normal((n, C)).astype(np.float32)
+    f[:, 2] = rng.uniform(0.5, 3, n).astype(np.float32)
+    assign = rng.integers(0, P, n).astype(np.int32)
+    assign[:P] = np.arange(P)
+    off = np.array([0, n], np.int64)
+    tc = np.array([P], np.int32)
+    g = rng.standard_normal((1, P, C)).astype(np.float32)
+    pooled, cnt = oracle_mod.pool(f, off, P, tc, mode=0, assign=assign, weighted=False)
+    got = oracle_mod.pool_backward(f, off, P, tc, pooled, g, mode=0, assign=assign,
+                                   weighted=False, charge_col=2)
+    want = (g[0][assign].astype(np.float64) / cnt[0][assign][:, None]).astype(np.float32)
+    np.testing.assert_array_equal(got, want)
+    # a pass-through event (n <= P, one pulse per token): the gradient is g,
+    # weighted or not, except for a pulse of zero weight
+    m = 6
+    fp = f[:m].copy()
+    fp[4, 2] = 0.0
+    offp = np.array([0, m], np.int64)
+    tcp = np.array([m], np.int32)
+    ap = np.arange(m, dtype=np.int32)
+    gp = g[:, :m].copy()
+    pooled_p, _ = oracle_mod.pool(fp, offp, m, tcp, mode=0, assign=ap, weighted=True, charge_col=2)
+    gotp = oracle_mod.pool_backward(fp, offp, m, tcp, pooled_p, gp, mode=0, assign=ap,
+                                    weighted=True, charge_col=2)
+    keep = np.arange(m) != 4
+    np.testing.assert_array_equal(gotp[keep], gp[0][keep])
+    assert np.all(gotp[4] == 0)
+
+
+def test_pool_backward_zero_weight_token_and_linearity(oracle_mod):
+    rng = np.random.default_rng(6)
+    n, P, C, k = 30, 5, 3, 6
+    f = rng.standard_normal((n, C)).astype(np.float32)
+    f[:, 0] = rng.uniform(0.5, 2, n).astype(np.float32)
+    knn = np.full((1, P, k), -1, np.int32)
+    for j in range(P):
+        knn[0, j] = rng.choice(n, k, replace=False)
+    f[knn[0, 2], 0] = 0.0  # token 2 has zero weight
+    # pulses only in token 2 get no gradient
+    only2 = [i for i in knn[0, 2] if all(i not in knn[0, j] for j in range(P) if j != 2)]
+    off = np.array([0, n], np.int64)
+    tc = np.array([P], np.int32)
+    kw = dict(mode=1, knn_idx=knn, k=k, weighted=True, charge_col=0)
+    pooled, _ = oracle_mod.pool(f, off, P, tc, **kw)
+    g1 = rng.standard_normal((1, P, C)).astype(np.float32)
+    g2 = rng.standard_normal((1, P, C)).astype(np.float32)
+    a = oracle_mod.pool_backward(f, off, P, tc, pooled, g1, **kw).astype(np.float64)
+    b = oracle_mod.pool_backward(f, off, P, tc, pooled, g2, **kw).astype(np.float64)
+    s = oracle_mod.pool_backward(f, off, P, tc, pooled, g1 + g2, **kw).astype(np.float64)
+    np.testing.assert_allclose(s, a + b, rtol=1e-6, atol=1e-6)
+    assert only2 and np.all(a[only2] == 0)
+    # rows j >= T are ignored
+    g3 = g1.copy()
+    g3[0, P - 1] = 1e6
+    tcs = np.array([P - 1], np.int32)
+    knn_s = knn.copy()
+    knn_s[0, P - 1] = -1
+    kws = dict(kw, knn_idx=knn_s)
+    p_s, _ = oracle_mod.pool(f, off, P, tcs, **kws)
+    np.testing.assert_array_equal(oracle_mod.pool_backward(f, off, P, tcs, p_s, g3, **kws),
+                                  oracle_mod.pool_backward(f, off, P, tcs, p_s, g1, **kws))

@@ -190,6 +190,67 @@ fpstok_status fpstok_tokenize(const fpstok_batch* batch, const fpstok_params* pa
                               float* pooled, int32_t* cell_count, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* ------------------------------------------------ next to the path -- */
+
+/* Packing of every event's tokens into one variable-length sequence for
+ * block-diagonal attention (graphnet PR #923, "What is added":
+ * models/utils.py pack / unpack for variable-length packing; its review
+ * thread: doc_id is the event index of every packed token, the packed length
+ * is the number of tokens).  Event b contributes its first T_b =
+ * token_count[b] slots, events in order.
+ *   token_count [B] int32 in (T_b outside [0, P] is clamped into it)
+ *   rows        [B,P,D] f32 in: one row of D floats per slot (pooled
+ *               features, D = C; centroids, D = 4; ...)
+ *   packed      [B*P, D] f32 out: rows 0 .. n_tokens-1 receive the tokens'
+ *               rows, event after event; later rows are not written
+ *   doc_id      [B*P] int32 out: event of every packed row (same extent), or
+ *               NULL
+ *   cu_seqlens  [B+1] int32 out: cu_seqlens[b] = T_0 + ... + T_{b-1};
+ *               cu_seqlens[B] = n_tokens
+ * No workspace.  Errors: EINVAL (NULL pointers, num_events < 0, num_patches
+ * outside [1, FPSTOK_MAX_PATCHES], row_width < 1), EUNSUPPORTED (B*P >= 2^31),
+ * EHIP. */
+fpstok_status fpstok_pack(int64_t num_events, int32_t num_patches, int32_t row_width,
+                          const int32_t* token_count, const float* rows, float* packed,
+                          int32_t* doc_id, int32_t* cu_seqlens, void* stream);
+
+/* The inverse of fpstok_pack: rows[b][j] = packed[cu_seqlens[b] + j] for
+ * j < T_b, 0 for T_b <= j < P.
+ *   token_count [B] int32 in (clamped into [0, P]); cu_seqlens [B+1] int32 in
+ *   (as fpstok_pack writes it); packed [n_tokens, D] f32 in;
+ *   rows [B,P,D] f32 out
+ * Errors: as fpstok_pack. */
+fpstok_status fpstok_unpack(int64_t num_events, int32_t num_patches, int32_t row_width,
+                            const int32_t* token_count, const int32_t* cu_seqlens,
+                            const float* packed, float* rows, void* stream);
+
+/* Gradient of fpstok_pool with respect to the features, for training through
+ * the tokenizer (graphnet PR #923, "Dependencies": time per training step;
+ * "What is added": gradient tests).  Token j of event b with members M_j
+ * (Voronoi: assign = j; kNN: the list entries != -1), weights w_i, weight sum
+ * W_j and forward output m_j = pooled[b][j]: for i in M_j and W_j != 0
+ *   d m_j[c] / d f_i[c'] = [c = c'] w_i / W_j
+ *                        + [c' = weight column] (f_i[c] - m_j[c]) / W_j
+ * (the second term only for weighted pooling with charge_col >= 0; a token of
+ * zero weight contributes nothing).  grad_features[i][c'] = sum over the
+ * tokens j containing i, ascending, of sum_c grad_pooled[b][j][c] *
+ * d m_j[c] / d f_i[c'], accumulated in float64 in that order (per token:
+ * grad_pooled[j][c'] * w_i / W_j, then, for the weight column,
+ * (sum over c ascending of grad_pooled[j][c] * (f_i[c] - m_j[c])) / W_j),
+ * with W_j the float64 weight sum in member order; rounded to float32.
+ * Pulses in no token get 0.
+ *   token_count [B] int32 in; assign [N] int32 in (Voronoi mode) or knn_idx
+ *   [B,P,k] int32 in (kNN mode), as given to fpstok_pool
+ *   pooled      [B,P,C] f32 in: the output of fpstok_pool
+ *   grad_pooled [B,P,C] f32 in (rows j >= T_b are ignored)
+ *   grad_features [N,C] f32 out
+ * Errors: as fpstok_pool. */
+fpstok_status fpstok_pool_backward(const fpstok_batch* batch, const fpstok_params* params,
+                                   const int32_t* token_count, const int32_t* assign,
+                                   const int32_t* knn_idx, const float* pooled,
+                                   const float* grad_pooled, float* grad_features, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Debug check of the data preconditions of `batch` (offsets monotone with
  * offsets[0] = 0 and offsets[B] = N, finite coords, charge >= 0 when
  * charge_col >= 0).  Copies the inputs to the host and synchronizes `stream`:

@@ -392,6 +392,83 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
     return ok();
 }
 
+static fpstok_status check_pack(int64_t B, int32_t P, int32_t D) {
+    if (B < 0) return fail(FPSTOK_EINVAL, "num_events < 0");
+    if (P < 1 || P > FPSTOK_MAX_PATCHES)
+        return fail(FPSTOK_EINVAL, "num_patches must be in [1, %d]", FPSTOK_MAX_PATCHES);
+    if (D < 1) return fail(FPSTOK_EINVAL, "row_width must be >= 1");
+    if (B >= ((int64_t)1 << 31) / P) return fail(FPSTOK_EUNSUPPORTED, "num_events * num_patches >= 2^31");
+    if (B * (int64_t)P * D >= ((int64_t)1 << 62)) return fail(FPSTOK_EUNSUPPORTED, "rows too large");
+    return FPSTOK_OK;
+}
+
+FPSTOK_API fpstok_status fpstok_pack(int64_t num_events, int32_t num_patches, int32_t row_width,
+                                     const int32_t* token_count, const float* rows,
+                                     float* packed, int32_t* doc_id, int32_t* cu_seqlens,
+                                     void* stream) {
+    fpstok_status st = check_pack(num_events, num_patches, row_width);
+    if (st != FPSTOK_OK) return st;
+    if (!cu_seqlens) return fail(FPSTOK_EINVAL, "cu_seqlens is NULL");
+    if (num_events > 0 && (!token_count || !rows || !packed))
+        return fail(FPSTOK_EINVAL, "token_count, rows and packed are required");
+    hipError_t e = launch_pack(num_events, num_patches, row_width, token_count, rows, packed,
+                               doc_id, cu_seqlens, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pack kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_unpack(int64_t num_events, int32_t num_patches, int32_t row_width,
+                                       const int32_t* token_count, const int32_t* cu_seqlens,
+                                       const float* packed, float* rows, void* stream) {
+    fpstok_status st = check_pack(num_events, num_patches, row_width);
+    if (st != FPSTOK_OK) return st;
+    if (num_events == 0) return ok();
+    if (!token_count || !cu_seqlens || !packed || !rows)
+        return fail(FPSTOK_EINVAL, "token_count, cu_seqlens, packed and rows are required");
+    hipError_t e = launch_unpack(num_events, num_patches, row_width, token_count, cu_seqlens,
+                                 packed, rows, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "unpack kernel launch");
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_pool_backward(const fpstok_batch* bt, const fpstok_params* pr,
+                                              const int32_t* token_count, const int32_t* assign,
+                                              const int32_t* knn_idx, const float* pooled,
+                                              const float* grad_pooled, float* grad_features,
+                                              void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_common(bt, pr, true, false);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    if (!token_count || !pooled || !grad_pooled)
+        return fail(FPSTOK_EINVAL, "token_count, pooled and grad_pooled are required");
+    if (bt->num_points > 0 && !grad_features) return fail(FPSTOK_EINVAL, "grad_features is NULL");
+    if (pr->assign_mode == FPSTOK_VORONOI && !assign && bt->num_points > 0)
+        return fail(FPSTOK_EINVAL, "assign is required in Voronoi mode");
+    if (pr->assign_mode == FPSTOK_KNN && !knn_idx)
+        return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    PoolBwdArgs a{};
+    a.features = bt->features;
+    a.offsets = bt->offsets;
+    a.N = bt->num_points;
+    a.C = bt->num_features;
+    a.wcol = pr->pool_weighted ? bt->charge_col : -1;
+    a.P = pr->num_patches;
+    a.mode = pr->assign_mode == FPSTOK_KNN ? 1 : 0;
+    a.k = pr->assign_mode == FPSTOK_KNN ? pr->k : 1;
+    a.token_count = token_count;
+    a.assign = assign;
+    a.knn_idx = knn_idx;
+    a.pooled = pooled;
+    a.grad_pooled = grad_pooled;
+    a.grad = grad_features;
+    a.perm = at<int32_t>(ws, L.perm);
+    hipError_t e = launch_pool_backward(a, bt->num_events, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pool backward kernel launch");
+    return ok();
+}
+
 FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
                                          const int32_t* start_idx, int32_t* centroid_idx,
                                          float* centroids, int32_t* token_count, int32_t* assign,

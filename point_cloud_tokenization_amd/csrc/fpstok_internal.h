@@ -123,6 +123,27 @@ struct LloydArgs {
     int32_t* perm;
 };
 
+struct PoolBwdArgs {
+    const float* features;
+    const int64_t* offsets;
+    int64_t N;
+    int C;
+    int wcol;  // weight column, -1: unit weights
+    int P;
+    int mode;  // 0 Voronoi, 1 kNN
+    int k;
+    const int32_t* token_count;
+    const int32_t* assign;
+    const int32_t* knn_idx;
+    const float* pooled;
+    const float* grad_pooled;
+    float* grad;
+    int32_t* perm;   // [N] workspace (events beyond the LDS sort)
+    int64_t bits_cap;  // words of the kNN token bitmap in LDS (set by the launcher)
+};
+
+constexpr int64_t kBwdBitsCap = 24 * 1024;  // kNN backward: LDS bitmap words (96 KB)
+
 struct PoolArgs {
     const float* features;
     const int64_t* offsets;
@@ -172,5 +193,10 @@ hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s);
 hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s);
 hipError_t launch_pool_combine(const PoolArgs& a, hipStream_t s);
 hipError_t launch_pool_knn(const PoolArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_pack(int64_t B, int P, int D, const int32_t* tc, const float* rows,
+                       float* packed, int32_t* doc_id, int32_t* cu, hipStream_t s);
+hipError_t launch_unpack(int64_t B, int P, int D, const int32_t* tc, const int32_t* cu,
+                         const float* packed, float* rows, hipStream_t s);
+hipError_t launch_pool_backward(const PoolBwdArgs& a, int64_t B, hipStream_t s);
 
 }  // namespace fpstok

@@ -2714,6 +2714,191 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
     }
 }
 
+// ------------------------------------------------ token packing (next)
+
+__device__ __forceinline__ int clamp_count(int t, int P) { return t < 0 ? 0 : (t > P ? P : t); }
+
+// cu[b] = T_0 + ... + T_{b-1} (counts clamped into [0, P]), cu[B] = the
+// total.  One workgroup of 1024 threads, 1024 events per round.
+__global__ __launch_bounds__(1024) void pack_scan_kernel(const int32_t* __restrict__ tc, int64_t B,
+                                                         int P, int32_t* __restrict__ cu) {
+    __shared__ int s_w[16];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    int carry = 0;
+    for (int64_t base = 0; base < B; base += 1024) {
+        const int64_t b = base + tid;
+        const int t = b < B ? clamp_count(tc[b], P) : 0;
+        const int incl = wave_incl_scan(t);
+        if (lane == 63) s_w[wave] = incl;
+        __syncthreads();
+        int wb = 0, total = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int v = s_w[w];
+            wb += w < wave ? v : 0;
+            total += v;
+        }
+        if (b < B) cu[b] = carry + wb + incl - t;
+        carry += total;
+        __syncthreads();
+    }
+    if (tid == 0) cu[B] = carry;
+}
+
+// Event b's first T_b rows of D floats (one contiguous block) to packed rows
+// cu[b] ..; block (bx, by): bx threads along a row, by rows at a time.
+__global__ __launch_bounds__(256) void pack_copy_kernel(const int32_t* __restrict__ tc, int P, int D,
+                                                        const int32_t* __restrict__ cu,
+                                                        const float* __restrict__ rows,
+                                                        float* __restrict__ packed,
+                                                        int32_t* __restrict__ doc_id) {
+    const int64_t b = blockIdx.x;
+    const int T = clamp_count(tc[b], P);
+    const int64_t at = cu[b];
+    const float* __restrict__ src = rows + b * (int64_t)P * D;
+    float* __restrict__ dst = packed + at * D;
+    for (int j = threadIdx.y; j < T; j += blockDim.y)
+        for (int d = threadIdx.x; d < D; d += blockDim.x)
+            dst[(int64_t)j * D + d] = src[(int64_t)j * D + d];
+    if (doc_id) {
+        const int nt = blockDim.x * blockDim.y;
+        for (int j = threadIdx.y * blockDim.x + threadIdx.x; j < T; j += nt)
+            doc_id[at + j] = (int32_t)b;
+    }
+}
+
+// rows[b][j] = packed[cu[b] + j] for j < T_b, else 0.
+__global__ __launch_bounds__(256) void unpack_kernel(const int32_t* __restrict__ tc, int P, int D,
+                                                     const int32_t* __restrict__ cu,
+                                                     const float* __restrict__ packed,
+                                                     float* __restrict__ rows) {
+    const int64_t b = blockIdx.x;
+    const int T = clamp_count(tc[b], P);
+    const float* __restrict__ src = packed + (int64_t)cu[b] * D;
+    float* __restrict__ dst = rows + b * (int64_t)P * D;
+    for (int j = threadIdx.y; j < P; j += blockDim.y)
+        for (int d = threadIdx.x; d < D; d += blockDim.x)
+            dst[(int64_t)j * D + d] = j < T ? src[(int64_t)j * D + d] : 0.0f;
+}
+
+// ---------------------------------------------- pooling backward (next)
+
+// One token's contribution to column c of member i's gradient: g[c] * w_i /
+// W, then, for the weight column, (sum over c2 of g[c2] * (f_i[c2] - m[c2]))
+// / W, in float64 with no contraction.
+__device__ __forceinline__ double bwd_token(const PoolBwdArgs& a, int64_t b, int64_t off, int j,
+                                           int64_t i, double W, double wi, int c, double acc) {
+    const int C = a.C;
+    const float* __restrict__ g = a.grad_pooled + (b * a.P + j) * (int64_t)C;
+    acc = acc + (double)g[c] * wi / W;
+    if (c == a.wcol) {
+        const float* __restrict__ m = a.pooled + (b * a.P + j) * (int64_t)C;
+        const float* __restrict__ f = a.features + (off + i) * C;
+        double s = 0.0;
+        for (int c2 = 0; c2 < C; ++c2) s = s + (double)g[c2] * ((double)f[c2] - (double)m[c2]);
+        acc = acc + s / W;
+    }
+    return acc;
+}
+
+__device__ __forceinline__ double bwd_weight(const PoolBwdArgs& a, int64_t row) {
+    return a.wcol >= 0 ? (double)a.features[row * a.C + a.wcol] : 1.0;
+}
+
+// Gradient of the pooling with respect to the features, one workgroup per
+// event.  Token weight sums W_j first (float64, member order: Voronoi
+// members sorted by slot, stable, so ascending; kNN lists in list order),
+// then one thread per pulse adds, column by column, the contributions of the
+// tokens that hold it, in ascending token order.  kNN mode finds
+// a pulse's tokens in a per-pulse bitmap over the tokens (dynamic LDS,
+// a.bits_cap words) when it fits, else by scanning every list.
+__global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
+    __shared__ double s_W[kMaxP];
+    __shared__ int s_cnt[kSortW * kMaxP];
+    __shared__ int s_off[kMaxP + 1];
+    __shared__ int s_perm[kLdsPerm];
+    extern __shared__ uint32_t s_bits[];
+    const int64_t b = blockIdx.x;
+    int64_t off;
+    int n;
+    event_range(a.offsets, a.N, b, off, n);
+    if (n == 0) return;
+    const int tid = threadIdx.x;
+    const int P = a.P;
+    const int C = a.C;
+    const int T = clamp_count(a.token_count[b], P);
+    if (a.mode == 0) {
+        if (T >= 1) {
+            int* perm = n <= kLdsPerm ? s_perm : a.perm + off;
+            block_sort_by_token(a.assign + off, n, T, perm, s_cnt, s_off);
+            for (int j = tid; j < T; j += kSortT) {
+                double W = 0.0;
+                for (int m = s_off[j]; m < s_off[j + 1]; ++m) W = W + bwd_weight(a, off + perm[m]);
+                s_W[j] = W;
+            }
+        }
+        __syncthreads();
+        for (int64_t i = tid; i < n; i += kSortT) {
+            const int j = a.assign[off + i];
+            const bool in = T >= 1 && j >= 0 && j < T && s_W[j] != 0.0;
+            const double W = in ? s_W[j] : 1.0;
+            const double wi = bwd_weight(a, off + i);
+            float* __restrict__ out = a.grad + (off + i) * C;
+            for (int c = 0; c < C; ++c)
+                out[c] = (float)(in ? bwd_token(a, b, off, j, i, W, wi, c, 0.0) : 0.0);
+        }
+        return;
+    }
+    // kNN: weight sums in list order
+    const int k = a.k;
+    const int32_t* __restrict__ lists = a.knn_idx + b * (int64_t)P * k;
+    for (int j = tid; j < T; j += kSortT) {
+        double W = 0.0;
+        for (int e = 0; e < k; ++e) {
+            const int q = lists[(int64_t)j * k + e];
+            if (q >= 0 && q < n) W = W + bwd_weight(a, off + q);
+        }
+        s_W[j] = W;
+    }
+    const int PW = (P + 31) >> 5;
+    const bool use_bits = (int64_t)n * PW <= a.bits_cap;
+    if (use_bits) {
+        for (int64_t q = tid; q < (int64_t)n * PW; q += kSortT) s_bits[q] = 0u;
+        __syncthreads();
+        for (int j = tid; j < T; j += kSortT)
+            for (int e = 0; e < k; ++e) {
+                const int q = lists[(int64_t)j * k + e];
+                if (q >= 0 && q < n) atomicOr(&s_bits[(int64_t)q * PW + (j >> 5)], 1u << (j & 31));
+            }
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += kSortT) {
+        const double wi = bwd_weight(a, off + i);
+        float* __restrict__ out = a.grad + (off + i) * C;
+        for (int c = 0; c < C; ++c) {
+            double acc = 0.0;
+            if (use_bits) {
+                for (int w = 0; w < PW; ++w) {
+                    uint32_t bits = s_bits[i * PW + w];
+                    while (bits) {
+                        const int j = (w << 5) + (int)__builtin_ctz(bits);
+                        bits &= bits - 1u;
+                        if (s_W[j] != 0.0) acc = bwd_token(a, b, off, j, i, s_W[j], wi, c, acc);
+                    }
+                }
+            } else {
+                for (int j = 0; j < T; ++j) {
+                    bool hit = false;
+                    for (int e = 0; e < k; ++e) hit = hit || lists[(int64_t)j * k + e] == (int)i;
+                    if (hit && s_W[j] != 0.0) acc = bwd_token(a, b, off, j, i, s_W[j], wi, c, acc);
+                }
+            }
+            out[c] = (float)acc;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline unsigned grid1(int64_t x) { return (unsigned)(x < 1 ? 1 : x); }
@@ -2841,6 +3026,36 @@ hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_
 
 hipError_t launch_pool_knn(const PoolArgs& a, int64_t B, hipStream_t s) {
     hipLaunchKernelGGL(pool_knn_kernel, dim3(grid1(B)), dim3(kSortT), 0, s, a);
+    return hipGetLastError();
+}
+
+static dim3 row_block(int D) {
+    const int bx = D < 256 ? D : 256;
+    return dim3((unsigned)bx, (unsigned)(256 / bx));
+}
+
+hipError_t launch_pack(int64_t B, int P, int D, const int32_t* tc, const float* rows,
+                       float* packed, int32_t* doc_id, int32_t* cu, hipStream_t s) {
+    hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(1024), 0, s, tc, B, P, cu);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || B == 0) return e;
+    hipLaunchKernelGGL(pack_copy_kernel, dim3((unsigned)B), row_block(D), 0, s, tc, P, D,
+                       (const int32_t*)cu, rows, packed, doc_id);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(int64_t B, int P, int D, const int32_t* tc, const int32_t* cu,
+                         const float* packed, float* rows, hipStream_t s) {
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)B), row_block(D), 0, s, tc, P, D, cu, packed,
+                       rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_backward(const PoolBwdArgs& a, int64_t B, hipStream_t s) {
+    PoolBwdArgs p = a;
+    p.bits_cap = a.mode == 1 ? kBwdBitsCap : 0;
+    const size_t lds = sizeof(uint32_t) * (size_t)p.bits_cap;
+    hipLaunchKernelGGL(pool_backward_kernel, dim3(grid1(B)), dim3(kSortT), lds, s, p);
     return hipGetLastError();
 }
 

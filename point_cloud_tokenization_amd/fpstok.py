@@ -65,8 +65,13 @@ def lib():
         L.fpstok_pool.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fpstok_tokenize.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fpstok_validate.argtypes = [B, vp]
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.fpstok_pack.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.fpstok_unpack.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.fpstok_pool_backward.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
-                  "fpstok_pool", "fpstok_tokenize", "fpstok_validate"):
+                  "fpstok_pool", "fpstok_tokenize", "fpstok_validate", "fpstok_pack",
+                  "fpstok_unpack", "fpstok_pool_backward"):
             getattr(L, f).restype = ctypes.c_int
         L.fpstok_status_string.argtypes = [ctypes.c_int]
         L.fpstok_status_string.restype = ctypes.c_char_p
@@ -189,6 +194,45 @@ def pool(bt, pr, token_count, assign_, knn_idx, pooled, cell_count, ws, stream=N
     _check(lib().fpstok_pool(ctypes.byref(bt), ctypes.byref(pr), _ptr(token_count),
                              _ptr(assign_), _ptr(knn_idx), _ptr(pooled), _ptr(cell_count),
                              _ptr(ws), ws.numel(), _stream_handle(stream)), "fpstok_pool")
+
+
+def pool_backward(bt, pr, token_count, assign_, knn_idx, pooled, grad_pooled, grad_features,
+                  ws, stream=None):
+    """fpstok_pool_backward: gradient of the pooling with respect to the features."""
+    _check(lib().fpstok_pool_backward(ctypes.byref(bt), ctypes.byref(pr), _ptr(token_count),
+                                      _ptr(assign_), _ptr(knn_idx), _ptr(pooled),
+                                      _ptr(grad_pooled), _ptr(grad_features), _ptr(ws),
+                                      ws.numel(), _stream_handle(stream)), "fpstok_pool_backward")
+
+
+def pack(token_count, rows, packed, doc_id, cu_seqlens, stream=None):
+    """fpstok_pack on device tensors: token_count [B] int32, rows [B,P,D]
+    float32; packed [B*P,D] float32, doc_id [B*P] int32 (or None) and
+    cu_seqlens [B+1] int32 are written."""
+    import torch
+
+    B, P, D = rows.shape
+    _need(token_count, torch.int32, "token_count")
+    _need(rows, torch.float32, "rows")
+    _need(packed, torch.float32, "packed")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    if doc_id is not None:
+        _need(doc_id, torch.int32, "doc_id")
+    _check(lib().fpstok_pack(B, P, D, _ptr(token_count), _ptr(rows), _ptr(packed), _ptr(doc_id),
+                             _ptr(cu_seqlens), _stream_handle(stream)), "fpstok_pack")
+
+
+def unpack(token_count, cu_seqlens, packed, rows, stream=None):
+    """fpstok_unpack: rows [B,P,D] float32 from the packed rows."""
+    import torch
+
+    B, P, D = rows.shape
+    for t, dt, name in ((token_count, torch.int32, "token_count"),
+                        (cu_seqlens, torch.int32, "cu_seqlens"),
+                        (packed, torch.float32, "packed"), (rows, torch.float32, "rows")):
+        _need(t, dt, name)
+    _check(lib().fpstok_unpack(B, P, D, _ptr(token_count), _ptr(cu_seqlens), _ptr(packed),
+                               _ptr(rows), _stream_handle(stream)), "fpstok_unpack")
 
 
 def tokenize_call(bt, pr, centroid_idx, centroids, token_count, assign_, knn_idx, pooled,

@@ -206,6 +206,55 @@ class Runner:
         return {c: v / steps for c, v in out.items()}
 
 
+def time_next(b, reps=50):
+    """The calls next to the path on one workload, after one forward call:
+    fpstok_pool_backward, and fpstok_pack / fpstok_unpack of the pooled rows.
+    Each is timed with a HIP event pair around `reps` back-to-back calls on
+    the current stream; GB/s is the algorithmic bytes (stated per call) over
+    the mean call time."""
+    import torch
+
+    r = Runner(b)
+    F, t, o = r.F, r.tok, r.tok.out
+    t()
+    torch.cuda.synchronize()
+    B, P = o["pooled"].shape[:2]
+    N, C = r.f.shape
+    dev = r.f.device
+    gp = torch.ones_like(o["pooled"])
+    grad = torch.empty_like(r.f)
+    T = int(o["token_count"].clamp(0, P).sum().item())
+    packed = torch.empty((B * P, C), dtype=torch.float32, device=dev)
+    doc = torch.empty(B * P, dtype=torch.int32, device=dev)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    rows = torch.empty_like(o["pooled"])
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    sec = timed(lambda: F.pool_backward(t.bt, t.pr, o["token_count"], o["assign"], o["knn_idx"],
+                                        o["pooled"], gp, grad, t.ws))
+    # reads features, the slot or list entries and two [B,P,C] rows; writes the gradient
+    nb = 4 * N * C * 2 + 4 * N + 8 * B * P * C + (4 * B * P * b["k"] if b["mode"] == 1 else 0)
+    out["pool_backward"] = dict(us=sec * 1e6, bytes=nb, GBps=nb / sec / 1e9)
+    sec = timed(lambda: F.pack(o["token_count"], o["pooled"], packed, doc, cu))
+    nb = 4 * B + 4 * (B + 1) + T * (8 * C + 4)
+    out["pack"] = dict(us=sec * 1e6, bytes=nb, GBps=nb / sec / 1e9, tokens=T)
+    sec = timed(lambda: F.unpack(o["token_count"], cu, packed, rows))
+    nb = 8 * B + 4 * T * C + 4 * B * P * C
+    out["unpack"] = dict(us=sec * 1e6, bytes=nb, GBps=nb / sec / 1e9)
+    return out
+
+
 def cpu_baseline(b, budget_s):
     """The oracle as it stands, single-threaded, on repeats of the same batch
     until about budget_s seconds of CPU work."""
@@ -331,6 +380,12 @@ def main():
                 P=s2["P"])
             log("secondary %s: %s" % (name, secondary[name]))
 
+    nxt = {}
+    if args.secondary:
+        for name in (args.workload, "icecube_b64_knn16"):
+            nxt[name] = time_next(synth.make_batch(name))
+            log("next %s: %s" % (name, nxt[name]))
+
     cpu = cpu_baseline(b, args.cpu_budget)
     line = {
         "metric": "events/sec (FPS+assign+pool) at batch 64, P=128",
@@ -357,6 +412,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "next": nxt,
         "host": {"cpu": platform.processor() or platform.machine(),
                  "nproc": os.cpu_count(), "gpu": torch.cuda.get_device_name(0)},
     }

@@ -2786,15 +2786,14 @@ __global__ __launch_bounds__(256) void unpack_kernel(const int32_t* __restrict__
 
 // One token's contribution to column c of member i's gradient: g[c] * w_i /
 // W, then, for the weight column, (sum over c2 of g[c2] * (f_i[c2] - m[c2]))
-// / W, in float64 with no contraction.
-__device__ __forceinline__ double bwd_token(const PoolBwdArgs& a, int64_t b, int64_t off, int j,
-                                           int64_t i, double W, double wi, int c, double acc) {
-    const int C = a.C;
-    const float* __restrict__ g = a.grad_pooled + (b * a.P + j) * (int64_t)C;
+// / W, in float64 with no contraction.  g, m: the token's rows (LDS or
+// device memory), f: the member's feature row.
+__device__ __forceinline__ double bwd_token(const float* __restrict__ g,
+                                           const float* __restrict__ m,
+                                           const float* __restrict__ f, int C, int wcol,
+                                           double W, double wi, int c, double acc) {
     acc = acc + (double)g[c] * wi / W;
-    if (c == a.wcol) {
-        const float* __restrict__ m = a.pooled + (b * a.P + j) * (int64_t)C;
-        const float* __restrict__ f = a.features + (off + i) * C;
+    if (c == wcol) {
         double s = 0.0;
         for (int c2 = 0; c2 < C; ++c2) s = s + (double)g[c2] * ((double)f[c2] - (double)m[c2]);
         acc = acc + s / W;
@@ -2806,18 +2805,96 @@ __device__ __forceinline__ double bwd_weight(const PoolBwdArgs& a, int64_t row) 
     return a.wcol >= 0 ? (double)a.features[row * a.C + a.wcol] : 1.0;
 }
 
+// Voronoi: each pulse's one token.  G, M: the event's token rows [T][C].
+__device__ __forceinline__ void bwd_pulses_voronoi(const PoolBwdArgs& a, int64_t off, int n,
+                                                   int T, const double* s_W,
+                                                   const float* __restrict__ G,
+                                                   const float* __restrict__ M) {
+    const int C = a.C;
+    for (int64_t i = threadIdx.x; i < n; i += kSortT) {
+        const int j = a.assign[off + i];
+        const bool in = T >= 1 && j >= 0 && j < T && s_W[j] != 0.0;
+        const double W = in ? s_W[j] : 1.0;
+        const double wi = bwd_weight(a, off + i);
+        const float* __restrict__ f = a.features + (off + i) * C;
+        const int jj = in ? j : 0;
+        float* __restrict__ out = a.grad + (off + i) * C;
+        for (int c = 0; c < C; ++c)
+            out[c] = (float)(in ? bwd_token(G + (int64_t)jj * C, M + (int64_t)jj * C, f, C,
+                                            a.wcol, W, wi, c, 0.0)
+                                : 0.0);
+    }
+}
+
+// kNN: each pulse's tokens in ascending order, from its words of the token
+// bitmap (bits: [n][PW] in LDS, or NULL: scan every list).
+__device__ __forceinline__ void bwd_pulses_knn(const PoolBwdArgs& a, int64_t off, int n, int T,
+                                               const double* s_W, const float* __restrict__ G,
+                                               const float* __restrict__ M,
+                                               const uint32_t* bits, int PW,
+                                               const int32_t* __restrict__ lists) {
+    const int C = a.C;
+    const int k = a.k;
+    for (int64_t i = threadIdx.x; i < n; i += kSortT) {
+        const double wi = bwd_weight(a, off + i);
+        const float* __restrict__ f = a.features + (off + i) * C;
+        float* __restrict__ out = a.grad + (off + i) * C;
+        uint32_t tw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) tw[w] = bits && w < PW ? bits[i * PW + w] : 0u;
+        for (int c = 0; c < C; ++c) {
+            double acc = 0.0;
+            if (bits && PW <= 4) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t bw = tw[w];
+                    while (bw) {
+                        const int j = (w << 5) + (int)__builtin_ctz(bw);
+                        bw &= bw - 1u;
+                        if (s_W[j] != 0.0)
+                            acc = bwd_token(G + (int64_t)j * C, M + (int64_t)j * C, f, C, a.wcol,
+                                            s_W[j], wi, c, acc);
+                    }
+                }
+            } else if (bits) {
+                for (int w = 0; w < PW; ++w) {
+                    uint32_t bw = bits[i * PW + w];
+                    while (bw) {
+                        const int j = (w << 5) + (int)__builtin_ctz(bw);
+                        bw &= bw - 1u;
+                        if (s_W[j] != 0.0)
+                            acc = bwd_token(G + (int64_t)j * C, M + (int64_t)j * C, f, C, a.wcol,
+                                            s_W[j], wi, c, acc);
+                    }
+                }
+            } else {
+                for (int j = 0; j < T; ++j) {
+                    bool hit = false;
+                    for (int e = 0; e < k; ++e) hit = hit || lists[(int64_t)j * k + e] == (int)i;
+                    if (hit && s_W[j] != 0.0)
+                        acc = bwd_token(G + (int64_t)j * C, M + (int64_t)j * C, f, C, a.wcol,
+                                        s_W[j], wi, c, acc);
+                }
+            }
+            out[c] = (float)acc;
+        }
+    }
+}
+
 // Gradient of the pooling with respect to the features, one workgroup per
 // event.  Token weight sums W_j first (float64, member order: Voronoi
-// members sorted by slot, stable, so ascending; kNN lists in list order),
-// then one thread per pulse adds, column by column, the contributions of the
-// tokens that hold it, in ascending token order.  kNN mode finds
-// a pulse's tokens in a per-pulse bitmap over the tokens (dynamic LDS,
+// members sorted by slot, stable, so ascending; kNN lists in list order, k
+// entries loaded together), then one thread per pulse adds, column by
+// column, the contributions of the tokens that hold it, in ascending token
+// order.  The event's grad_pooled and pooled rows are copied to LDS (the
+// sort's permutation area, free by then) when they fit.  kNN mode finds a
+// pulse's tokens in a per-pulse bitmap over the tokens (dynamic LDS,
 // a.bits_cap words) when it fits, else by scanning every list.
 __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
     __shared__ double s_W[kMaxP];
     __shared__ int s_cnt[kSortW * kMaxP];
     __shared__ int s_off[kMaxP + 1];
-    __shared__ int s_perm[kLdsPerm];
+    __shared__ __align__(16) int s_perm[kLdsPerm];
     extern __shared__ uint32_t s_bits[];
     const int64_t b = blockIdx.x;
     int64_t off;
@@ -2828,74 +2905,82 @@ __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
     const int P = a.P;
     const int C = a.C;
     const int T = clamp_count(a.token_count[b], P);
+    const int k = a.k;
+    const int32_t* __restrict__ lists = a.knn_idx ? a.knn_idx + b * (int64_t)P * k : nullptr;
+    const int PW = (P + 31) >> 5;
+    const bool use_bits = a.mode == 1 && (int64_t)n * PW <= a.bits_cap;
     if (a.mode == 0) {
         if (T >= 1) {
             int* perm = n <= kLdsPerm ? s_perm : a.perm + off;
             block_sort_by_token(a.assign + off, n, T, perm, s_cnt, s_off);
             for (int j = tid; j < T; j += kSortT) {
+                // kBatch weights loaded together, added in member order (a
+                // padded batch adds +0.0, which leaves the sum unchanged)
                 double W = 0.0;
-                for (int m = s_off[j]; m < s_off[j + 1]; ++m) W = W + bwd_weight(a, off + perm[m]);
+                const int e = s_off[j + 1];
+                for (int m0 = s_off[j]; m0 < e; m0 += kBatch) {
+                    double wv[kBatch];
+#pragma unroll
+                    for (int q = 0; q < kBatch; ++q)
+                        wv[q] = m0 + q < e ? bwd_weight(a, off + perm[m0 + q]) : 0.0;
+#pragma unroll
+                    for (int q = 0; q < kBatch; ++q) W = W + wv[q];
+                }
                 s_W[j] = W;
             }
         }
-        __syncthreads();
-        for (int64_t i = tid; i < n; i += kSortT) {
-            const int j = a.assign[off + i];
-            const bool in = T >= 1 && j >= 0 && j < T && s_W[j] != 0.0;
-            const double W = in ? s_W[j] : 1.0;
-            const double wi = bwd_weight(a, off + i);
-            float* __restrict__ out = a.grad + (off + i) * C;
-            for (int c = 0; c < C; ++c)
-                out[c] = (float)(in ? bwd_token(a, b, off, j, i, W, wi, c, 0.0) : 0.0);
+    } else {
+        if (use_bits) {
+            for (int64_t q = tid; q < (int64_t)n * PW; q += kSortT) s_bits[q] = 0u;
+            __syncthreads();
         }
-        return;
-    }
-    // kNN: weight sums in list order
-    const int k = a.k;
-    const int32_t* __restrict__ lists = a.knn_idx + b * (int64_t)P * k;
-    for (int j = tid; j < T; j += kSortT) {
-        double W = 0.0;
-        for (int e = 0; e < k; ++e) {
-            const int q = lists[(int64_t)j * k + e];
-            if (q >= 0 && q < n) W = W + bwd_weight(a, off + q);
-        }
-        s_W[j] = W;
-    }
-    const int PW = (P + 31) >> 5;
-    const bool use_bits = (int64_t)n * PW <= a.bits_cap;
-    if (use_bits) {
-        for (int64_t q = tid; q < (int64_t)n * PW; q += kSortT) s_bits[q] = 0u;
-        __syncthreads();
-        for (int j = tid; j < T; j += kSortT)
-            for (int e = 0; e < k; ++e) {
-                const int q = lists[(int64_t)j * k + e];
-                if (q >= 0 && q < n) atomicOr(&s_bits[(int64_t)q * PW + (j >> 5)], 1u << (j & 31));
+        for (int j = tid; j < T; j += kSortT) {
+            double W = 0.0;
+            for (int e0 = 0; e0 < k; e0 += kBatch) {
+                int iv[kBatch];
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) iv[q] = e0 + q < k ? lists[(int64_t)j * k + e0 + q] : -1;
+                double wv[kBatch];
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q)
+                    wv[q] = iv[q] >= 0 && iv[q] < n ? bwd_weight(a, off + iv[q]) : 0.0;
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) W = W + wv[q];
+                if (use_bits) {
+#pragma unroll
+                    for (int q = 0; q < kBatch; ++q)
+                        if (iv[q] >= 0 && iv[q] < n)
+                            atomicOr(&s_bits[(int64_t)iv[q] * PW + (j >> 5)], 1u << (j & 31));
+                }
             }
+            s_W[j] = W;
+        }
     }
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kSortT) {
-        const double wi = bwd_weight(a, off + i);
-        float* __restrict__ out = a.grad + (off + i) * C;
-        for (int c = 0; c < C; ++c) {
-            double acc = 0.0;
-            if (use_bits) {
-                for (int w = 0; w < PW; ++w) {
-                    uint32_t bits = s_bits[i * PW + w];
-                    while (bits) {
-                        const int j = (w << 5) + (int)__builtin_ctz(bits);
-                        bits &= bits - 1u;
-                        if (s_W[j] != 0.0) acc = bwd_token(a, b, off, j, i, s_W[j], wi, c, acc);
-                    }
-                }
-            } else {
-                for (int j = 0; j < T; ++j) {
-                    bool hit = false;
-                    for (int e = 0; e < k; ++e) hit = hit || lists[(int64_t)j * k + e] == (int)i;
-                    if (hit && s_W[j] != 0.0) acc = bwd_token(a, b, off, j, i, s_W[j], wi, c, acc);
-                }
-            }
-            out[c] = (float)acc;
+    // the event's token rows, in LDS when both fit the permutation area
+    const float* G = a.grad_pooled + b * (int64_t)P * C;
+    const float* M = a.pooled + b * (int64_t)P * C;
+    const bool stage = 2 * (int64_t)T * C <= kLdsPerm;
+    if (stage) {
+        float* sg = reinterpret_cast<float*>(s_perm);
+        for (int q = tid; q < T * C; q += kSortT) {
+            sg[q] = G[q];
+            sg[T * C + q] = M[q];
         }
+    }
+    __syncthreads();
+    const uint32_t* bits = use_bits ? s_bits : nullptr;
+    if (stage) {
+        const float* sg = reinterpret_cast<const float*>(s_perm);
+        if (a.mode == 0)
+            bwd_pulses_voronoi(a, off, n, T, s_W, sg, sg + T * C);
+        else
+            bwd_pulses_knn(a, off, n, T, s_W, sg, sg + T * C, bits, PW, lists);
+    } else {
+        if (a.mode == 0)
+            bwd_pulses_voronoi(a, off, n, T, s_W, G, M);
+        else
+            bwd_pulses_knn(a, off, n, T, s_W, G, M, bits, PW, lists);
     }
 }
 

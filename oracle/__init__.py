@@ -57,9 +57,12 @@ def _load():
         lib.oracle_unpack.argtypes = [P, i64, i32, i32, P, P, P]
         lib.oracle_pool_backward.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P,
                                              P, P, P]
+        lib.oracle_philox4x32_10.argtypes = [P, P, P]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_random_start.argtypes = [P, i64, ctypes.c_uint64, ctypes.c_uint64, P]
         for f in ("oracle_sample", "oracle_assign", "oracle_knn", "oracle_lloyd",
                   "oracle_pool", "oracle_tokenize", "oracle_pack", "oracle_unpack",
-                  "oracle_pool_backward"):
+                  "oracle_pool_backward", "oracle_random_start"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -247,4 +250,23 @@ def pool_backward(features, offsets, P, token_count, pooled, grad_pooled, mode=0
     _check(_load().oracle_pool_backward(_ptr(f), _ptr(o), B, C, charge_col, P, mode, k,
                                         int(weighted), _ptr(tc), _ptr(a), _ptr(kn), _ptr(pm),
                                         _ptr(g), _ptr(out)), "pool_backward")
+    return out
+
+
+def philox4x32_10(counter, key):
+    """One block of Philox4x32-10 (4 words) for a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def random_start(offsets, seed, step=0):
+    """A random FPS start per event ([B] int32) from Philox4x32-10."""
+    o = _offs(offsets)
+    B = o.size - 1
+    out = np.empty(B, np.int32)
+    _check(_load().oracle_random_start(_ptr(o), B, int(seed) & (2**64 - 1),
+                                       int(step) & (2**64 - 1), _ptr(out)), "random_start")
     return out

@@ -526,3 +526,54 @@ int oracle_pool_backward(const float* features, const int64_t* offsets, int64_t 
     free(W); free(G);
     return 0;
 }
+
+/* ----------------------------------------------- random FPS start (next) -- */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011): ten rounds
+ * of two 32x32->64-bit multiplications (multipliers 0xD2511F53 and
+ * 0xCD9E8D57) mixed with the key, the key advanced by the Weyl constants
+ * 0x9E3779B9 and 0xBB67AE85 between rounds. */
+static void philox4x32_10(const uint32_t in[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = in[0], c1 = in[1], c2 = in[2], c3 = in[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Exposed for the generator's known-answer tests. */
+void oracle_philox4x32_10(const uint32_t* in, const uint32_t* key, uint32_t* out)
+{
+    philox4x32_10(in, key, out);
+}
+
+/* A random FPS start per event ([PR] review thread on the FPS arguments:
+ * start_idx, random_start, generator; the pages do not say how the start is
+ * drawn).  Event b draws word 0 of Philox4x32-10 at counter (b low, b high,
+ * step low, step high) with key (seed low, seed high) and maps it to
+ * floor(u * n_b / 2^32), a pulse index in [0, n_b); an empty event gets 0.
+ *   start_idx: [B] int32 out */
+int oracle_random_start(const int64_t* offsets, int64_t B, uint64_t seed, uint64_t step,
+                        int32_t* start_idx)
+{
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t n = offsets[b + 1] - offsets[b];
+        uint32_t in[4] = {(uint32_t)b, (uint32_t)((uint64_t)b >> 32), (uint32_t)step,
+                          (uint32_t)(step >> 32)};
+        uint32_t out[4];
+        philox4x32_10(in, key, out);
+        start_idx[b] = n > 0 ? (int32_t)(((uint64_t)out[0] * (uint64_t)n) >> 32) : 0;
+    }
+    return 0;
+}

@@ -44,6 +44,10 @@ MUTANTS = [
      "        for (int32_t j = 0; j + 1 < T; ++j) {\n            for (int32_t d = 0; d < D; ++d)\n                packed"),
     ("unpack_no_zero_padding", "                    j < T ? packed[((int64_t)cu_seqlens[b] + j) * D + d] : 0.0f;",
      "                    j < T ? packed[((int64_t)cu_seqlens[b] + j) * D + d] : 1.0f;"),
+    ("philox_key_not_advanced", "        if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }", "        (void)r;"),
+    ("philox_words_swapped", "        uint32_t n1 = (uint32_t)p1;", "        uint32_t n1 = (uint32_t)p0;"),
+    ("random_start_modulo", "start_idx[b] = n > 0 ? (int32_t)(((uint64_t)out[0] * (uint64_t)n) >> 32) : 0;",
+     "start_idx[b] = n > 0 ? (int32_t)((uint64_t)out[0] % (uint64_t)n) : 0;"),
     ("backward_ignores_weight", "    int32_t wcol = weighted != 0 ? charge_col : -1;", "    int32_t wcol = -1;"),
     ("backward_drops_weight_term", "                    gi[wcol] += s / W[j];", "                    (void)s;"),
     ("backward_unit_weight", "for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] * w / W[j];",
@@ -63,6 +67,8 @@ PIN_CALLS = [
     lambda m: nxt.test_pool_backward_worked_example(m),
     lambda m: nxt.test_pool_backward_plain_mean_and_passthrough(m),
     lambda m: nxt.test_pool_backward_zero_weight_token_and_linearity(m),
+    lambda m: nxt.test_philox_known_answers(m),
+    lambda m: nxt.test_random_start_mapping_and_spread(m),
     lambda m: [pins.test_closed_forms(m, c) for c in pins._cases()],
     lambda m: pins.test_identical_cloud_knn_pool_lloyd(m),
     lambda m: [pins.test_fps_and_assign_brute_force(m, s) for s in (1, 2, 3)],

@@ -217,3 +217,38 @@ def test_pool_backward_zero_weight_token_and_linearity(oracle_mod):
     p_s, _ = oracle_mod.pool(f, off, P, tcs, **kws)
     np.testing.assert_array_equal(oracle_mod.pool_backward(f, off, P, tcs, p_s, g3, **kws),
                                   oracle_mod.pool_backward(f, off, P, tcs, p_s, g1, **kws))
+
+
+# ------------------------------------------------------- random FPS start
+
+def test_philox_known_answers(oracle_mod):
+    with open(os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")) as fh:
+        vecs = json.load(fh)["vectors"]
+    for v in vecs:
+        c = np.array([int(h, 16) for h in v["counter"]], np.uint32)
+        k = np.array([int(h, 16) for h in v["key"]], np.uint32)
+        np.testing.assert_array_equal(oracle_mod.philox4x32_10(c, k),
+                                      np.array([int(h, 16) for h in v["out"]], np.uint32))
+
+
+def test_random_start_mapping_and_spread(oracle_mod):
+    rng = np.random.default_rng(3)
+    n = rng.integers(0, 5000, 4000)
+    n[:7] = [0, 1, 2, 3, 2**31 - 1, 7, 1]
+    off = np.concatenate([[0], np.cumsum(n.astype(np.int64))])
+    s = oracle_mod.random_start(off, seed=12345, step=0)
+    # the mapping from word 0 of the counter's block, recomputed per event
+    for b in (0, 1, 2, 5, 100, 3999):
+        u = int(oracle_mod.philox4x32_10(np.array([b, 0, 0, 0], np.uint32),
+                                         np.array([12345, 0], np.uint32))[0])
+        assert s[b] == ((u * int(n[b])) >> 32 if n[b] > 0 else 0)
+    assert np.all((s >= 0) & ((s < n) | (n == 0)))
+    # roughly uniform: start / n over many events fills ten equal bins
+    frac = s[n > 100] / n[n > 100]
+    h = np.histogram(frac, bins=10, range=(0, 1))[0]
+    expect = frac.size / 10
+    assert ((h - expect) ** 2 / expect).sum() < 30  # chi-square, 9 dof
+    # a different step or seed gives different starts; the same ones repeat
+    assert np.any(oracle_mod.random_start(off, 12345, 1) != s)
+    assert np.any(oracle_mod.random_start(off, 12346, 0) != s)
+    np.testing.assert_array_equal(oracle_mod.random_start(off, 12345, 0), s)

@@ -208,7 +208,8 @@ class Runner:
 
 def time_next(b, reps=50):
     """The calls next to the path on one workload, after one forward call:
-    fpstok_pool_backward, and fpstok_pack / fpstok_unpack of the pooled rows.
+    fpstok_pool_backward, fpstok_pack / fpstok_unpack of the pooled rows and
+    fpstok_random_start.
     Each is timed with a HIP event pair around `reps` back-to-back calls on
     the current stream; GB/s is the algorithmic bytes (stated per call) over
     the mean call time."""
@@ -252,6 +253,9 @@ def time_next(b, reps=50):
     sec = timed(lambda: F.unpack(o["token_count"], cu, packed, rows))
     nb = 8 * B + 4 * T * C + 4 * B * P * C
     out["unpack"] = dict(us=sec * 1e6, bytes=nb, GBps=nb / sec / 1e9)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+    sec = timed(lambda: F.random_start(r.off, st, 1, 0))
+    out["random_start"] = dict(us=sec * 1e6, bytes=8 * (B + 1) + 4 * B)
     return out
 
 

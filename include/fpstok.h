@@ -251,6 +251,21 @@ fpstok_status fpstok_pool_backward(const fpstok_batch* batch, const fpstok_param
                                    const float* grad_pooled, float* grad_features, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* A random FPS start per event, for FPS's random_start option (graphnet PR
+ * #923, review thread on the FPS arguments: start_idx, random_start,
+ * generator; the pages do not say how the start is drawn).  Event b takes
+ * word 0 of Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC 2011) at counter (b low, b high, step low,
+ * step high) with key (seed low, seed high), maps it to
+ * floor(u * n_b / 2^32), a pulse index in [0, n_b), and writes it to
+ * start_idx[b] (0 for an empty event).  Pass the result as start_idx to
+ * fpstok_sample or fpstok_tokenize; change `step` (e.g. per training step)
+ * for new draws with the same seed.
+ *   offsets   [B+1] int64 in (device); start_idx [B] int32 out (device)
+ * Errors: EINVAL (NULL pointers, num_events < 0), EHIP. */
+fpstok_status fpstok_random_start(const int64_t* offsets, int64_t num_events, uint64_t seed,
+                                  uint64_t step, int32_t* start_idx, void* stream);
+
 /* Debug check of the data preconditions of `batch` (offsets monotone with
  * offsets[0] = 0 and offsets[B] = N, finite coords, charge >= 0 when
  * charge_col >= 0).  Copies the inputs to the host and synchronizes `stream`:

@@ -469,6 +469,19 @@ FPSTOK_API fpstok_status fpstok_pool_backward(const fpstok_batch* bt, const fpst
     return ok();
 }
 
+FPSTOK_API fpstok_status fpstok_random_start(const int64_t* offsets, int64_t num_events,
+                                             uint64_t seed, uint64_t step, int32_t* start_idx,
+                                             void* stream) {
+    if (num_events < 0) return fail(FPSTOK_EINVAL, "num_events < 0");
+    if (num_events == 0) return ok();
+    if (!offsets || !start_idx) return fail(FPSTOK_EINVAL, "offsets and start_idx are required");
+    if (num_events >= ((int64_t)1 << 31)) return fail(FPSTOK_EUNSUPPORTED, "num_events >= 2^31");
+    hipError_t e = launch_random_start(offsets, num_events, seed, step, start_idx,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "random start kernel launch");
+    return ok();
+}
+
 FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
                                          const int32_t* start_idx, int32_t* centroid_idx,
                                          float* centroids, int32_t* token_count, int32_t* assign,

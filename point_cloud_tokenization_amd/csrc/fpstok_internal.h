@@ -198,5 +198,7 @@ hipError_t launch_pack(int64_t B, int P, int D, const int32_t* tc, const float* 
 hipError_t launch_unpack(int64_t B, int P, int D, const int32_t* tc, const int32_t* cu,
                          const float* packed, float* rows, hipStream_t s);
 hipError_t launch_pool_backward(const PoolBwdArgs& a, int64_t B, hipStream_t s);
+hipError_t launch_random_start(const int64_t* offsets, int64_t B, uint64_t seed, uint64_t step,
+                               int32_t* start_idx, hipStream_t s);
 
 }  // namespace fpstok

@@ -2984,6 +2984,42 @@ __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
     }
 }
 
+// ----------------------------------------------- random FPS start (next)
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds, each
+// two 32x32 -> 64-bit products of counter words 0 and 2 with 0xD2511F53 and
+// 0xCD9E8D57, their halves crossed with words 1 and 3 and the key; the key
+// advances by 0x9E3779B9 and 0xBB67AE85 between rounds.  Returns word 0.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+
+// start_idx[b] = floor(u_b * n_b / 2^32), u_b = word 0 of the block at
+// counter (b, step) and key seed; one thread per event.
+__global__ __launch_bounds__(256) void random_start_kernel(const int64_t* __restrict__ offsets,
+                                                           int64_t B, uint64_t seed, uint64_t step,
+                                                           int32_t* __restrict__ start_idx) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= B) return;
+    const int64_t n = offsets[b + 1] - offsets[b];
+    const uint32_t u = philox_word0((uint32_t)b, (uint32_t)((uint64_t)b >> 32), (uint32_t)step,
+                                    (uint32_t)(step >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
+    start_idx[b] = n > 0 ? (int32_t)(((uint64_t)u * (uint64_t)n) >> 32) : 0;
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline unsigned grid1(int64_t x) { return (unsigned)(x < 1 ? 1 : x); }
@@ -3133,6 +3169,13 @@ hipError_t launch_unpack(int64_t B, int P, int D, const int32_t* tc, const int32
                          const float* packed, float* rows, hipStream_t s) {
     hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)B), row_block(D), 0, s, tc, P, D, cu, packed,
                        rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_random_start(const int64_t* offsets, int64_t B, uint64_t seed, uint64_t step,
+                               int32_t* start_idx, hipStream_t s) {
+    hipLaunchKernelGGL(random_start_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
+                       offsets, B, seed, step, start_idx);
     return hipGetLastError();
 }
 

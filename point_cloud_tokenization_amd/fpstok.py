@@ -69,9 +69,10 @@ def lib():
         L.fpstok_pack.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
         L.fpstok_unpack.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
         L.fpstok_pool_backward.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_random_start.argtypes = [vp, i64, ctypes.c_uint64, ctypes.c_uint64, vp, vp]
         for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
                   "fpstok_pool", "fpstok_tokenize", "fpstok_validate", "fpstok_pack",
-                  "fpstok_unpack", "fpstok_pool_backward"):
+                  "fpstok_unpack", "fpstok_pool_backward", "fpstok_random_start"):
             getattr(L, f).restype = ctypes.c_int
         L.fpstok_status_string.argtypes = [ctypes.c_int]
         L.fpstok_status_string.restype = ctypes.c_char_p
@@ -203,6 +204,20 @@ def pool_backward(bt, pr, token_count, assign_, knn_idx, pooled, grad_pooled, gr
                                       _ptr(assign_), _ptr(knn_idx), _ptr(pooled),
                                       _ptr(grad_pooled), _ptr(grad_features), _ptr(ws),
                                       ws.numel(), _stream_handle(stream)), "fpstok_pool_backward")
+
+
+def random_start(offsets, start_idx, seed, step=0, stream=None):
+    """fpstok_random_start: a random FPS start per event into start_idx [B]
+    int32 (offsets [B+1] int64), from Philox4x32-10 with the given seed and
+    step."""
+    import torch
+
+    _need(offsets, torch.int64, "offsets")
+    _need(start_idx, torch.int32, "start_idx")
+    B = offsets.numel() - 1
+    _check(lib().fpstok_random_start(_ptr(offsets), B, int(seed) & (2**64 - 1),
+                                     int(step) & (2**64 - 1), _ptr(start_idx),
+                                     _stream_handle(stream)), "fpstok_random_start")
 
 
 def pack(token_count, rows, packed, doc_id, cu_seqlens, stream=None):

@@ -85,10 +85,12 @@ class Runner:
         self.x = torch.from_numpy(b["coords"]).to(dev)
         self.f = torch.from_numpy(b["features"]).to(dev)
         self.off = torch.from_numpy(b["offsets"]).to(dev)
+        # the batch is assembled on the host, so its largest event is known there
+        self.max_n = int(np.diff(b["offsets"]).max()) if b["offsets"].size > 1 else 0
         self.tok = F.Tokenizer(self.x, self.f, self.off, num_patches=b["P"],
                                assign_mode="knn" if b["mode"] == 1 else "voronoi", k=b["k"],
                                lloyd_iters=b["L"], pool="charge" if b["weighted"] else "mean",
-                               charge_col=b["charge_col"])
+                               charge_col=b["charge_col"], max_event_points=self.max_n)
         self.calls = ["sample"] + (["lloyd"] if b["L"] > 0 else []) + \
                      (["knn"] if b["mode"] == 1 else []) + ["pool"]
 
@@ -408,7 +410,7 @@ def main():
                    "num_patches": st["P"], "features": st["C"],
                    "assign_mode": "knn" if b["mode"] == 1 else "voronoi",
                    "lloyd_iters": b["L"], "pool": "charge" if b["weighted"] else "mean",
-                   "seed": b["seed"], "launch": mode},
+                   "seed": b["seed"], "max_event_points": r.max_n, "launch": mode},
         "events_per_s_by_launch": {m: st["B"] * args.steps / w for m, w in walls.items()},
         "step_gpu_us": step_gpu * 1e6,
         "fps_point_iters_per_s": st["point_iters"] / step_gpu,

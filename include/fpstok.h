@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define FPSTOK_ABI_VERSION 1
+#define FPSTOK_ABI_VERSION 2
 #define FPSTOK_MAX_PATCHES 1024 /* largest num_patches accepted             */
 #define FPSTOK_MAX_K 64         /* largest kNN list length accepted           */
 #define FPSTOK_MAX_LLOYD 1000   /* largest lloyd_iters accepted               */
@@ -101,6 +101,13 @@ typedef struct {
     int64_t num_points;      /* N >= 0, N < 2^31                                  */
     int32_t num_features;    /* C >= 1 for calls that read features                */
     int32_t charge_col;      /* charge column 0..C-1, or -1 for unit charge       */
+    int64_t max_event_points;/* optional host-side bound on the pulses of any     */
+                             /* event, 0 if unknown.  A bound <= 4096 lets        */
+                             /* fpstok_sample / fpstok_tokenize skip planning     */
+                             /* their work list (every event then runs on one     */
+                             /* workgroup); a bound that is too small stays       */
+                             /* correct: a larger event falls back to the slower  */
+                             /* one-workgroup streaming FPS.                      */
 } fpstok_batch;
 
 typedef struct {

@@ -167,6 +167,7 @@ static SampleArgs sample_args(const fpstok_batch* bt, const fpstok_params* pr,
     a.assign = assign;
     a.ws_mind = at<float>(ws, L.mind);
     a.ws_near = at<int32_t>(ws, L.near);
+    a.direct = bt->max_event_points > 0 && bt->max_event_points <= kFpsCapPulses ? 1 : 0;
     a.header = at<int32_t>(ws, L.header);
     a.item_ev = at<int32_t>(ws, L.item_ev);
     a.item_g = at<int32_t>(ws, L.item_g);

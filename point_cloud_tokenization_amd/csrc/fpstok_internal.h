@@ -11,6 +11,7 @@ namespace fpstok {
 
 // Pulses per chunk of the assign kernel: four threads per pulse in a
 // 256-thread workgroup.
+constexpr int kFpsCapPulses = 4096;  // pulses one FPS workgroup holds in registers
 constexpr int kChunk = 64;
 
 // Pulses per chunk of the chunked Voronoi pooling: the largest slot sort one
@@ -75,6 +76,8 @@ struct SampleArgs {
     int32_t* assign;
     float* ws_mind;
     int32_t* ws_near;
+    int direct;                     // 1: item i is event i, no work list (every event
+                                    // within one workgroup's registers, else streaming)
     int32_t* header;                // [1] items, [2] claim counter, [3] error word,
                                     // [5] gang items (0: item i is event i)
     int32_t* item_ev;               // [max_items] event of each work item

@@ -295,6 +295,7 @@ constexpr int kFpsT = 256;                 // threads per workgroup (4 waves)
 constexpr int kFpsW = kFpsT / 64;
 constexpr int kFpsM = 16;                  // register-resident pulses per thread
 constexpr int kFpsCap = kFpsT * kFpsM;     // pulses one workgroup holds in registers
+static_assert(kFpsCap == kFpsCapPulses, "host and device disagree on the register capacity");
 constexpr int kGangMax = 64;               // workgroups sharing one event at most
 constexpr uint32_t kSpinLimit = 1u << 22;  // bound on every inter-workgroup wait
 
@@ -1305,21 +1306,28 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     const int tid = threadIdx.x;
     ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0, false};
     // without gangs item i is event i: the event's range is read together
-    // with the header, and nothing is claimed
+    // with the header, and nothing is claimed; in direct mode (no work list
+    // was planned) the header is not read at all
     const int64_t bd = (int64_t)blockIdx.x < a.B ? (int64_t)blockIdx.x : a.B - 1;
     int64_t off;
     int n;
     event_range(a.offsets, a.N, bd, off, n);
-    const int nitems = a.header[1];
     int item;
     int64_t b;
     int g;
-    if (a.header[5] == 0) {
+    if (a.direct) {
+        item = (int)blockIdx.x;
+        if (item >= a.B) return it;
+        b = item;
+        g = 0;
+    } else if (a.header[5] == 0) {
+        const int nitems = a.header[1];
         item = (int)blockIdx.x;
         if (item >= nitems) return it;
         b = item;
         g = 0;
     } else {
+        const int nitems = a.header[1];
         // items are claimed in list order, so the shards of one gang go to
         // workgroups that start one after another: a gang whose workgroups
         // wait for a partner only ever waits for a workgroup that will start
@@ -1366,7 +1374,7 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
         fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg, st);
         it.kind = 1;
         it.cnt = n;
-    } else if (n <= kGangMax * kFpsCap) {
+    } else if (!a.direct && n <= kGangMax * kFpsCap) {
         const int G = (n + kFpsCap - 1) / kFpsCap;
         const int S = (n + G - 1) / G;
         const int lo = g * S;
@@ -3079,25 +3087,30 @@ static unsigned plan_fps_threads(int64_t B) {
 }
 
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(plan_fps_threads(B)), 0, s, a, B);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sample_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), 0, s, a);
+    if (!a.direct) {
+        hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(plan_fps_threads(B)), 0, s, a, B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sample_kernel, dim3(grid1(a.direct ? B : sample_max_items(B, a.N))),
+                       dim3(kFpsT), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, hipStream_t s) {
-    hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(plan_fps_threads(B)), 0, s, a, B);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!a.direct) {
+        hipLaunchKernelGGL(plan_fps_kernel, dim3(1), dim3(plan_fps_threads(B)), 0, s, a, B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // feature rows of small single-workgroup events are staged in LDS when
     // that leaves two workgroups per CU their room
     PoolArgs p = pa;
     p.stage_cap = a.P <= 512 ? kStage : 0;
     const size_t lds = sizeof(int) * ((size_t)kSortW * a.P + a.P + 1 + 2 * (size_t)kFpsCap) +
                        sizeof(float) * (size_t)p.stage_cap;
-    hipLaunchKernelGGL(tokenize_kernel, dim3(grid1(sample_max_items(B, a.N))), dim3(kFpsT), lds, s,
-                       a, p);
+    hipLaunchKernelGGL(tokenize_kernel, dim3(grid1(a.direct ? B : sample_max_items(B, a.N))),
+                       dim3(kFpsT), lds, s, a, p);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ class Batch(ctypes.Structure):
     _fields_ = [("coords", ctypes.c_void_p), ("features", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("num_events", ctypes.c_int64),
                 ("num_points", ctypes.c_int64), ("num_features", ctypes.c_int32),
-                ("charge_col", ctypes.c_int32)]
+                ("charge_col", ctypes.c_int32), ("max_event_points", ctypes.c_int64)]
 
 
 class Params(ctypes.Structure):
@@ -129,8 +129,10 @@ def _need(t, dtype, name, dev=None):
     return t
 
 
-def make_batch(coords, offsets, features=None, charge_col=-1):
-    """A Batch struct (plus the tensors it points into, kept alive)."""
+def make_batch(coords, offsets, features=None, charge_col=-1, max_event_points=0):
+    """A Batch struct (plus the tensors it points into, kept alive).
+    max_event_points: optional host-side bound on the pulses of any event (0:
+    unknown); see fpstok_batch in include/fpstok.h."""
     import torch
 
     _need(coords, torch.float32, "coords")
@@ -144,7 +146,8 @@ def make_batch(coords, offsets, features=None, charge_col=-1):
             raise ValueError("features must be [N,C]")
         C = features.shape[1]
     bt = Batch(coords.data_ptr(), features.data_ptr() if features is not None else None,
-               offsets.data_ptr(), offsets.numel() - 1, coords.shape[0], C, charge_col)
+               offsets.data_ptr(), offsets.numel() - 1, coords.shape[0], C, charge_col,
+               int(max_event_points))
     return bt
 
 
@@ -282,12 +285,12 @@ class Tokenizer:
     stream without host synchronization."""
 
     def __init__(self, coords, features, offsets, num_patches=128, assign_mode="voronoi", k=16,
-                 lloyd_iters=0, pool="charge", charge_col=-1):
+                 lloyd_iters=0, pool="charge", charge_col=-1, max_event_points=0):
         import torch
 
         self.mode = {"voronoi": VORONOI, "knn": KNN}[assign_mode]
         self.coords, self.features, self.offsets = coords, features, offsets
-        self.bt = make_batch(coords, offsets, features, charge_col)
+        self.bt = make_batch(coords, offsets, features, charge_col, max_event_points)
         self.pr = make_params(num_patches, k, lloyd_iters, self.mode,
                               1 if pool == "charge" else 0)
         dev = coords.device
@@ -306,9 +309,25 @@ class Tokenizer:
             cell_count=torch.empty((B, P), dtype=torch.int32, device=dev),
         )
         self.ws = alloc_workspace(self.bt, self.pr, dev)
+        # the call's fixed arguments, marshalled once; only the stream is
+        # looked up per call (torch's current stream on this device)
+        o = self.out
+        self._fn = lib().fpstok_tokenize
+        self._head = (ctypes.byref(self.bt), ctypes.byref(self.pr))
+        self._tail = (_ptr(o["centroid_idx"]), _ptr(o["centroids"]), _ptr(o["token_count"]),
+                      _ptr(o["assign"]), _ptr(o["knn_idx"]), _ptr(o["pooled"]),
+                      _ptr(o["cell_count"]), _ptr(self.ws), self.ws.numel())
+        self._dev = dev.index if dev.index is not None else torch.cuda.current_device()
+        self._raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
     def __call__(self, start_idx=None, stream=None):
         """fpstok_tokenize on the preallocated buffers."""
+        if stream is None and self._raw_stream is not None:
+            rc = self._fn(*self._head, _ptr(start_idx), *self._tail,
+                          ctypes.c_void_p(self._raw_stream(self._dev)))
+            if rc != OK:
+                _check(rc, "fpstok_tokenize")
+            return self.out
         o = self.out
         tokenize_call(self.bt, self.pr, o["centroid_idx"], o["centroids"], o["token_count"],
                       o["assign"], o["knn_idx"], o["pooled"], o["cell_count"], self.ws,

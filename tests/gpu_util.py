@@ -73,7 +73,8 @@ def assert_close_scaled(got, ref, scale, what):
     return float(np.mean(got == ref))
 
 
-def run_pipeline(batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5, start_idx=None):
+def run_pipeline(batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5, start_idx=None,
+                 max_event_points=0):
     """Every stage on the GPU; returns numpy arrays of each stage's output and
     the stage inputs needed to replay them on the oracle."""
     import torch
@@ -86,7 +87,7 @@ def run_pipeline(batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5, start
     B = batch["offsets"].size - 1
     N = batch["coords"].shape[0]
     C = batch["features"].shape[1]
-    bt = F.make_batch(x, off, f, charge_col)
+    bt = F.make_batch(x, off, f, charge_col, max_event_points)
     pr = F.make_params(P, k, L, mode, 1 if weighted else 0)
     ws = F.alloc_workspace(bt, pr, x.device)
     dev = x.device
@@ -120,12 +121,12 @@ def run_pipeline(batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5, start
 
 
 def check_pipeline(oracle, batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5,
-                   start_idx=None, label=""):
+                   start_idx=None, label="", max_event_points=0):
     """Run the GPU pipeline and compare every stage with the oracle fed the
     same inputs.  Returns a dict of exact-match fractions of float outputs."""
     log("parity case %s: B=%d N=%d P=%d mode=%d k=%d L=%d" % (
         label, batch["offsets"].size - 1, batch["coords"].shape[0], P, mode, k, L))
-    g = run_pipeline(batch, P, mode, k, L, weighted, charge_col, start_idx)
+    g = run_pipeline(batch, P, mode, k, L, weighted, charge_col, start_idx, max_event_points)
     x, f, off = batch["coords"], batch["features"], batch["offsets"]
     stats = {}
     sel, cen, tc, asg = oracle.sample(x, off, P, start_idx=start_idx)

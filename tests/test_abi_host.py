@@ -37,7 +37,7 @@ def test_only_the_abi_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.fpstok_version() == 1
+    assert L.fpstok_version() == 2
     assert L.fpstok_status_string(0) == b"ok"
     assert L.fpstok_status_string(2) == b"workspace too small"
     assert L.fpstok_status_string(99) == b"unknown status"

@@ -186,7 +186,7 @@ def test_graph_replay_matches_eager(oracle_mod):
 
 
 def _tokenize_vs_oracle(oracle_mod, b, P, mode=0, k=16, L=0, weighted=True, charge_col=5,
-                        stepwise=False, label=""):
+                        stepwise=False, label="", max_event_points=0):
     """fpstok_tokenize (or the five calls) against oracle.tokenize."""
     from point_cloud_tokenization_amd import fpstok as F
     from tests.gpu_util import assert_close_scaled, member_scale
@@ -195,7 +195,8 @@ def _tokenize_vs_oracle(oracle_mod, b, P, mode=0, k=16, L=0, weighted=True, char
         label, b["offsets"].size - 1, b["coords"].shape[0], P, mode, L, stepwise))
     x, f, off = to_dev(b["coords"]), to_dev(b["features"]), to_dev(b["offsets"])
     tok = F.Tokenizer(x, f, off, num_patches=P, assign_mode="knn" if mode else "voronoi", k=k,
-                      lloyd_iters=L, pool="charge" if weighted else "mean", charge_col=charge_col)
+                      lloyd_iters=L, pool="charge" if weighted else "mean", charge_col=charge_col,
+                      max_event_points=max_event_points)
     out = tok.stepwise() if stepwise else tok()
     got = {key: to_np(v) for key, v in out.items() if v is not None}
     ref = oracle_mod.tokenize(b["coords"], b["features"], b["offsets"], P=P, mode=mode, k=k, L=L,
@@ -269,3 +270,24 @@ def test_tokenize_fused_edges(oracle_mod):
     _tokenize_vs_oracle(oracle_mod, b, 32, label="fused streaming")
     b = synth.icecube_events([800, 12000, 90], 26, C=6)
     _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=16, L=1, stepwise=True, label="stepwise")
+
+
+def test_max_event_points_hint(oracle_mod):
+    """The work-list-free path: a correct bound (every event within one
+    workgroup) and a bound that is too small (events above 4096 pulses fall
+    back to the one-workgroup streaming FPS), fused and stepwise."""
+    for name in ("icecube_b64_voronoi", "tiny_uniform", "icecube_b256_lloyd3"):
+        w = synth.WORKLOADS[name]
+        b = synth.make_batch(name, synth.parity_seed(name, 2))
+        m = int(np.diff(b["offsets"]).max())
+        _tokenize_vs_oracle(oracle_mod, b, w["P"], w["mode"], w["k"], w["L"], w["weighted"], 5,
+                            label=name + " hint", max_event_points=m)
+        check_pipeline(oracle_mod, b, P=w["P"], mode=w["mode"], k=w["k"], L=w["L"],
+                       label=name + " hint stepwise", max_event_points=m)
+    b = synth.icecube_events([0, 3, 129, 700, 4096, 4097, 9000, 50], 27, C=6)
+    _tokenize_vs_oracle(oracle_mod, b, 128, label="hint too small", max_event_points=100)
+    _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=16, L=1, stepwise=True,
+                        label="hint too small stepwise", max_event_points=100)
+    check_pipeline(oracle_mod, b, P=128, L=2, label="hint too small sample", max_event_points=5)
+    _tokenize_vs_oracle(oracle_mod, b, 128, label="hint above one workgroup",
+                        max_event_points=9000)

@@ -333,6 +333,7 @@ __device__ __forceinline__ void write_selection(const SampleArgs& a, int64_t b,
 
 // ------------------------------------ single-workgroup FPS, candidate list
 
+constexpr int kBmW4 = 8;  // 128-bit words per bitmap row: events of up to 1024 pulses
 constexpr int kStage = 6144;              // feature floats an event may stage in LDS
 constexpr int kStageR = kStage / kFpsT;   // staged floats per thread
 
@@ -346,6 +347,7 @@ struct Stage {
     int nf;            // floats to copy (n * C), at most kStage - C
     int nz;            // floats written: nf + C (the zero row), 0 when none
     float* dst;        // LDS, kStage floats
+    int defer_sel;     // 1: the caller writes the selection (centroid_idx, centroids)
 };
 
 constexpr int kListCap = 64;  // entries of the candidate list (one per lane)
@@ -640,7 +642,7 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             st.dst[q] = q < st.nf ? fr[r] : 0.0f;
         }
     }
-    write_selection(a, b, p, s_sel);
+    if (!st.defer_sel) write_selection(a, b, p, s_sel);
 }
 
 __device__ __forceinline__ void fps_single_dispatch(const SampleArgs& a, int64_t b, int64_t off,
@@ -1293,6 +1295,7 @@ struct ItemInfo {
     int item0;    // work item of shard 0 (gangs)
     int par;      // gang record parity no shard reads any more (gangs)
     bool staged;  // the event's feature rows were staged in LDS (single workgroup)
+    bool deferred;  // the selection is left to the caller (staged, bitmap-sortable)
 };
 
 // Claim one work item and run FPS (or pass-through) for it.  s_asg, when not
@@ -1304,7 +1307,7 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
                                                 int* s_sel, int* s_asg, const float* feats, int C,
                                                 int stage_cap, float* s_feat) {
     const int tid = threadIdx.x;
-    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0, false};
+    ItemInfo it{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0, false, false};
     // without gangs item i is event i: the event's range is read together
     // with the header, and nothing is claimed; in direct mode (no work list
     // was planned) the header is not read at all
@@ -1369,8 +1372,12 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     if (s0 < 0 || s0 >= n) s0 = 0;
     if (n <= kFpsCap) {
         it.staged = feats != nullptr && (int64_t)(n + 1) * C <= stage_cap;
+        // a staged event that the fused tail sorts through bitmaps writes its
+        // selection there, after the pooling (the coordinates' loads then
+        // overlap the sort)
+        it.deferred = it.staged && n <= kBmW4 * 128 && P * ((n + 127) >> 7) <= kFpsCap / 4;
         const Stage st{it.staged ? feats + off * C : nullptr, it.staged ? n * C : 0,
-                       it.staged ? (n + 1) * C : 0, s_feat};
+                       it.staged ? (n + 1) * C : 0, s_feat, it.deferred ? 1 : 0};
         fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg, st);
         it.kind = 1;
         it.cnt = n;
@@ -1756,8 +1763,6 @@ __device__ __forceinline__ bool block_sort_small(int* asg, int n, int T, int* tm
     __syncthreads();
     return true;
 }
-
-constexpr int kBmW4 = 8;  // 128-bit words per bitmap row: events of up to 1024 pulses
 
 // Stable sort of a small event's pulses by slot through per-slot bitmaps
 // (bit i of row k: pulse i has slot k).  A pulse's rank among its slot's
@@ -2603,17 +2608,25 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         return;
     }
     lds_barrier();
-    if (it.kind == 1 && it.staged) {
-        // small event, rows in LDS: bitmap sort into s_asg[1024 ..), pooling
-        // from LDS (s_asg holds at most 1024 slots here)
-        const int W4 = (it.n + 127) >> 7;
-        if (it.n <= kBmW4 * 128 && P * W4 <= kFpsCap / 4) {
-            int* perm = s_asg + kBmW4 * 128;
-            block_sort_bitmap(s_asg, it.n, P, reinterpret_cast<uint32_t*>(s_perm),
-                              s_asg + 2 * kBmW4 * 128, s_off, perm);
-            pool_slots_lds(pa, b, it.n, perm, s_off, s_feat);
-            return;
-        }
+    if (it.kind == 1 && it.deferred) {
+        // small event, rows in LDS: the selection's indices now and its
+        // coordinates' loads in flight across the sort and pooling (whose
+        // barriers order LDS only); bitmap sort into s_asg[1024 ..), pooling
+        // from LDS (s_asg holds at most 1024 slots here; P <= 512)
+        const int j0 = tid, j1 = tid + kFpsT;
+        const int s0 = j0 < P ? s_sel[j0] : 0;
+        const int s1 = j1 < P ? s_sel[j1] : 0;
+        if (j0 < P) a.centroid_idx[b * P + j0] = s0;
+        if (j1 < P) a.centroid_idx[b * P + j1] = s1;
+        const float4 c0 = a.coords[off + s0];
+        const float4 c1 = a.coords[off + s1];
+        int* perm = s_asg + kBmW4 * 128;
+        block_sort_bitmap(s_asg, it.n, P, reinterpret_cast<uint32_t*>(s_perm),
+                          s_asg + 2 * kBmW4 * 128, s_off, perm);
+        pool_slots_lds(pa, b, it.n, perm, s_off, s_feat);
+        if (j0 < P) a.centroids[b * P + j0] = c0;
+        if (j1 < P) a.centroids[b * P + j1] = c1;
+        return;
     }
     // the shard's pulses sorted by slot: in s_asg itself when every slot is
     // small, else in s_perm

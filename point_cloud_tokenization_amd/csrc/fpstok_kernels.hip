@@ -3153,9 +3153,6 @@ static size_t pool_lds_bytes(int P, int C, int sub) {
 
 hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s) {
     if (a.P <= kPoolLdsMaxP) {
-        // the largest piece (at most 1024 pulses, a multiple of 128) whose
-        // rows the threads can hold in registers and whose LDS leaves room
-        // for two workgroups per CU
         // 1024-pulse pieces, when the threads can hold a piece's rows in
         // registers and two workgroups per CU fit in LDS; otherwise (wide
         // rows) gathering members from device memory is faster

@@ -203,7 +203,13 @@ static PoolArgs pool_args(const fpstok_batch* bt, const fpstok_params* pr,
     a.big_ev = at<int32_t>(ws, L.big_ev);
     a.B = bt->num_events;
     // the combine kernel's blocks hold one thread per (field, slot)
-    a.comb_last = bt->num_features + 2 <= 256 ? kCombLast : (1 << 30);
+    // events of more than kCombLast chunks are finished by the combine
+    // kernel; when the caller's bound on event size rules them out, the
+    // last chunk of every event finishes it (still correct if the bound is
+    // wrong) and the combine kernel is not launched
+    const bool no_big = bt->max_event_points > 0 &&
+                        bt->max_event_points <= (int64_t)kCombLast * kPoolChunk;
+    a.comb_last = bt->num_features + 2 <= 256 && !no_big ? kCombLast : (1 << 30);
     a.part = at<double>(ws, L.part);
     return a;
 }

@@ -1269,7 +1269,7 @@ __global__ __launch_bounds__(1024) void plan_all_kernel(SampleArgs a, int64_t B,
                                                         int64_t max_chunks, PoolArgs pa,
                                                         int64_t max_pool_chunks,
                                                         int64_t max_parts, int chunks, int pool) {
-    plan_fps(a, B);
+    if (!a.direct) plan_fps(a, B);  // no work list in direct mode
     if (chunks) {
         __syncthreads();
         plan_chunks(a.offsets, B, a.N, max_chunks, a.header, chunk_ev, chunk_beg);

@@ -291,3 +291,10 @@ def test_max_event_points_hint(oracle_mod):
     check_pipeline(oracle_mod, b, P=128, L=2, label="hint too small sample", max_event_points=5)
     _tokenize_vs_oracle(oracle_mod, b, 128, label="hint above one workgroup",
                         max_event_points=9000)
+    # a bound that rules out events of more than four pooling chunks: the last
+    # chunk of every event finishes it, also for an event of ten chunks when
+    # the bound is wrong
+    b = synth.icecube_events([40000, 300, 5000], 28, C=6)
+    check_pipeline(oracle_mod, b, P=128, label="hint too small, 10-chunk event",
+                   max_event_points=100)
+    check_pipeline(oracle_mod, b, P=256, weighted=False, label="hint 16384", max_event_points=16384)

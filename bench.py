@@ -45,8 +45,8 @@ FPS_OPS_PER_POINT_ITER = 14
 # source it was taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "e6e93576c9e3d8ed019c31a2b37250dba88e20457f5eb6ff68d9b649de8f48fc",
-    "bytes": int(round((2 * 397.9 + 419.3) * 1024)),
+    "kernels_sha256": "94e807ddaf3dc17cec9a547c91ba4ff29dc7a2a4a10bedeba00981cfd8590297",
+    "bytes": int(round((2 * 382.8 + 419.3) * 1024)),
 }
 
 

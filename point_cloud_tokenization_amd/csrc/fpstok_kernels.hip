@@ -467,7 +467,7 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
         int wm;
         for (;;) {
             selv = lane == (j & 63) ? s : selv;
-            if ((j & 63) == 63 && wave == 0) s_sel[j - 63 + lane] = selv;
+            if (__builtin_expect((j & 63) == 63 && wave == 0, 0)) s_sel[j - 63 + lane] = selv;
             {
                 const float d = sqd(lx, ly, lz, lt, cx, cy, cz, ct);
                 lv = d < lv ? d : lv;
@@ -489,7 +489,7 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             cy = readlane_f(ly, Lw);
             cz = readlane_f(lz, Lw);
             ct = readlane_f(lt, Lw);
-            if (j + 1 == P || wm <= U) break;
+            if (__builtin_expect(j + 1 == P || wm <= U, 0)) break;
             ++j;
         }
         if (j + 1 == P) break;

@@ -776,7 +776,7 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
     for (;;) {
         for (;;) {
             selv = lane == (j & 63) ? s : selv;
-            if ((j & 63) == 63 && wave == 0) s_sel[j - 63 + lane] = selv;
+            if (__builtin_expect((j & 63) == 63 && wave == 0, 0)) s_sel[j - 63 + lane] = selv;
             int lb = INT32_MIN, le = 0;
 #pragma unroll
             for (int e = 0; e < kGangE; ++e) {
@@ -797,7 +797,7 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
                 nr[k] = u ? j : nr[k];
                 md[k] = u ? d : md[k];
             }
-            if (j + 1 == P || wm <= U) break;
+            if (__builtin_expect(j + 1 == P || wm <= U, 0)) break;
             const uint64_t m = ballot(lb == wm);
             int Lw, ew;
             if (__popcll(m) == 1) {

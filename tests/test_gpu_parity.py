@@ -153,13 +153,16 @@ def test_graph_replay_matches_eager(oracle_mod):
 
     from point_cloud_tokenization_amd import fpstok as F
 
-    for name in ("icecube_b64_voronoi", "icecube_b64_knn16", "icecube_b256_lloyd3"):
+    cases = [(name, hint) for name in ("icecube_b64_voronoi", "icecube_b64_knn16",
+                                       "icecube_b256_lloyd3") for hint in (False, True)]
+    for name, hint in cases:
         b = synth.make_batch(name, 77)
         w = synth.WORKLOADS[name]
         x, f, off = to_dev(b["coords"]), to_dev(b["features"]), to_dev(b["offsets"])
         tok = F.Tokenizer(x, f, off, num_patches=w["P"],
                           assign_mode="knn" if w["mode"] == 1 else "voronoi", k=w["k"],
-                          lloyd_iters=w["L"], pool="charge", charge_col=5)
+                          lloyd_iters=w["L"], pool="charge", charge_col=5,
+                          max_event_points=int(np.diff(b["offsets"]).max()) if hint else 0)
         ref = {k_: (to_np(v) if v is not None else None) for k_, v in tok().items()}
         torch.cuda.synchronize()
         s = torch.cuda.Stream()
@@ -181,8 +184,8 @@ def test_graph_replay_matches_eager(oracle_mod):
             float(scratch)
             for k_, v in tok.out.items():
                 if v is not None:
-                    assert np.array_equal(to_np(v), ref[k_]), (name, rep, k_)
-        log("graph replay ok: %s" % name)
+                    assert np.array_equal(to_np(v), ref[k_]), (name, hint, rep, k_)
+        log("graph replay ok: %s hint=%s" % (name, hint))
 
 
 def _tokenize_vs_oracle(oracle_mod, b, P, mode=0, k=16, L=0, weighted=True, charge_col=5,

@@ -735,6 +735,7 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
     const float4* __restrict__ p = a.coords + off;
     const int lbase = sh.lo + tid * M;  // event-local index of this lane's first pulse
     const int send = sh.lo + sh.cnt;
+    __builtin_amdgcn_s_setprio(2);
 
     float px[M], py[M], pz[M], pt[M], md[M];
     int nr[M];
@@ -1078,6 +1079,7 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
             if (i < send) s_asg[i - sh.lo] = nr[k];
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (sh.g == 0) write_selection(a, b, p, s_sel);
     return ex;
 }

@@ -933,31 +933,35 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
         // thread t reads record entries F = t + 256q (shard F/64, slot
         // F%64); threads t < G also the best pulse and the bound of shard t
         const int nF = G * kRecSlots;
+        const int nq = (nF + kFpsT - 1) / kFpsT;  // read rounds in use (uniform)
         const char* rbase = reinterpret_cast<const char*>(rec0);
         unsigned long long vw[kGangQ];
         unsigned long long bw0 = 0, bw1 = 0;
         {
             const uint32_t so = (uint32_t)(tid < G ? tid : 0) * 2u * kGangRecWords * 8u;
             for (uint32_t spin = 0;; ++spin) {
-                bool ok = true;
+                // every load of a spin is issued before any is tested, so a
+                // spin costs one round trip: no load sits in a divergent
+                // branch (lanes past the records re-read the last entry, and
+                // threads t >= G the words of shard 0)
                 // an opaque zero keeps the offsets from being hoisted out of
                 // the wait loop (they are cheap; registers are not)
                 int z;
                 asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
                 for (int q = 0; q < kGangQ; ++q) {
-                    const int F = tid + kFpsT * q + z;
-                    if (F < nF) {
+                    if (q < nq) {
+                        const int F = min(tid + kFpsT * q + z, nF - 1);
                         const uint32_t o = ((uint32_t)(F >> 6) * 2u * kGangRecWords + (uint32_t)(F & 63)) * 8u;
                         vw[q] = rec_load(reinterpret_cast<const unsigned long long*>(rbase + o));
-                        ok = ok && rec_ok(vw[q], tag);
                     }
                 }
-                if (tid < G) {
-                    bw0 = rec_load(reinterpret_cast<const unsigned long long*>(rbase + so + (kRecSlots - 1) * 8u));
-                    bw1 = rec_load(reinterpret_cast<const unsigned long long*>(rbase + so + kRecBound * 8u));
-                    ok = ok && rec_ok(bw0, tag) && rec_ok(bw1, tag);
-                }
+                bw0 = rec_load(reinterpret_cast<const unsigned long long*>(rbase + so + (kRecSlots - 1) * 8u));
+                bw1 = rec_load(reinterpret_cast<const unsigned long long*>(rbase + so + kRecBound * 8u));
+                bool ok = rec_ok(bw0, tag) && rec_ok(bw1, tag);
+#pragma unroll
+                for (int q = 0; q < kGangQ; ++q)
+                    if (q < nq) ok = ok && rec_ok(vw[q], tag);
                 if (__syncthreads_and(ok)) break;
                 if (spin >= kSpinLimit) {
                     if (tid == 0)
@@ -990,7 +994,7 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
 #pragma unroll
         for (int q = 0; q < kGangQ; ++q) {
             const int F = tid + kFpsT * q;
-            const bool kq = F < nF && rec_val(vw[q]) > Ug;
+            const bool kq = q < nq && F < nF && rec_val(vw[q]) > Ug;
             const uint64_t kb = ballot(kq);
             if (lane == 0) L.gcnt[q * kFpsW + wave] = __popcll(kb);
         }
@@ -1006,14 +1010,12 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
 #pragma unroll
         for (int q = 0; q < kGangQ; ++q) {
             const int F = tid + kFpsT * q;
-            const bool kq = F < nF && rec_val(vw[q]) > Ug;
+            const bool kq = q < nq && F < nF && rec_val(vw[q]) > Ug;
             const int gpos = readlane_i(excl_l, q * kFpsW + wave) + mbcnt(ballot(kq));
             if (kq && gpos < kGangCap) {
-                const int gi = min(rec_idx(vw[q]), n - 1);
                 FpsSlot& o = L.glist[gpos];
                 o.v = __int_as_float(rec_val(vw[q]));
-                o.i = gi;
-                o.c = p[gi];
+                o.i = min(rec_idx(vw[q]), n - 1);
             }
             dropped = kq && gpos >= kGangCap ? max(dropped, rec_val(vw[q])) : dropped;
         }
@@ -1045,19 +1047,24 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
         const int Cl = min(Cg, kGangCap);
         nreg = __builtin_amdgcn_readfirstlane((Cl + 63) >> 6);
         U = __builtin_amdgcn_readfirstlane(Ug);
+        // the entries' coordinates come from the input, one gather per list
+        // register, all in flight together (entries past the list read pulse
+        // 0 and stay unused)
 #pragma unroll
         for (int e = 0; e < kGangE; ++e) {
             const int f = e * 64 + lane;
-            if (f < Cl) {
-                const FpsSlot o = L.glist[f];
-                lv[e] = o.v;
-                li[e] = o.i;
-                lx[e] = o.c.x;
-                ly[e] = o.c.y;
-                lz[e] = o.c.z;
-                lt[e] = o.c.w;
-            } else {
-                lv[e] = -1.0f;
+            const bool has = f < Cl;
+            li[e] = has ? L.glist[f].i : 0;
+            lv[e] = has ? L.glist[f].v : -1.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kGangE; ++e) {
+            if (e < nreg) {
+                const float4 q = p[li[e]];
+                lx[e] = q.x;
+                ly[e] = q.y;
+                lz[e] = q.z;
+                lt[e] = q.w;
             }
         }
         ++ex;

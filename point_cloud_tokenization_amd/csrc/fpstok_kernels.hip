@@ -1048,8 +1048,8 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
         nreg = __builtin_amdgcn_readfirstlane((Cl + 63) >> 6);
         U = __builtin_amdgcn_readfirstlane(Ug);
         // the entries' coordinates come from the input, one gather per list
-        // register, all in flight together (entries past the list read pulse
-        // 0 and stay unused)
+        // register, all in flight together: no gather sits behind a branch
+        // (entries past the list read pulse 0 and stay unused)
 #pragma unroll
         for (int e = 0; e < kGangE; ++e) {
             const int f = e * 64 + lane;
@@ -1059,13 +1059,11 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
         }
 #pragma unroll
         for (int e = 0; e < kGangE; ++e) {
-            if (e < nreg) {
-                const float4 q = p[li[e]];
-                lx[e] = q.x;
-                ly[e] = q.y;
-                lz[e] = q.z;
-                lt[e] = q.w;
-            }
+            const float4 q = p[li[e]];
+            lx[e] = q.x;
+            ly[e] = q.y;
+            lz[e] = q.z;
+            lt[e] = q.w;
         }
         ++ex;
         ++j;
@@ -1311,6 +1309,7 @@ struct ItemInfo {
 // null, receives the shard's Voronoi slots (register-resident paths only).
 // With `feats` given, a single-workgroup event of at most stage_cap feature
 // floats also gets its C-column feature rows copied to s_feat.
+template <bool kDirect>
 __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item,
                                                 FpsSlot (*s_slots)[kFpsW], GangLds& s_gang,
                                                 int* s_sel, int* s_asg, const float* feats, int C,
@@ -1327,7 +1326,7 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
     int item;
     int64_t b;
     int g;
-    if (a.direct) {
+    if (kDirect || a.direct) {
         item = (int)blockIdx.x;
         if (item >= a.B) return it;
         b = item;
@@ -1390,7 +1389,7 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
         fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg, st);
         it.kind = 1;
         it.cnt = n;
-    } else if (!a.direct && n <= kGangMax * kFpsCap) {
+    } else if (!kDirect && !a.direct && n <= kGangMax * kFpsCap) {
         const int G = (n + kFpsCap - 1) / kFpsCap;
         const int S = (n + G - 1) / G;
         const int lo = g * S;
@@ -1415,7 +1414,7 @@ __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
     __shared__ GangLds s_gang;
-    sample_item(a, &s_item, s_slots, s_gang, s_sel, nullptr, nullptr, 0, 0, nullptr);
+    sample_item<false>(a, &s_item, s_slots, s_gang, s_sel, nullptr, nullptr, 0, 0, nullptr);
 }
 
 // ------------------------------------------------------------------- assign
@@ -2071,10 +2070,19 @@ __device__ __forceinline__ void pool_identity(const PoolArgs& a, int64_t b, int6
     for (int j = threadIdx.x; j < a.P; j += blockDim.x) {
         if (j < T) {
             const float* __restrict__ row = a.features + (off + j) * (int64_t)C;
+            float* __restrict__ out = a.pooled + (b * a.P + j) * (int64_t)C;
             const double w = a.weight_col >= 0 ? (double)row[a.weight_col] : 1.0;
-            for (int c = 0; c < C; ++c)
-                a.pooled[(b * a.P + j) * (int64_t)C + c] =
-                    w != 0.0 ? (float)((w * (double)row[c]) / w) : 0.0f;
+            // a group of columns is loaded whole before any is written, so
+            // the loads overlap
+            constexpr int U = 8;
+            for (int c0 = 0; c0 < C; c0 += U) {
+                float f[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) f[u] = row[min(c0 + u, C - 1)];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (c0 + u < C) out[c0 + u] = w != 0.0 ? (float)((w * (double)f[u]) / w) : 0.0f;
+            }
         } else {
             for (int c = 0; c < C; ++c) a.pooled[(b * a.P + j) * (int64_t)C + c] = 0.0f;
         }
@@ -2583,6 +2591,11 @@ __device__ __forceinline__ void pool_slots_lds(const PoolArgs& a, int64_t b, int
 //  * streaming (beyond gang size): a workgroup-wide sort in device memory.
 // Dynamic LDS: s_perm[kFpsCap] (during FPS: the FpsLds of a single-workgroup
 // event), s_asg[kFpsCap], s_cnt[kSortW*P], s_off[P+1].
+//
+// Two instantiations: kDirect (every workgroup takes the event of its own
+// index; no gang code at all, so the common small-event kernel's code and
+// registers do not depend on the gang path) and the work-list kernel.
+template <bool kDirect>
 __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs pa) {
     __shared__ int s_item;
     __shared__ FpsSlot s_slots[2][kFpsW];
@@ -2599,8 +2612,8 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
     int* s_off = s_cnt + kSortW * P;
     GangLds& s_gang = *reinterpret_cast<GangLds*>(s_perm);
     float* s_feat = reinterpret_cast<float*>(s_off + P + 1);
-    const ItemInfo it = sample_item(a, &s_item, s_slots, s_gang, s_sel, s_asg, pa.features, pa.C,
-                                    pa.stage_cap, s_feat);
+    const ItemInfo it = sample_item<kDirect>(a, &s_item, s_slots, s_gang, s_sel, s_asg, pa.features,
+                                             pa.C, pa.stage_cap, s_feat);
     if (it.b < 0) return;
     const int64_t b = it.b;
     const int64_t off = it.off;
@@ -2644,7 +2657,7 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         block_sort_by_token(s_asg, it.cnt, P, s_perm, s_cnt, s_off);
         sorted = s_perm;
     }
-    if (it.kind == 1) {
+    if (kDirect || it.kind == 1) {
         pool_slots_sorted(pa, b, off, P, sorted, s_off);
         return;
     }
@@ -3131,8 +3144,11 @@ hipError_t launch_tokenize(const SampleArgs& a, const PoolArgs& pa, int64_t B, h
     p.stage_cap = a.P <= 512 ? kStage : 0;
     const size_t lds = sizeof(int) * ((size_t)kSortW * a.P + a.P + 1 + 2 * (size_t)kFpsCap) +
                        sizeof(float) * (size_t)p.stage_cap;
-    hipLaunchKernelGGL(tokenize_kernel, dim3(grid1(a.direct ? B : sample_max_items(B, a.N))),
-                       dim3(kFpsT), lds, s, a, p);
+    if (a.direct)
+        hipLaunchKernelGGL(tokenize_kernel<true>, dim3(grid1(B)), dim3(kFpsT), lds, s, a, p);
+    else
+        hipLaunchKernelGGL(tokenize_kernel<false>, dim3(grid1(sample_max_items(B, a.N))),
+                           dim3(kFpsT), lds, s, a, p);
     return hipGetLastError();
 }
 

@@ -2844,8 +2844,42 @@ __device__ __forceinline__ double bwd_token(const float* __restrict__ g,
     return acc;
 }
 
+// The same with the member's row in registers (C <= kPoolCols): identical
+// float64 operations in the same order.
+__device__ __forceinline__ double bwd_token_r(const float* __restrict__ g,
+                                             const float* __restrict__ m,
+                                             const float (&fr)[kPoolCols], int C, int wcol,
+                                             double W, double wi, int c, double acc) {
+    acc = acc + (double)g[c] * wi / W;
+    if (c == wcol) {
+        // the token's two rows loaded whole before the sum
+        float gr[kPoolCols], mr[kPoolCols];
+#pragma unroll
+        for (int c2 = 0; c2 < kPoolCols; ++c2) {
+            gr[c2] = g[min(c2, C - 1)];
+            mr[c2] = m[min(c2, C - 1)];
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int c2 = 0; c2 < kPoolCols; ++c2)
+            if (c2 < C) s = s + (double)gr[c2] * ((double)fr[c2] - (double)mr[c2]);
+        acc = acc + s / W;
+    }
+    return acc;
+}
+
+// A member's feature row in registers, every load issued together.
+__device__ __forceinline__ void bwd_row(const float* __restrict__ f, int C, float (&fr)[kPoolCols]) {
+#pragma unroll
+    for (int c = 0; c < kPoolCols; ++c) fr[c] = f[min(c, C - 1)];
+}
+
+// The member's weight (1 without a weight column).  The load is issued
+// either way (column 0 then), so a batch of them is not serialised behind
+// the test.
 __device__ __forceinline__ double bwd_weight(const PoolBwdArgs& a, int64_t row) {
-    return a.wcol >= 0 ? (double)a.features[row * a.C + a.wcol] : 1.0;
+    const float v = a.features[row * a.C + (a.wcol >= 0 ? a.wcol : 0)];
+    return a.wcol >= 0 ? (double)v : 1.0;
 }
 
 // Voronoi: each pulse's one token.  G, M: the event's token rows [T][C].
@@ -2862,10 +2896,19 @@ __device__ __forceinline__ void bwd_pulses_voronoi(const PoolBwdArgs& a, int64_t
         const float* __restrict__ f = a.features + (off + i) * C;
         const int jj = in ? j : 0;
         float* __restrict__ out = a.grad + (off + i) * C;
-        for (int c = 0; c < C; ++c)
-            out[c] = (float)(in ? bwd_token(G + (int64_t)jj * C, M + (int64_t)jj * C, f, C,
-                                            a.wcol, W, wi, c, 0.0)
-                                : 0.0);
+        if (C <= kPoolCols) {
+            float fr[kPoolCols];
+            bwd_row(f, C, fr);
+            for (int c = 0; c < C; ++c)
+                out[c] = (float)(in ? bwd_token_r(G + (int64_t)jj * C, M + (int64_t)jj * C, fr, C,
+                                                  a.wcol, W, wi, c, 0.0)
+                                    : 0.0);
+        } else {
+            for (int c = 0; c < C; ++c)
+                out[c] = (float)(in ? bwd_token(G + (int64_t)jj * C, M + (int64_t)jj * C, f, C,
+                                                a.wcol, W, wi, c, 0.0)
+                                    : 0.0);
+        }
     }
 }
 
@@ -2885,6 +2928,26 @@ __device__ __forceinline__ void bwd_pulses_knn(const PoolBwdArgs& a, int64_t off
         uint32_t tw[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) tw[w] = bits && w < PW ? bits[i * PW + w] : 0u;
+        if (bits && PW <= 4 && C <= kPoolCols) {
+            float fr[kPoolCols];
+            bwd_row(f, C, fr);
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t bw = tw[w];
+                    while (bw) {
+                        const int j = (w << 5) + (int)__builtin_ctz(bw);
+                        bw &= bw - 1u;
+                        if (s_W[j] != 0.0)
+                            acc = bwd_token_r(G + (int64_t)j * C, M + (int64_t)j * C, fr, C,
+                                              a.wcol, s_W[j], wi, c, acc);
+                    }
+                }
+                out[c] = (float)acc;
+            }
+            continue;
+        }
         for (int c = 0; c < C; ++c) {
             double acc = 0.0;
             if (bits && PW <= 4) {
@@ -2964,8 +3027,11 @@ __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
                 for (int m0 = s_off[j]; m0 < e; m0 += kBatch) {
                     double wv[kBatch];
 #pragma unroll
-                    for (int q = 0; q < kBatch; ++q)
-                        wv[q] = m0 + q < e ? bwd_weight(a, off + perm[m0 + q]) : 0.0;
+                    for (int q = 0; q < kBatch; ++q) {
+                        // past the slot: member e-1 re-read, its weight unused
+                        const double v = bwd_weight(a, off + perm[min(m0 + q, e - 1)]);
+                        wv[q] = m0 + q < e ? v : 0.0;
+                    }
 #pragma unroll
                     for (int q = 0; q < kBatch; ++q) W = W + wv[q];
                 }
@@ -2985,8 +3051,12 @@ __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
                 for (int q = 0; q < kBatch; ++q) iv[q] = e0 + q < k ? lists[(int64_t)j * k + e0 + q] : -1;
                 double wv[kBatch];
 #pragma unroll
-                for (int q = 0; q < kBatch; ++q)
-                    wv[q] = iv[q] >= 0 && iv[q] < n ? bwd_weight(a, off + iv[q]) : 0.0;
+                for (int q = 0; q < kBatch; ++q) {
+                    // a missing entry reads row 0, its weight unused
+                    const bool ok = iv[q] >= 0 && iv[q] < n;
+                    const double v = bwd_weight(a, off + (ok ? iv[q] : 0));
+                    wv[q] = ok ? v : 0.0;
+                }
 #pragma unroll
                 for (int q = 0; q < kBatch; ++q) W = W + wv[q];
                 if (use_bits) {

@@ -2929,23 +2929,47 @@ __device__ __forceinline__ void bwd_pulses_knn(const PoolBwdArgs& a, int64_t off
 #pragma unroll
         for (int w = 0; w < 4; ++w) tw[w] = bits && w < PW ? bits[i * PW + w] : 0u;
         if (bits && PW <= 4 && C <= kPoolCols) {
+            // narrow rows: tokens outer, columns inner, one float64 sum per
+            // column in registers (each column's additions keep ascending
+            // token order); each token's rows are read once
             float fr[kPoolCols];
             bwd_row(f, C, fr);
-            for (int c = 0; c < C; ++c) {
-                double acc = 0.0;
+            double acc[kPoolCols];
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t bw = tw[w];
-                    while (bw) {
-                        const int j = (w << 5) + (int)__builtin_ctz(bw);
-                        bw &= bw - 1u;
-                        if (s_W[j] != 0.0)
-                            acc = bwd_token_r(G + (int64_t)j * C, M + (int64_t)j * C, fr, C,
-                                              a.wcol, s_W[j], wi, c, acc);
+            for (int c = 0; c < kPoolCols; ++c) acc[c] = 0.0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t bw = tw[w];
+                while (bw) {
+                    const int j = (w << 5) + (int)__builtin_ctz(bw);
+                    bw &= bw - 1u;
+                    const double W = s_W[j];
+                    if (W == 0.0) continue;
+                    const float* __restrict__ g = G + (int64_t)j * C;
+                    const float* __restrict__ m = M + (int64_t)j * C;
+                    float gr[kPoolCols], mr[kPoolCols];
+#pragma unroll
+                    for (int c = 0; c < kPoolCols; ++c) {
+                        gr[c] = g[min(c, C - 1)];
+                        mr[c] = m[min(c, C - 1)];
+                    }
+#pragma unroll
+                    for (int c = 0; c < kPoolCols; ++c)
+                        if (c < C) acc[c] = acc[c] + (double)gr[c] * wi / W;
+                    if (a.wcol >= 0) {
+                        double sw = 0.0;
+#pragma unroll
+                        for (int c = 0; c < kPoolCols; ++c)
+                            if (c < C) sw = sw + (double)gr[c] * ((double)fr[c] - (double)mr[c]);
+#pragma unroll
+                        for (int c = 0; c < kPoolCols; ++c)
+                            if (c == a.wcol) acc[c] = acc[c] + sw / W;
                     }
                 }
-                out[c] = (float)acc;
             }
+#pragma unroll
+            for (int c = 0; c < kPoolCols; ++c)
+                if (c < C) out[c] = (float)acc[c];
             continue;
         }
         for (int c = 0; c < C; ++c) {

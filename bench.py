@@ -37,16 +37,17 @@ VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12
 # (the float32 squared distance), 1 running-min update, 1 fused Voronoi
 # select, 1 argmax compare
 FPS_OPS_PER_POINT_ITER = 14
-# HBM bytes of one fpstok_tokenize call on the headline workload
-# (plan_fps_kernel + tokenize_kernel), from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE per dispatch, each scaled by its reading for a plain
+# HBM bytes of one fpstok_tokenize call on the headline workload (one
+# launch of tokenize_kernel<true>, the direct kernel: the batch's bound on
+# event size is under one workgroup's registers), from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE per dispatch, each scaled by its reading for a plain
 # device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
-# 2 * (439.9 + 4.0) KiB, writes 418.6 + 0.5 KiB.  Valid only for the kernel
-# source it was taken on; reported as null for any other.
+# 2 * 378.6 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
+# taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "bb9e506367f127a3104620dafb7c5e6e191067d8fd4ad9f71a570a0723fc043a",
-    "bytes": int(round((2 * 388.3 + 419.3) * 1024)),
+    "kernels_sha256": "4707718c2eb127913e8f0b3e35e2d08fc4bddcfde4881a994724703a37ad1b9a",
+    "bytes": int(round((2 * 378.6 + 419.3) * 1024)),
 }
 
 
@@ -354,12 +355,16 @@ def main():
     value = st["B"] * args.steps / wall
     per_call = r.per_call(max(10, args.steps // 4))
     fused = b["mode"] == 0 and b["L"] == 0
-    # the dominant kernel of the step: the fused FPS + pooling kernel (one
-    # call = the work-list kernel + tokenize_kernel) in Voronoi mode without
-    # Lloyd, else fpstok_sample
+    b_direct = 0 < st["max_n"] <= 4096
+    # the dominant kernel of the step: the fused FPS + pooling kernel in
+    # Voronoi mode without Lloyd (one launch of tokenize_kernel<true> when the
+    # batch's bound on event size fits one workgroup, else the work-list
+    # kernel + tokenize_kernel<false>), else fpstok_sample
     roof = fps_roofline(st, step_gpu if fused else per_call["sample"],
-                        "fpstok_tokenize call: tokenize_kernel (FPS + fused Voronoi pooling; "
-                        "the batch's bound on event size skips the work-list kernel)" if fused else "fpstok_sample call: plan_fps_kernel + "
+                        ("fpstok_tokenize call: tokenize_kernel<true> (FPS + fused Voronoi "
+                         "pooling, one workgroup per event)" if b_direct else
+                         "fpstok_tokenize call: plan_fps_kernel + tokenize_kernel<false> (FPS + "
+                         "fused Voronoi pooling, work list)") if fused else "fpstok_sample call: plan_fps_kernel + "
                         "sample_kernel (FPS)",
                         measured_traffic(args.workload) if fused else None)
     log("per-step GPU %.1f us; per call (stepwise) %s" % (

@@ -1592,6 +1592,7 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
 constexpr int kSortT = 256;
 constexpr int kSortW = kSortT / 64;
 constexpr int kMaxP = 1024;
+constexpr int kMaxBits = 10;  // bits of a slot index below kMaxP
 constexpr int kLdsPerm = 4096;  // events up to this size keep their permutation in LDS
 constexpr int kBatch = 8;       // members whose loads are issued together
 
@@ -1603,6 +1604,10 @@ constexpr int kBatch = 8;       // members whose loads are issued together
 // atomics.  Two passes: count per (wave, slot), then place.  `perm` may point
 // to LDS or to device memory.
 //   s_cnt: LDS int[kSortW * kMaxP];  s_off: LDS int[kMaxP + 1]
+// kAtomicCount: the counting pass adds with LDS atomics (the order of the
+// counts does not matter) and the placing pass unrolls its key bits; used
+// where it measured faster (the pooling backward), the plain form elsewhere.
+template <bool kAtomicCount = false>
 __device__ __forceinline__ void block_sort_by_token(const int32_t* __restrict__ asg, int n, int T,
                                                     int* __restrict__ perm, int* s_cnt,
                                                     int* s_off) {
@@ -1619,23 +1624,55 @@ __device__ __forceinline__ void block_sort_by_token(const int32_t* __restrict__ 
     int* __restrict__ wc = s_cnt + wave * T;
 
     for (int pass = 0; pass < 2; ++pass) {
-        for (int t0 = sbeg; t0 < send; t0 += 64) {
-            const int i = t0 + lane;
-            int key = i < send ? asg[i] : -1;
-            const bool valid = key >= 0 && key < T;
-            const uint64_t act = ballot(valid);
-            uint64_t match = act;
-            for (int bit = 0; bit < nbits; ++bit) {
-                const bool bb = (key >> bit) & 1;
-                const uint64_t bal = ballot(valid && bb);
-                match &= bb ? bal : (act & ~bal);
+        if (kAtomicCount && pass == 0) {
+            for (int i = sbeg + lane; i < send; i += 64) {
+                const int key = asg[i];
+                if (key >= 0 && key < T) atomicAdd(&wc[key], 1);
             }
-            const int rank = mbcnt(match);
-            const int cnt = __popcll(match);
-            if (pass == 1 && valid) perm[wc[key] + rank] = i;
-            __builtin_amdgcn_wave_barrier();
-            if (valid && rank == 0) wc[key] += cnt;
-            __builtin_amdgcn_wave_barrier();
+        } else if (kAtomicCount) {
+            for (int t0 = sbeg; t0 < send; t0 += 64) {
+                const int i = t0 + lane;
+                const int key = i < send ? asg[i] : -1;
+                const bool valid = key >= 0 && key < T;
+                const uint64_t act = ballot(valid);
+                uint32_t mlo = (uint32_t)act, mhi = (uint32_t)(act >> 32);
+#pragma unroll
+                for (int bit = 0; bit < kMaxBits; ++bit) {
+                    if (bit < nbits) {
+                        const bool bb = ((key >> bit) & 1) != 0;
+                        const uint64_t bal = ballot(valid && bb);
+                        const uint64_t nb = act & ~bal;
+                        mlo &= bb ? (uint32_t)bal : (uint32_t)nb;
+                        mhi &= bb ? (uint32_t)(bal >> 32) : (uint32_t)(nb >> 32);
+                    }
+                }
+                const uint64_t match = ((uint64_t)mhi << 32) | mlo;
+                const int rank = mbcnt(match);
+                const int cnt = __popcll(match);
+                if (valid) perm[wc[key] + rank] = i;
+                __builtin_amdgcn_wave_barrier();
+                if (valid && rank == 0) wc[key] += cnt;
+                __builtin_amdgcn_wave_barrier();
+            }
+        } else {
+            for (int t0 = sbeg; t0 < send; t0 += 64) {
+                const int i = t0 + lane;
+                int key = i < send ? asg[i] : -1;
+                const bool valid = key >= 0 && key < T;
+                const uint64_t act = ballot(valid);
+                uint64_t match = act;
+                for (int bit = 0; bit < nbits; ++bit) {
+                    const bool bb = (key >> bit) & 1;
+                    const uint64_t bal = ballot(valid && bb);
+                    match &= bb ? bal : (act & ~bal);
+                }
+                const int rank = mbcnt(match);
+                const int cnt = __popcll(match);
+                if (pass == 1 && valid) perm[wc[key] + rank] = i;
+                __builtin_amdgcn_wave_barrier();
+                if (valid && rank == 0) wc[key] += cnt;
+                __builtin_amdgcn_wave_barrier();
+            }
         }
         __syncthreads();
         if (pass == 0) {
@@ -3042,7 +3079,7 @@ __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
     if (a.mode == 0) {
         if (T >= 1) {
             int* perm = n <= kLdsPerm ? s_perm : a.perm + off;
-            block_sort_by_token(a.assign + off, n, T, perm, s_cnt, s_off);
+            block_sort_by_token<true>(a.assign + off, n, T, perm, s_cnt, s_off);
             for (int j = tid; j < T; j += kSortT) {
                 // kBatch weights loaded together, added in member order (a
                 // padded batch adds +0.0, which leaves the sum unchanged)

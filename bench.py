@@ -42,12 +42,12 @@ FPS_OPS_PER_POINT_ITER = 14
 # event size is under one workgroup's registers), from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE per dispatch, each scaled by its reading for a plain
 # device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
-# 2 * 378.6 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
+# 2 * 375.0 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
 # taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "4707718c2eb127913e8f0b3e35e2d08fc4bddcfde4881a994724703a37ad1b9a",
-    "bytes": int(round((2 * 378.6 + 419.3) * 1024)),
+    "kernels_sha256": "aa85ef189a845e0391823e595a06118a8527611c907e6f21059001679c491b39",
+    "bytes": int(round((2 * 375.0 + 419.3) * 1024)),
 }
 
 

@@ -44,3 +44,34 @@ def test_library_is_built_for_gfx950():
         fbuild.build()
     data = open(fbuild.LIB, "rb").read()
     assert b"gfx950" in data
+
+
+def _kernel_body(asm, prefix):
+    m = re.search(r"^(%s\S*):" % re.escape(prefix), asm, re.M)
+    assert m, prefix
+    start = m.end()
+    end = asm.index(".Lfunc_end", start)
+    return asm[start:end]
+
+
+def test_gang_poll_loads_issued_together(asm):
+    """Every agent-scope (sc1) record load of the gang's poll spin is issued
+    before any is waited for: hipcc waits for a load inside a divergent branch
+    before leaving the branch, which made each spin cost one round trip per
+    load.  In the work-list kernel no sc1 load may be followed by a full
+    vmcnt(0) wait before the next sc1 load of the same run."""
+    body = _kernel_body(asm, "_ZN6fpstok15tokenize_kernelILb0E")
+    lines = [l.strip() for l in body.splitlines()]
+    runs = 0
+    for i, l in enumerate(lines):
+        if not (l.startswith("global_load_dwordx2") and l.endswith("sc1")):
+            continue
+        # the next sc1 load within a few lines belongs to the same spin
+        for k in range(i + 1, min(i + 24, len(lines))):
+            if lines[k].startswith("global_load_dwordx2") and lines[k].endswith("sc1"):
+                between = lines[i + 1:k]
+                assert not any(b.startswith("s_waitcnt") and "vmcnt(0)" in b for b in between), \
+                    "serialised record loads near line %d" % i
+                runs += 1
+                break
+    assert runs > 0, "no poll spin found"

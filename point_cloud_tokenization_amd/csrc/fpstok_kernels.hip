@@ -1253,8 +1253,12 @@ __device__ __forceinline__ void plan_fps(const SampleArgs& a, int64_t B) {
     // gang items come first: clear their records (stale tags of an earlier
     // call must not match)
     gang_items = (int)min((int64_t)gang_items, max_items);
-    const int64_t gw = (int64_t)gang_items * 2 * kGangRecWords;
-    for (int64_t w = tid; w < gw; w += nt) a.gang_rec[w] = 0ull;
+    // 16-byte stores (a gang item's records are 2 * kGangRecWords 64-bit
+    // words, an even count, from a 256-byte aligned base)
+    static_assert(kGangRecWords % 2 == 0, "records clear in 16-byte stores");
+    const int64_t gw = (int64_t)gang_items * kGangRecWords;
+    uint4* rec4 = reinterpret_cast<uint4*>(a.gang_rec);
+    for (int64_t w = tid; w < gw; w += nt) rec4[w] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) {
         a.header[1] = (int)min((int64_t)items, max_items);  // items
         a.header[2] = 0;                                   // claim counter

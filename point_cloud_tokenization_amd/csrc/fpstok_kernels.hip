@@ -1488,6 +1488,7 @@ __global__ __launch_bounds__(kAsgT) void assign_kernel(AssignArgs a) {
 constexpr int kKnnT = 256;
 constexpr int kKnnW = kKnnT / 64;
 constexpr int kKnnCap = 512;  // candidates per wave held in LDS
+constexpr int kKnnReg = 8;    // keys per lane kept in registers (events of up to 512 pulses)
 
 __device__ __forceinline__ uint64_t dkey(float d, int i) {
     return ((uint64_t)__float_as_uint(d) << 32) | (uint32_t)i;
@@ -1524,11 +1525,29 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
     const float4 c = a.centroids[b * P + j];
     const float4* __restrict__ p = a.coords + off;
 
+    // events of up to kKnnReg * 64 pulses keep their keys in registers
+    // (lane l: pulses l, l+64, ...), loaded together with clamped indices,
+    // so both passes below read the coordinates once
+    const bool inreg = n <= kKnnReg * 64;
+    uint64_t keys[kKnnReg];
     uint64_t mykey = ~0ull;
-    for (int i = lane; i < n; i += 64) {
-        const float4 q = p[i];
-        const uint64_t key = dkey(sqd(q.x, q.y, q.z, q.w, c.x, c.y, c.z, c.w), i);
-        mykey = key < mykey ? key : mykey;
+    if (inreg) {
+        float4 qs[kKnnReg];
+#pragma unroll
+        for (int r = 0; r < kKnnReg; ++r) qs[r] = p[min(r * 64 + lane, n - 1)];
+#pragma unroll
+        for (int r = 0; r < kKnnReg; ++r) {
+            const int i = r * 64 + lane;
+            keys[r] = i < n ? dkey(sqd(qs[r].x, qs[r].y, qs[r].z, qs[r].w, c.x, c.y, c.z, c.w), i)
+                            : ~0ull;
+            mykey = keys[r] < mykey ? keys[r] : mykey;
+        }
+    } else {
+        for (int i = lane; i < n; i += 64) {
+            const float4 q = p[i];
+            const uint64_t key = dkey(sqd(q.x, q.y, q.z, q.w, c.x, c.y, c.z, c.w), i);
+            mykey = key < mykey ? key : mykey;
+        }
     }
     const int valid = min(n, 64);
     uint64_t tau = ~0ull;
@@ -1545,18 +1564,33 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
     }
     uint64_t* __restrict__ buf = s_buf[wave];
     int cnt = 0;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-        const int i = i0 + lane;
-        uint64_t key = ~0ull;
-        if (i < n) {
-            const float4 q = p[i];
-            key = dkey(sqd(q.x, q.y, q.z, q.w, c.x, c.y, c.z, c.w), i);
+    if (inreg) {
+#pragma unroll
+        for (int r = 0; r < kKnnReg; ++r) {
+            if (r * 64 < n) {
+                const int i = r * 64 + lane;
+                const uint64_t key = keys[r];
+                const bool take = i < n && key <= tau;
+                const uint64_t bl = ballot(take);
+                const int pos = cnt + mbcnt(bl);
+                if (take && pos < kKnnCap) buf[pos] = key;
+                cnt += __popcll(bl);
+            }
         }
-        const bool take = i < n && key <= tau;
-        const uint64_t bl = ballot(take);
-        const int pos = cnt + mbcnt(bl);
-        if (take && pos < kKnnCap) buf[pos] = key;
-        cnt += __popcll(bl);
+    } else {
+        for (int i0 = 0; i0 < n; i0 += 64) {
+            const int i = i0 + lane;
+            uint64_t key = ~0ull;
+            if (i < n) {
+                const float4 q = p[i];
+                key = dkey(sqd(q.x, q.y, q.z, q.w, c.x, c.y, c.z, c.w), i);
+            }
+            const bool take = i < n && key <= tau;
+            const uint64_t bl = ballot(take);
+            const int pos = cnt + mbcnt(bl);
+            if (take && pos < kKnnCap) buf[pos] = key;
+            cnt += __popcll(bl);
+        }
     }
     const int need = min(k, n);
     if (cnt <= kKnnCap) {

@@ -39,6 +39,8 @@ static fpstok_status hip_fail(hipError_t e, const char* what) {
     return fail(FPSTOK_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+static_assert(kKnnMaxK == FPSTOK_MAX_K, "kNN list bound");
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
@@ -505,6 +507,8 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     if ((voronoi || pr->lloyd_iters > 0) && !assign && bt->num_points > 0)
         return fail(FPSTOK_EINVAL, "assign is required in Voronoi mode and for Lloyd");
     if (!voronoi && !knn_idx) return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
+    if (!voronoi && (pr->k < 1 || pr->k > FPSTOK_MAX_K))
+        return fail(FPSTOK_EINVAL, "k must be in [1, %d]", FPSTOK_MAX_K);
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
     const SampleArgs a = sample_args(bt, pr, start_idx, centroid_idx, centroids, token_count,
@@ -515,15 +519,37 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
         // every work list planned by one launch
         const PoolArgs p = pool_args(bt, pr, token_count, assign, knn_idx, pooled, cell_count, ws,
                                      L);
-        hipError_t e = launch_plan_all(a, bt->num_events, ws, L, p, pr->lloyd_iters > 0, voronoi, s);
-        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+        hipError_t e = hipSuccess;
+        // nothing to plan: no FPS work list (event-size bound), no Lloyd
+        // chunks, and kNN pooling needs no chunk list
+        if (!a.direct || pr->lloyd_iters > 0 || voronoi) {
+            e = launch_plan_all(a, bt->num_events, ws, L, p, pr->lloyd_iters > 0, voronoi, s);
+            if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+        }
         e = launch_sample_items(a, bt->num_events, s);
         if (e != hipSuccess) return hip_fail(e, "sample kernel launch");
         e = run_lloyd(bt, pr, centroids, token_count, assign, ws, L, s);
         if (e != hipSuccess) return hip_fail(e, "lloyd kernel launch");
-        if (!voronoi && (st = fpstok_knn(bt, pr, centroids, token_count, knn_idx, ws, ws_bytes,
-                                         stream)) != FPSTOK_OK)
-            return st;
+        if (!voronoi) {
+            // the lists and their pooling in one launch
+            KnnArgs k{};
+            k.coords = (const float4*)bt->coords;
+            k.offsets = bt->offsets;
+            k.N = bt->num_points;
+            k.P = pr->num_patches;
+            k.k = pr->k;
+            k.centroids = (const float4*)centroids;
+            k.token_count = token_count;
+            k.knn_idx = knn_idx;
+            k.features = p.features;
+            k.C = p.C;
+            k.weight_col = p.weight_col;
+            k.pooled = pooled;
+            k.cell_count = cell_count;
+            e = launch_knn(k, bt->num_events, s);
+            if (e != hipSuccess) return hip_fail(e, "knn kernel launch");
+            return ok();
+        }
         e = run_pool(bt, pr, p, L, s);
         if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
         return ok();

@@ -101,6 +101,8 @@ struct AssignArgs {
     int skip_small;  // leave events with n <= P untouched
 };
 
+constexpr int kKnnMaxK = 64;  // longest kNN list (the API's FPSTOK_MAX_K)
+
 struct KnnArgs {
     const float4* coords;
     const int64_t* offsets;
@@ -110,6 +112,13 @@ struct KnnArgs {
     const float4* centroids;
     const int32_t* token_count;
     int32_t* knn_idx;
+    // with `pooled` set, each list's members are pooled by the wave that
+    // ranked them (fpstok_tokenize); NULL for fpstok_knn
+    const float* features;
+    int C;
+    int weight_col;
+    float* pooled;
+    int32_t* cell_count;
 };
 
 struct LloydArgs {

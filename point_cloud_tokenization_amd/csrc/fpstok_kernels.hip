@@ -1488,6 +1488,7 @@ __global__ __launch_bounds__(kAsgT) void assign_kernel(AssignArgs a) {
 constexpr int kKnnT = 256;
 constexpr int kKnnW = kKnnT / 64;
 constexpr int kKnnCap = 512;  // candidates per wave held in LDS
+constexpr int kKnnPoolB = 8;  // list members whose rows are loaded together when pooling
 constexpr int kKnnReg = 8;    // keys per lane kept in registers (events of up to 512 pulses)
 
 __device__ __forceinline__ uint64_t dkey(float d, int i) {
@@ -1502,8 +1503,54 @@ __device__ __forceinline__ uint64_t dkey(float d, int i) {
 //  3. The candidates are ranked by counting and the first k written out.
 //  If more than kKnnCap keys are <= tau, k rounds of wave-wide
 //  min-extraction are used instead.
+// The members of token j's list, pooled in list order by the wave that
+// ranked them: lane c sums column c (and every lane the weights) in float64,
+// as the kNN pooling kernel does; members are loaded kBatch at a time with
+// clamped indices (no load behind a per-lane branch).
+__device__ __forceinline__ void knn_pool_list(const KnnArgs& a, int64_t b, int64_t off, int n,
+                                              int j, int len, const int* lst) {
+    const int lane = lane_id();
+    const int C = a.C;
+    float* __restrict__ out = a.pooled + (b * a.P + j) * (int64_t)C;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+        const int c = c0 + lane;
+        const int cc = c < C ? c : C - 1;
+        double W = 0.0, S = 0.0;
+        for (int m0 = 0; m0 < len; m0 += kKnnPoolB) {
+            int idx[kKnnPoolB];
+            float w[kKnnPoolB], f[kKnnPoolB];
+#pragma unroll
+            for (int q = 0; q < kKnnPoolB; ++q) {
+                const int i = lst[min(m0 + q, len - 1)];
+                idx[q] = m0 + q < len && i >= 0 && i < n ? i : -1;
+            }
+#pragma unroll
+            for (int q = 0; q < kKnnPoolB; ++q) {
+                const float* __restrict__ r = a.features + (off + (idx[q] >= 0 ? idx[q] : 0)) * (int64_t)C;
+                w[q] = a.weight_col >= 0 ? r[a.weight_col] : 1.0f;
+                f[q] = r[cc];
+            }
+#pragma unroll
+            for (int q = 0; q < kKnnPoolB; ++q) {
+                if (idx[q] >= 0) {
+                    const double wd = (double)w[q];
+                    W += wd;
+                    S += wd * (double)f[q];
+                }
+            }
+        }
+        if (c < C) out[c] = W != 0.0 ? (float)(S / W) : 0.0f;
+    }
+    if (a.cell_count && lane == 0) {
+        int count = 0;
+        for (int e = 0; e < len; ++e) count += (lst[e] >= 0 && lst[e] < n) ? 1 : 0;
+        a.cell_count[b * a.P + j] = count;
+    }
+}
+
 __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
     __shared__ uint64_t s_buf[kKnnW][kKnnCap];
+    __shared__ int s_lst[kKnnW][kKnnMaxK];
     const int P = a.P;
     const int k = a.k;
     const int nb = (P + kKnnW - 1) / kKnnW;
@@ -1518,8 +1565,19 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
     int T = a.token_count[b];
     T = T < 0 ? 0 : (T > P ? P : T);
     int32_t* __restrict__ row = a.knn_idx + (b * P + j) * (int64_t)k;
+    int* lst = s_lst[wave];
     if (j >= T || n <= P) {
-        for (int e = lane; e < k; e += 64) row[e] = (e == 0 && j < T && j < n) ? j : -1;
+        for (int e = lane; e < k; e += 64) {
+            const int v = (e == 0 && j < T && j < n) ? j : -1;
+            row[e] = v;
+            lst[e] = v;
+        }
+        if (a.pooled) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            knn_pool_list(a, b, off, n, j, j < T ? k : 0, lst);
+        }
         return;
     }
     const float4 c = a.centroids[b * P + j];
@@ -1600,7 +1658,10 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
             const uint64_t kq = buf[q];
             int rank = 0;
             for (int r = 0; r < cnt; ++r) rank += buf[r] < kq ? 1 : 0;
-            if (rank < k) row[rank] = (int)(uint32_t)kq;
+            if (rank < k) {
+                row[rank] = (int)(uint32_t)kq;
+                lst[rank] = (int)(uint32_t)kq;
+            }
         }
     } else {
         // k rounds of extracting the smallest key above the previous one
@@ -1619,10 +1680,22 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
             const bool cand = hi == (uint32_t)mhi;
             const int mlo = wave_min_i(cand ? (int)(lo ^ 0x80000000u) : 0x7fffffff) ^ (int)0x80000000u;
             last = ((uint64_t)(uint32_t)mhi << 32) | (uint32_t)mlo;
-            if (lane == 0) row[e] = (int)(uint32_t)last;
+            if (lane == 0) {
+                row[e] = (int)(uint32_t)last;
+                lst[e] = (int)(uint32_t)last;
+            }
         }
     }
-    for (int e = need + lane; e < k; e += 64) row[e] = -1;
+    for (int e = need + lane; e < k; e += 64) {
+        row[e] = -1;
+        lst[e] = -1;
+    }
+    if (a.pooled) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        knn_pool_list(a, b, off, n, j, k, lst);
+    }
 }
 
 // ---------------------------------------------------- stable sort by token

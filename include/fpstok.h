@@ -187,7 +187,8 @@ fpstok_status fpstok_pool(const fpstok_batch* batch, const fpstok_params* params
  * results as calling them in that order (README of felixyu7/neptune, "How it
  * works" step 1: FPS, Voronoi or kNN pooling, optional Lloyd).  In Voronoi mode without Lloyd the
  * FPS and the pooling run in one kernel: each workgroup pools its event as
- * soon as its sampling ends.  Outputs as in the calls above; `assign` is
+ * soon as its sampling ends; in kNN mode each token's list is pooled by the
+ * wave that ranked it, in the kNN kernel.  Outputs as in the calls above; `assign` is
  * required in Voronoi mode and for Lloyd (else it may be NULL), `knn_idx` in
  * kNN mode (else it may be NULL), `features` are always read.
  * Errors: those of the calls it makes. */

@@ -275,6 +275,27 @@ def test_tokenize_fused_edges(oracle_mod):
     _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=16, L=1, stepwise=True, label="stepwise")
 
 
+def test_knn_fused_pooling(oracle_mod):
+    """fpstok_tokenize in kNN mode pools each list inside the kNN kernel:
+    empty and one-pulse events, events at and around P, k above n, k = 1
+    and the largest k, plain and unit-charge means, rows wider than a wave
+    (C = 70: two column rounds), with and without the event-size bound."""
+    ns = [0, 1, 5, 127, 128, 129, 300, 1000, 4097, 0, 40]
+    b = synth.icecube_events(ns, 61, C=6)
+    m = int(np.diff(b["offsets"]).max())
+    for k, hint in ((16, 0), (16, m), (1, m), (64, 0)):
+        _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=k, label="knn fused k=%d hint=%d" % (k, hint),
+                            max_event_points=hint)
+    _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=16, weighted=False,
+                        label="knn fused plain mean", max_event_points=m)
+    _tokenize_vs_oracle(oracle_mod, b, 128, mode=1, k=16, charge_col=-1,
+                        label="knn fused unit charge", max_event_points=m)
+    w = synth.icecube_events([0, 3, 200, 700], 62, C=70)
+    _tokenize_vs_oracle(oracle_mod, w, 64, mode=1, k=16, label="knn fused C=70",
+                        max_event_points=700)
+    _tokenize_vs_oracle(oracle_mod, w, 64, mode=1, k=16, L=2, label="knn fused C=70 Lloyd")
+
+
 def test_max_event_points_hint(oracle_mod):
     """The work-list-free path: a correct bound (every event within one
     workgroup) and a bound that is too small (events above 4096 pulses fall

@@ -85,7 +85,9 @@ typedef enum {
     FPSTOK_EINVAL = 1,      /* invalid argument; nothing was enqueued               */
     FPSTOK_EWORKSPACE = 2,  /* ws is NULL or ws_bytes < fpstok_workspace_size(...)  */
     FPSTOK_EUNSUPPORTED = 3,/* valid request beyond an implementation limit         */
-    FPSTOK_EHIP = 4         /* a HIP runtime call failed; see fpstok_last_error()   */
+    FPSTOK_EHIP = 4,        /* a HIP runtime call failed; see fpstok_last_error()   */
+    FPSTOK_EDEVICE = 5      /* fpstok_device_status only: a kernel's bounded wait    */
+                            /* gave up, the call's outputs are not valid             */
 } fpstok_status;
 
 typedef enum { FPSTOK_VORONOI = 0, FPSTOK_KNN = 1 } fpstok_assign_mode;
@@ -273,6 +275,28 @@ fpstok_status fpstok_pool_backward(const fpstok_batch* batch, const fpstok_param
  * Errors: EINVAL (NULL pointers, num_events < 0), EHIP. */
 fpstok_status fpstok_random_start(const int64_t* offsets, int64_t num_events, uint64_t seed,
                                   uint64_t step, int32_t* start_idx, void* stream);
+
+/* Device-side status of the last fpstok_sample or fpstok_tokenize call on
+ * the workspace `ws` (its first ws_bytes bytes; at least the 256-byte
+ * header).  An event of more than 4096 pulses is split over a gang of
+ * workgroups that wait for one another's candidate records and pooling
+ * partial sums; every such wait is bounded (a few million polls) so that a
+ * stalled partner can never hang the GPU.  A wait that gives up sets a word
+ * in the workspace and the call completes with outputs that are not valid.
+ * This function waits for `stream` (it synchronizes: not for the hot path),
+ * reads that word and returns FPSTOK_OK, or FPSTOK_EDEVICE with the detail
+ * in fpstok_last_error(), or FPSTOK_EHIP.  Every fpstok_sample and
+ * fpstok_tokenize call clears the word when it starts; the other calls
+ * neither set nor clear it.  Errors: EINVAL (NULL ws, ws_bytes < 256). */
+fpstok_status fpstok_device_status(const void* ws, size_t ws_bytes, void* stream);
+
+/* Testing only: the number of polls after which a wait between workgroups
+ * gives up, for calls made after this one in the process (0 restores the
+ * default).  Tests of the failure path set a tiny limit so that a gang's
+ * wait gives up and fpstok_device_status reports it, while every kernel still
+ * ends normally.  Not for production use: a small limit makes large events
+ * fail. */
+void fpstok_debug_set_spin_limit(uint32_t polls);
 
 /* Debug check of the data preconditions of `batch` (offsets monotone with
  * offsets[0] = 0 and offsets[B] = N, finite coords, charge >= 0 when

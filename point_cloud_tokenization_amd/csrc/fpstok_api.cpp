@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -40,6 +41,9 @@ static fpstok_status hip_fail(hipError_t e, const char* what) {
 }
 
 static_assert(kKnnMaxK == FPSTOK_MAX_K, "kNN list bound");
+
+// Polls before a wait between workgroups gives up (fpstok_debug_set_spin_limit).
+static std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -170,6 +174,7 @@ static SampleArgs sample_args(const fpstok_batch* bt, const fpstok_params* pr,
     a.ws_mind = at<float>(ws, L.mind);
     a.ws_near = at<int32_t>(ws, L.near);
     a.direct = bt->max_event_points > 0 && bt->max_event_points <= kFpsCapPulses ? 1 : 0;
+    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     a.header = at<int32_t>(ws, L.header);
     a.item_ev = at<int32_t>(ws, L.item_ev);
     a.item_g = at<int32_t>(ws, L.item_g);
@@ -491,14 +496,14 @@ FPSTOK_API fpstok_status fpstok_random_start(const int64_t* offsets, int64_t num
     return ok();
 }
 
-FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
-                                         const int32_t* start_idx, int32_t* centroid_idx,
-                                         float* centroids, int32_t* token_count, int32_t* assign,
-                                         int32_t* knn_idx, float* pooled, int32_t* cell_count,
-                                         void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of fpstok_tokenize, the workspace aside.
+static fpstok_status check_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
+                                    int32_t* centroid_idx, float* centroids,
+                                    int32_t* token_count, int32_t* assign, int32_t* knn_idx,
+                                    float* pooled) {
     fpstok_status st = check_common(bt, pr, true, true);
     if (st != FPSTOK_OK) return st;
-    if (bt->num_events == 0) return ok();
+    if (bt->num_events == 0) return FPSTOK_OK;
     if (!centroid_idx || !centroids || !token_count || !pooled)
         return fail(FPSTOK_EINVAL, "centroid_idx, centroids, token_count and pooled are required");
     if (((uintptr_t)centroids & 15u) != 0)
@@ -509,8 +514,16 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     if (!voronoi && !knn_idx) return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
     if (!voronoi && (pr->k < 1 || pr->k > FPSTOK_MAX_K))
         return fail(FPSTOK_EINVAL, "k must be in [1, %d]", FPSTOK_MAX_K);
-    WorkspaceLayout L;
-    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    return FPSTOK_OK;
+}
+
+// The tokenizer's launches on a checked workspace.
+static fpstok_status run_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
+                                  const int32_t* start_idx, int32_t* centroid_idx,
+                                  float* centroids, int32_t* token_count, int32_t* assign,
+                                  int32_t* knn_idx, float* pooled, int32_t* cell_count, void* ws,
+                                  const WorkspaceLayout& L, void* stream) {
+    const bool voronoi = pr->assign_mode == FPSTOK_VORONOI;
     const SampleArgs a = sample_args(bt, pr, start_idx, centroid_idx, centroids, token_count,
                                      assign, ws, L);
     hipStream_t s = (hipStream_t)stream;
@@ -560,6 +573,21 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     return ok();
 }
 
+FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
+                                         const int32_t* start_idx, int32_t* centroid_idx,
+                                         float* centroids, int32_t* token_count, int32_t* assign,
+                                         int32_t* knn_idx, float* pooled, int32_t* cell_count,
+                                         void* ws, size_t ws_bytes, void* stream) {
+    fpstok_status st = check_tokenize(bt, pr, centroid_idx, centroids, token_count, assign,
+                                      knn_idx, pooled);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    WorkspaceLayout L;
+    if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    return run_tokenize(bt, pr, start_idx, centroid_idx, centroids, token_count, assign, knn_idx,
+                        pooled, cell_count, ws, L, stream);
+}
+
 FPSTOK_API fpstok_status fpstok_validate(const fpstok_batch* bt, void* stream) {
     if (!bt) return fail(FPSTOK_EINVAL, "batch is NULL");
     const int64_t B = bt->num_events, N = bt->num_points;
@@ -602,6 +630,30 @@ FPSTOK_API fpstok_status fpstok_validate(const fpstok_batch* bt, void* stream) {
     return ok();
 }
 
+FPSTOK_API fpstok_status fpstok_device_status(const void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return fail(FPSTOK_EINVAL, "workspace is NULL");
+    if (ws_bytes < 64 * sizeof(int32_t))
+        return fail(FPSTOK_EINVAL, "workspace has %zu bytes, fewer than its header", ws_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, (const int32_t*)ws + 3, sizeof(word),
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of the device error word");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (word == 0) return ok();
+    return fail(FPSTOK_EDEVICE,
+                "a wait between the workgroups of one event gave up (error word 0x%x:%s%s); "
+                "the outputs of the last fpstok_sample / fpstok_tokenize call on this "
+                "workspace are not valid",
+                (unsigned)word, (word & kErrFpsWait) ? " FPS candidate exchange" : "",
+                (word & kErrPoolWait) ? " pooling partial sums" : "");
+}
+
+FPSTOK_API void fpstok_debug_set_spin_limit(uint32_t polls) {
+    g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls, std::memory_order_relaxed);
+}
+
 FPSTOK_API const char* fpstok_status_string(fpstok_status status) {
     switch (status) {
         case FPSTOK_OK: return "ok";
@@ -609,6 +661,7 @@ FPSTOK_API const char* fpstok_status_string(fpstok_status status) {
         case FPSTOK_EWORKSPACE: return "workspace too small";
         case FPSTOK_EUNSUPPORTED: return "unsupported";
         case FPSTOK_EHIP: return "HIP runtime error";
+        case FPSTOK_EDEVICE: return "device-side failure";
     }
     return "unknown status";
 }

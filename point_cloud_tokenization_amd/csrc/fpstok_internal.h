@@ -26,6 +26,14 @@ constexpr int kCombLast = 4;
 // candidate entries of one word each, the shard's bound, padding.
 constexpr int kGangRecWords = 64 + 8;
 
+// Bits of the device error word (workspace header[3]): a bounded wait
+// between the workgroups of one event gave up, so that call's outputs are
+// not valid.
+constexpr int32_t kErrFpsWait = 1;   // the gang FPS exchange of candidate records
+constexpr int32_t kErrPoolWait = 2;  // the gang shards' pooling partial sums
+// Default bound on every wait between workgroups (polls; about a second).
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+
 // Workspace carve-up.  Every region starts on a 256-byte boundary.
 struct WorkspaceLayout {
     size_t header;      // int32[64]: [0] = number of chunks
@@ -78,8 +86,10 @@ struct SampleArgs {
     int32_t* ws_near;
     int direct;                     // 1: item i is event i, no work list (every event
                                     // within one workgroup's registers, else streaming)
-    int32_t* header;                // [1] items, [2] claim counter, [3] error word,
-                                    // [5] gang items (0: item i is event i)
+    uint32_t spin_limit;            // polls before a wait between workgroups gives up
+    int32_t* header;                // [1] items, [2] claim counter, [3] device error word
+                                    // (kErrFpsWait | kErrPoolWait bits), [5] gang items
+                                    // (0: item i is event i)
     int32_t* item_ev;               // [max_items] event of each work item
     int32_t* item_g;                // [max_items] shard of each work item
     unsigned long long* gang_rec;   // [max_items][2][kGangRecWords] gang records

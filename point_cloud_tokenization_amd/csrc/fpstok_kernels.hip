@@ -14,6 +14,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "fpstok_internal.h"
 
 namespace fpstok {
@@ -297,7 +298,6 @@ constexpr int kFpsM = 16;                  // register-resident pulses per threa
 constexpr int kFpsCap = kFpsT * kFpsM;     // pulses one workgroup holds in registers
 static_assert(kFpsCap == kFpsCapPulses, "host and device disagree on the register capacity");
 constexpr int kGangMax = 64;               // workgroups sharing one event at most
-constexpr uint32_t kSpinLimit = 1u << 22;  // bound on every inter-workgroup wait
 
 struct __align__(16) FpsSlot {
     float v;
@@ -317,6 +317,7 @@ struct Shard {
     int G;                     // shards of the event
     unsigned long long* rec;   // records of the gang: [G][2][kGangRecWords]
     int32_t* err;              // device error word (bounded wait exceeded)
+    uint32_t spin_limit;       // polls before a wait gives up
 };
 
 
@@ -963,9 +964,12 @@ __device__ __forceinline__ int fps_gang(const SampleArgs& a, int64_t b, int64_t 
                 for (int q = 0; q < kGangQ; ++q)
                     if (q < nq) ok = ok && rec_ok(vw[q], tag);
                 if (__syncthreads_and(ok)) break;
-                if (spin >= kSpinLimit) {
+                if (spin >= sh.spin_limit) {
+                    // give up: the exchange goes on with what it read, and the
+                    // error word tells the caller the outputs are not valid
                     if (tid == 0)
-                        __hip_atomic_store(sh.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_fetch_or(sh.err, kErrFpsWait, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -1398,7 +1402,8 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
         const int S = (n + G - 1) / G;
         const int lo = g * S;
         const Shard sh{lo, min(S, n - lo), g, G,
-                       a.gang_rec + (size_t)(item - g) * 2 * kGangRecWords, a.header + 3};
+                       a.gang_rec + (size_t)(item - g) * 2 * kGangRecWords, a.header + 3,
+                       a.spin_limit};
         it.par = fps_gang_dispatch(a, b, off, n, s0, sh, s_gang, s_sel, s_asg) & 1;
         it.kind = 2;
         it.G = G;
@@ -1414,6 +1419,9 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
 }
 
 __global__ __launch_bounds__(kFpsT) void sample_kernel(SampleArgs a) {
+    // in direct mode no planner clears the device error word (nothing in
+    // this mode can set it)
+    if (a.direct && blockIdx.x == 0 && threadIdx.x == 0) a.header[3] = 0;
     __shared__ int s_item;
     __shared__ FpsSlot s_slots[2][kFpsW];
     __shared__ int s_sel[FPSTOK_MAX_SLOTS];
@@ -2760,6 +2768,9 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
     int* s_off = s_cnt + kSortW * P;
     GangLds& s_gang = *reinterpret_cast<GangLds*>(s_perm);
     float* s_feat = reinterpret_cast<float*>(s_off + P + 1);
+    // in direct mode no planner clears the device error word (nothing in
+    // this mode can set it)
+    if (kDirect && blockIdx.x == 0 && threadIdx.x == 0) a.header[3] = 0;
     const ItemInfo it = sample_item<kDirect>(a, &s_item, s_slots, s_gang, s_sel, s_asg, pa.features,
                                              pa.C, pa.stage_cap, s_feat);
     if (it.b < 0) return;
@@ -2850,9 +2861,10 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
                 ok = ok && rec_ok(w, (int)want);
             }
             if (ballot(!ok) == 0) break;
-            if (spin >= kSpinLimit) {
+            if (spin >= a.spin_limit) {
                 if (lane == 0)
-                    __hip_atomic_store(a.header + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_or(a.header + 3, kErrPoolWait, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);

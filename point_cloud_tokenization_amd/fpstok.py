@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfpstok.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fpstok.h")
 
-OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP, EDEVICE = 0, 1, 2, 3, 4, 5
 VORONOI, KNN = 0, 1
 MAX_PATCHES, MAX_K, MAX_LLOYD = 1024, 64, 1000
 
@@ -27,7 +27,8 @@ class FpstokError(RuntimeError):
 
 
 _STATUS = {OK: "ok", EINVAL: "invalid argument", EWORKSPACE: "workspace too small",
-           EUNSUPPORTED: "unsupported", EHIP: "HIP runtime error"}
+           EUNSUPPORTED: "unsupported", EHIP: "HIP runtime error",
+           EDEVICE: "device-side failure"}
 
 
 class Batch(ctypes.Structure):
@@ -70,9 +71,13 @@ def lib():
         L.fpstok_unpack.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
         L.fpstok_pool_backward.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fpstok_random_start.argtypes = [vp, i64, ctypes.c_uint64, ctypes.c_uint64, vp, vp]
+        L.fpstok_device_status.argtypes = [vp, sz, vp]
+        L.fpstok_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
+        L.fpstok_debug_set_spin_limit.restype = None
         for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
                   "fpstok_pool", "fpstok_tokenize", "fpstok_validate", "fpstok_pack",
-                  "fpstok_unpack", "fpstok_pool_backward", "fpstok_random_start"):
+                  "fpstok_unpack", "fpstok_pool_backward", "fpstok_random_start",
+                  "fpstok_device_status"):
             getattr(L, f).restype = ctypes.c_int
         L.fpstok_status_string.argtypes = [ctypes.c_int]
         L.fpstok_status_string.restype = ctypes.c_char_p
@@ -266,6 +271,20 @@ def validate(bt, stream=None):
     _check(lib().fpstok_validate(ctypes.byref(bt), _stream_handle(stream)), "fpstok_validate")
 
 
+def device_status(ws, stream=None):
+    """fpstok_device_status: raises FpstokError (status EDEVICE) if a bounded
+    wait between workgroups gave up in the last sample / tokenize call on the
+    workspace tensor `ws`.  Synchronizes the stream."""
+    _check(lib().fpstok_device_status(_ptr(ws), ws.numel(), _stream_handle(stream)),
+           "fpstok_device_status")
+
+
+def debug_set_spin_limit(polls):
+    """Testing only: polls before a wait between workgroups gives up (0: the
+    default)."""
+    lib().fpstok_debug_set_spin_limit(int(polls))
+
+
 # ------------------------------------------------------------- convenience
 
 def offsets_from_batch_ids(batch_ids, num_events):
@@ -333,6 +352,11 @@ class Tokenizer:
                       o["assign"], o["knn_idx"], o["pooled"], o["cell_count"], self.ws,
                       start_idx, stream)
         return o
+
+    def check(self, stream=None):
+        """Raise if the last call's outputs are not valid (fpstok_device_status;
+        synchronizes)."""
+        device_status(self.ws, stream)
 
     def stepwise(self, start_idx=None, stream=None):
         """The same result through the five separate calls."""

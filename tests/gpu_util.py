@@ -61,6 +61,49 @@ def member_scale(values, offsets, P, weights, mode, assign=None, knn_idx=None):
     return s.reshape(B, P, C)
 
 
+def backward_scale(features, offsets, P, token_count, pooled, grad_pooled, mode, assign=None,
+                   knn_idx=None, weighted=True, charge_col=-1):
+    """Per-element scale of the pooling gradient: for pulse i and column c',
+    the sum over the tokens j that hold i (weight sum W_j != 0) of the
+    absolute values of the terms the gradient adds, |g_j[c']| |w_i| / |W_j|,
+    plus, for the weight column, sum_c |g_j[c]| (|f_i[c]| + |m_j[c]|) / |W_j|.
+    |gpu - oracle| <= 1e-5 max(|oracle|, scale) bounds each element by the
+    rounding of its own sum, however small it is next to its row."""
+    f = features.astype(np.float64)
+    N, C = f.shape
+    B = offsets.size - 1
+    wcol = charge_col if (weighted and charge_col >= 0) else -1
+    w = f[:, wcol] if wcol >= 0 else np.ones(N)
+    tc = np.clip(token_count.astype(np.int64), 0, P)
+    if mode == 0:
+        ev = np.repeat(np.arange(B), np.diff(offsets))
+        a = assign.astype(np.int64)
+        ok = (a >= 0) & (a < tc[ev])
+        pi = np.nonzero(ok)[0]
+        pb, pj = ev[ok], a[ok]
+    else:
+        k = knn_idx.shape[-1]
+        lists = knn_idx.reshape(B, P, k).astype(np.int64)
+        n = np.diff(offsets)
+        bb, jj, _ = np.meshgrid(np.arange(B), np.arange(P), np.arange(k), indexing="ij")
+        ok = (lists >= 0) & (lists < n[bb]) & (jj < tc[bb])
+        pb, pj = bb[ok], jj[ok]
+        pi = offsets[pb] + lists[ok]
+    W = np.zeros(B * P)
+    np.add.at(W, pb * P + pj, w[pi])
+    Wp = np.abs(W[pb * P + pj])
+    use = Wp != 0
+    pi, pb, pj, Wp = pi[use], pb[use], pj[use], Wp[use]
+    g = np.abs(grad_pooled.astype(np.float64)).reshape(B * P, C)[pb * P + pj]
+    m = np.abs(pooled.astype(np.float64)).reshape(B * P, C)[pb * P + pj]
+    scale = np.zeros((N, C))
+    np.add.at(scale, pi, g * (np.abs(w[pi]) / Wp)[:, None])
+    if wcol >= 0:
+        t2 = (g * (np.abs(f[pi]) + m)).sum(axis=1) / Wp
+        np.add.at(scale[:, wcol], pi, t2)
+    return scale
+
+
 def assert_close_scaled(got, ref, scale, what):
     got = got.astype(np.float64)
     ref = ref.astype(np.float64)
@@ -97,6 +140,7 @@ def run_pipeline(batch, P, mode=0, k=16, L=0, weighted=True, charge_col=5, start
     asg = torch.empty(N, dtype=torch.int32, device=dev)
     st = None if start_idx is None else to_dev(np.asarray(start_idx, np.int32))
     F.sample(bt, pr, cidx, cen, tc, asg, ws, st)
+    F.device_status(ws)  # no bounded wait between workgroups gave up
     torch.cuda.synchronize()
     out = dict(centroid_idx=to_np(cidx), centroids=to_np(cen), token_count=to_np(tc),
                assign=to_np(asg))

@@ -136,6 +136,13 @@ def test_other_calls_reject_bad_arguments(L):
                          None) == F.EINVAL
 
 
+def test_device_status_rejects_bad_workspace(L):
+    assert L.fpstok_device_status(None, 1 << 20, None) == F.EINVAL
+    assert L.fpstok_last_error() != b""
+    assert L.fpstok_device_status(FAKE, 255, None) == F.EINVAL
+    assert L.fpstok_status_string(F.EDEVICE) == b"device-side failure"
+
+
 def test_validate_rejects_null_batch(L):
     assert L.fpstok_validate(None, None) == F.EINVAL
     bt = _bt(B=0, N=0)

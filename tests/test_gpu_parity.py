@@ -27,8 +27,7 @@ def _params(name):
                 charge_col=synth.CHARGE_COL)
 
 
-@pytest.mark.parametrize("name,r", [(n, r) for n in synth.WORKLOAD_ORDER[:4] for r in range(3)]
-                         + [("icecube_highE_b512", 0)])
+@pytest.mark.parametrize("name,r", [(n, r) for n in synth.WORKLOAD_ORDER for r in range(5)])
 def test_workloads(oracle_mod, name, r):
     b = synth.make_batch(name, synth.parity_seed(name, r))
     st = check_pipeline(oracle_mod, b, label="%s/r%d" % (name, r), **_params(name))
@@ -201,6 +200,7 @@ def _tokenize_vs_oracle(oracle_mod, b, P, mode=0, k=16, L=0, weighted=True, char
                       lloyd_iters=L, pool="charge" if weighted else "mean", charge_col=charge_col,
                       max_event_points=max_event_points)
     out = tok.stepwise() if stepwise else tok()
+    tok.check()  # no bounded wait between workgroups gave up
     got = {key: to_np(v) for key, v in out.items() if v is not None}
     ref = oracle_mod.tokenize(b["coords"], b["features"], b["offsets"], P=P, mode=mode, k=k, L=L,
                               weighted=weighted, charge_col=charge_col)
@@ -221,10 +221,10 @@ def _tokenize_vs_oracle(oracle_mod, b, P, mode=0, k=16, L=0, weighted=True, char
     assert_close_scaled(got["centroids"], ref["centroids"], cscale, "centroids " + label)
 
 
-@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
-def test_tokenize_workloads(oracle_mod, name):
+@pytest.mark.parametrize("name,r", [(n, r) for n in synth.WORKLOAD_ORDER for r in range(5)])
+def test_tokenize_workloads(oracle_mod, name, r):
     w = synth.WORKLOADS[name]
-    b = synth.make_batch(name, synth.parity_seed(name, 1))
+    b = synth.make_batch(name, synth.parity_seed(name, r))
     _tokenize_vs_oracle(oracle_mod, b, w["P"], w["mode"], w["k"], w["L"], w["weighted"], 5,
                         label=name)
 

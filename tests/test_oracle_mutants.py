@@ -48,6 +48,11 @@ MUTANTS = [
     ("philox_words_swapped", "        uint32_t n1 = (uint32_t)p1;", "        uint32_t n1 = (uint32_t)p0;"),
     ("random_start_modulo", "start_idx[b] = n > 0 ? (int32_t)(((uint64_t)out[0] * (uint64_t)n) >> 32) : 0;",
      "start_idx[b] = n > 0 ? (int32_t)((uint64_t)out[0] % (uint64_t)n) : 0;"),
+    ("random_start_event_and_step_swapped",
+     "uint32_t in[4] = {(uint32_t)b, (uint32_t)((uint64_t)b >> 32), (uint32_t)step,\n                          (uint32_t)(step >> 32)};",
+     "uint32_t in[4] = {(uint32_t)step, (uint32_t)(step >> 32), (uint32_t)b,\n                          (uint32_t)((uint64_t)b >> 32)};"),
+    ("random_start_word1", "(int32_t)(((uint64_t)out[0] * (uint64_t)n) >> 32)",
+     "(int32_t)(((uint64_t)out[1] * (uint64_t)n) >> 32)"),
     ("backward_ignores_weight", "    int32_t wcol = weighted != 0 ? charge_col : -1;", "    int32_t wcol = -1;"),
     ("backward_drops_weight_term", "                    gi[wcol] += s / W[j];", "                    (void)s;"),
     ("backward_unit_weight", "for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] * w / W[j];",
@@ -69,6 +74,8 @@ PIN_CALLS = [
     lambda m: nxt.test_pool_backward_zero_weight_token_and_linearity(m),
     lambda m: nxt.test_philox_known_answers(m),
     lambda m: nxt.test_random_start_mapping_and_spread(m),
+    lambda m: nxt.test_random_start_from_the_known_answer_vector(m),
+    lambda m: nxt.test_random_start_counter_layout(m),
     lambda m: [pins.test_closed_forms(m, c) for c in pins._cases()],
     lambda m: pins.test_identical_cloud_knn_pool_lloyd(m),
     lambda m: [pins.test_fps_and_assign_brute_force(m, s) for s in (1, 2, 3)],

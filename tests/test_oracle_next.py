@@ -252,3 +252,52 @@ def test_random_start_mapping_and_spread(oracle_mod):
     assert np.any(oracle_mod.random_start(off, 12345, 1) != s)
     assert np.any(oracle_mod.random_start(off, 12346, 0) != s)
     np.testing.assert_array_equal(oracle_mod.random_start(off, 12345, 0), s)
+
+
+def test_random_start_from_the_known_answer_vector(oracle_mod):
+    """The index mapping and the choice of word 0, worked by hand from the
+    generator's first known-answer vector (tests/golden/random_start_forms.json)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "random_start_forms.json")) as fh:
+        g = json.load(fh)
+    for case in g["cases"]:
+        off = np.array([0, case["n"]], np.int64)
+        assert oracle_mod.random_start(off, g["seed"], g["step"])[0] == case["start"], case
+
+
+# Philox4x32-10 written again from its definition in Salmon, Moraes, Dror and
+# Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011), with Python
+# integers: each round takes the two 32x32-bit products of counter words 0
+# and 2, crosses their high halves with words 1 and 3 and the round key, and
+# the key advances by the two Weyl constants after every round.
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+
+
+def _philox_py(ctr, key):
+    c = [int(v) for v in ctr]
+    k = [int(v) for v in key]
+    for _ in range(10):
+        p0, p1 = _PHILOX_M[0] * c[0], _PHILOX_M[1] * c[2]
+        c = [(p1 >> 32) ^ c[1] ^ k[0], p1 & 0xFFFFFFFF, (p0 >> 32) ^ c[3] ^ k[1], p0 & 0xFFFFFFFF]
+        k = [(k[0] + _PHILOX_W[0]) & 0xFFFFFFFF, (k[1] + _PHILOX_W[1]) & 0xFFFFFFFF]
+    return c
+
+
+def test_random_start_counter_layout(oracle_mod):
+    """Event index in counter words 0-1, step in words 2-3 (its high word
+    non-zero), seed in the key (both words non-zero): the oracle against the
+    independent Python generator above, which is itself checked against the
+    published known-answer vectors first."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")) as fh:
+        for v in json.load(fh)["vectors"]:
+            assert _philox_py([int(h, 16) for h in v["counter"]],
+                              [int(h, 16) for h in v["key"]]) == [int(h, 16) for h in v["out"]]
+    rng = np.random.default_rng(11)
+    n = rng.integers(1, 100000, 300).astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(n)])
+    for seed, step in ((0x299F31D0A4093822, (7 << 32) + 3), (5, 2**64 - 1), (2**63 + 1, 1 << 40)):
+        s = oracle_mod.random_start(off, seed, step)
+        for b in (0, 1, 2, 17, 255, 299):
+            w0 = _philox_py([b & 0xFFFFFFFF, b >> 32, step & 0xFFFFFFFF, step >> 32],
+                            [seed & 0xFFFFFFFF, seed >> 32])[0]
+            assert s[b] == (w0 * int(n[b])) >> 32, (seed, step, b)

@@ -175,7 +175,7 @@ class Runner:
     def timed(self, steps, warmup):
         """K host-launched steps with a HIP event pair around each (on the
         stream the kernels run on).  Returns (wall seconds, mean step seconds
-        on the GPU)."""
+        on the GPU, the K step durations in seconds)."""
         import torch
 
         for _ in range(warmup):
@@ -190,8 +190,35 @@ class Runner:
             evs[s][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        gpu = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e-3 / steps
-        return wall, gpu
+        per = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+        return wall, sum(per) / steps, per
+
+    def pool_flushed(self, reps, flush_mib=512):
+        """fpstok_pool alone, `reps` times after one sampling call, with a
+        write of flush_mib MiB before each so that the 256 MB infinity cache
+        holds none of the inputs; a HIP event pair around each pool call.
+        Returns the mean seconds per call."""
+        import torch
+
+        F, t, o = self.F, self.tok, self.tok.out
+        F.sample(t.bt, t.pr, o["centroid_idx"], o["centroids"], o["token_count"], o["assign"],
+                 t.ws)
+        if t.pr.lloyd_iters > 0:
+            F.lloyd(t.bt, t.pr, o["centroids"], o["token_count"], o["assign"], t.ws)
+        if t.mode == F.KNN:
+            F.knn(t.bt, t.pr, o["centroids"], o["token_count"], o["knn_idx"], t.ws)
+        junk = torch.empty(flush_mib << 18, dtype=torch.float32, device=self.x.device)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for r in range(reps):
+            junk.fill_(float(r))
+            evs[r][0].record()
+            F.pool(t.bt, t.pr, o["token_count"], o["assign"], o["knn_idx"], o["pooled"],
+                   o["cell_count"], t.ws)
+            evs[r][1].record()
+        torch.cuda.synchronize()
+        del junk
+        return sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e-3 / reps
 
     def per_call(self, steps):
         """Mean duration of each of the five calls (stepwise path)."""
@@ -262,26 +289,96 @@ def time_next(b, reps=50):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else the platform string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_threads(cap=16):
+    """Host threads this process may use (its CPU affinity), at most `cap`
+    (the CPU share of one GPU on the measurement boxes)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, cap))
+
+
 def cpu_baseline(b, budget_s):
-    """The oracle as it stands, single-threaded, on repeats of the same batch
-    until about budget_s seconds of CPU work."""
+    """The oracle as it stands on the host, on repeats of the same batch:
+    (1) one thread, the whole batch per call, for about budget_s seconds;
+    (2) event-parallel: the events dealt to a pool of host threads, largest
+    cost n (P - 1) first, each to the thread with the least work so far; each
+    thread's events are gathered into one sub-batch once, and every repeat is
+    one oracle call per thread (the oracle releases the interpreter lock while
+    it runs), for about budget_s / 2 seconds.  The oracle's per-event code is
+    the same in both legs; only the driver differs.  Returns the
+    event-parallel leg with the single-thread one nested."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
     kw = dict(P=b["P"], mode=b["mode"], k=b["k"], L=b["L"], weighted=b["weighted"],
               charge_col=b["charge_col"])
-    oracle.tokenize(b["coords"], b["features"], b["offsets"], **kw)  # load + warm
+    x, f, off = b["coords"], b["features"], b["offsets"]
+    B = off.size - 1
+    oracle.tokenize(x, f, off, **kw)  # load + warm
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.tokenize(b["coords"], b["features"], b["offsets"], **kw)
+        oracle.tokenize(x, f, off, **kw)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    B = b["offsets"].size - 1
-    return dict(value=B * reps / el, unit="events/s", cores=1, kind="oracle",
-                sample="%d repeats of the same %d-event batch (%.1f s, one host thread)" % (
-                    reps, B, el))
+    single = dict(value=B * reps / el, unit="events/s", cores=1, kind="oracle",
+                  sample="%d repeats of the same %d-event batch (%.1f s, one host thread)" % (
+                      reps, B, el))
+    # event-parallel leg: longest-processing-time-first dealing of the events
+    n = np.diff(off)
+    cost = np.where(n > b["P"], n * (b["P"] - 1), n).astype(np.int64)
+    nt = min(host_threads(), max(1, B))
+    load = [0] * nt
+    mine = [[] for _ in range(nt)]
+    for e in sorted(range(B), key=lambda e: -int(cost[e])):
+        t = load.index(min(load))
+        mine[t].append(e)
+        load[t] += int(cost[e]) + 1
+    subs = []
+    for evs in mine:
+        evs = sorted(evs)
+        if not evs:
+            continue
+        xe = np.concatenate([x[off[e]:off[e + 1]] for e in evs])
+        fe = np.concatenate([f[off[e]:off[e + 1]] for e in evs])
+        oe = np.concatenate([[0], np.cumsum(n[evs])]).astype(np.int64)
+        subs.append((xe, fe, oe))
+
+    def one(sb):
+        oracle.tokenize(sb[0], sb[1], sb[2], **kw)
+
+    reps_p = 0
+    with ThreadPoolExecutor(max_workers=len(subs)) as ex:
+        list(ex.map(one, subs))  # warm
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(one, subs))
+            reps_p += 1
+            elp = time.perf_counter() - t0
+            if elp >= budget_s / 2:
+                break
+    nt = len(subs)
+    return dict(value=B * reps_p / elp, unit="events/s", cores=nt, kind="oracle",
+                sample="%d repeats of the same %d-event batch, its events dealt to %d host "
+                       "threads, one oracle call per thread (%.1f s)" % (reps_p, B, nt, elp),
+                cpu=cpu_model(), single_thread=single)
 
 
 def measured_traffic(workload):
@@ -295,6 +392,24 @@ def measured_traffic(workload):
     if workload != MEASURED_TRAFFIC["workload"] or sha != MEASURED_TRAFFIC["kernels_sha256"]:
         return None
     return MEASURED_TRAFFIC["bytes"]
+
+
+def percentiles_us(per_step_s):
+    """p10 / median / p90 of per-step durations, in microseconds."""
+    a = np.asarray(per_step_s) * 1e6
+    return dict(p10=float(np.percentile(a, 10)), p50=float(np.percentile(a, 50)),
+                p90=float(np.percentile(a, 90)), n=int(a.size))
+
+
+def pool_roofline(st, seconds, b):
+    """HBM roofline of one fpstok_pool call (the infinity cache flushed before
+    it): algorithmic bytes (features and slot of every pulse read, pooled row
+    and member count of every slot written) over its duration."""
+    ach = st["pool_bytes"] / seconds / 1e9
+    kind = "kNN" if b["mode"] == 1 else "Voronoi"
+    return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
+                frac=ach / HBM_PEAK_GBPS, traffic=None, us=seconds * 1e6,
+                kernel="fpstok_pool call (%s), infinity cache flushed before each call" % kind)
 
 
 def fps_roofline(st, seconds, kernel, traffic=None):
@@ -349,7 +464,7 @@ def main():
     r = Runner(b)
     # per-step GPU time: a HIP event pair around each of K host-launched
     # steps, on the stream the kernels run on
-    _, step_gpu = r.timed(args.steps, args.warmup)
+    _, step_gpu, step_list = r.timed(args.steps, args.warmup)
     wall, mode, walls = r.timed_launch(args.steps, args.warmup, args.launch)
     ms = wall / args.steps * 1e3
     value = st["B"] * args.steps / wall
@@ -379,13 +494,15 @@ def main():
             s2 = workload_stats(bb)
             steps = 20 if s2["N"] > 1_000_000 else 100
             rr = Runner(bb)
-            _, g2 = rr.timed(steps, 5)
+            _, g2, l2 = rr.timed(steps, 5)
             w2, mode2, _ = rr.timed_launch(steps, 5, args.launch)
             pc2 = rr.per_call(max(5, steps // 4))
+            pool_s = rr.pool_flushed(10)
             secondary[name] = dict(
                 events_per_s=s2["B"] * steps / w2, ms_per_step=w2 / steps * 1e3, launch=mode2,
-                step_gpu_us=g2 * 1e6,
+                step_gpu_us=g2 * 1e6, step_gpu_us_pct=percentiles_us(l2),
                 per_call_us={c: v * 1e6 for c, v in pc2.items()},
+                pool_roofline=pool_roofline(s2, pool_s, bb),
                 fps_point_iters_per_s=s2["point_iters"] / pc2["sample"],
                 pool_GBps=s2["pool_bytes"] / pc2["pool"] / 1e9, B=s2["B"], N=s2["N"],
                 P=s2["P"])
@@ -418,14 +535,15 @@ def main():
                    "seed": b["seed"], "max_event_points": r.max_n, "launch": mode},
         "events_per_s_by_launch": {m: st["B"] * args.steps / w for m, w in walls.items()},
         "step_gpu_us": step_gpu * 1e6,
+        "step_gpu_us_pct": percentiles_us(step_list),
         "fps_point_iters_per_s": st["point_iters"] / step_gpu,
         "per_call_us": {c: v * 1e6 for c, v in per_call.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
         "secondary": secondary,
         "next": nxt,
-        "host": {"cpu": platform.processor() or platform.machine(),
-                 "nproc": os.cpu_count(), "gpu": torch.cuda.get_device_name(0)},
+        "host": {"cpu": cpu_model(), "nproc": os.cpu_count(), "threads": host_threads(),
+                 "gpu": torch.cuda.get_device_name(0)},
     }
     print(json.dumps(line), flush=True)
 

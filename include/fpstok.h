@@ -200,6 +200,27 @@ fpstok_status fpstok_tokenize(const fpstok_batch* batch, const fpstok_params* pa
                               float* pooled, int32_t* cell_count, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph or
+ * stream capture, tight serving loops, harnesses that forbid allocation):
+ * fpstok_tokenize with the same arguments and results, but no workspace.
+ * Its workspace is a fixed scratch region of FPSTOK_NOALLOC_MAX_WORKSPACE
+ * bytes in the library's device memory, one per GPU, held by every GPU the
+ * library runs on until the process ends; the call allocates and frees
+ * nothing.  Every call on one GPU uses that GPU's region (the kernels leave
+ * in it what the last call wrote and clear what must start at zero), so calls
+ * that overlap in time on one GPU -- from several streams or host threads --
+ * race and must be serialized by the caller.  `stream` must belong to the
+ * current device (NULL: the legacy default stream).
+ * Errors: as fpstok_tokenize; EUNSUPPORTED when the batch needs more than
+ * FPSTOK_NOALLOC_MAX_WORKSPACE bytes of workspace (fpstok_workspace_size;
+ * nothing is enqueued); EINVAL when the stream is on another device. */
+#define FPSTOK_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+fpstok_status fpstok_tokenize_noalloc(const fpstok_batch* batch, const fpstok_params* params,
+                                      const int32_t* start_idx, int32_t* centroid_idx,
+                                      float* centroids, int32_t* token_count, int32_t* assign,
+                                      int32_t* knn_idx, float* pooled, int32_t* cell_count,
+                                      void* stream);
+
 /* ------------------------------------------------ next to the path -- */
 
 /* Packing of every event's tokens into one variable-length sequence for

@@ -41,6 +41,7 @@ static fpstok_status hip_fail(hipError_t e, const char* what) {
 }
 
 static_assert(kKnnMaxK == FPSTOK_MAX_K, "kNN list bound");
+static_assert(kNoAllocBytes == FPSTOK_NOALLOC_MAX_WORKSPACE, "scratch region size");
 
 // Polls before a wait between workgroups gives up (fpstok_debug_set_spin_limit).
 static std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
@@ -496,7 +497,7 @@ FPSTOK_API fpstok_status fpstok_random_start(const int64_t* offsets, int64_t num
     return ok();
 }
 
-// Argument checks of fpstok_tokenize, the workspace aside.
+// Argument checks of fpstok_tokenize and fpstok_tokenize_noalloc, the workspace aside.
 static fpstok_status check_tokenize(const fpstok_batch* bt, const fpstok_params* pr,
                                     int32_t* centroid_idx, float* centroids,
                                     int32_t* token_count, int32_t* assign, int32_t* knn_idx,
@@ -584,6 +585,41 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     if (bt->num_events == 0) return ok();
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    return run_tokenize(bt, pr, start_idx, centroid_idx, centroids, token_count, assign, knn_idx,
+                        pooled, cell_count, ws, L, stream);
+}
+
+FPSTOK_API fpstok_status fpstok_tokenize_noalloc(const fpstok_batch* bt, const fpstok_params* pr,
+                                                 const int32_t* start_idx, int32_t* centroid_idx,
+                                                 float* centroids, int32_t* token_count,
+                                                 int32_t* assign, int32_t* knn_idx, float* pooled,
+                                                 int32_t* cell_count, void* stream) {
+    fpstok_status st = check_tokenize(bt, pr, centroid_idx, centroids, token_count, assign,
+                                      knn_idx, pooled);
+    if (st != FPSTOK_OK) return st;
+    if (bt->num_events == 0) return ok();
+    const WorkspaceLayout L = workspace_layout(bt->num_events, bt->num_points, pr->num_patches,
+                                               bt->num_features > 0 ? bt->num_features : 1);
+    if (L.total > kNoAllocBytes)
+        return fail(FPSTOK_EUNSUPPORTED,
+                    "this batch needs %zu bytes of workspace; the no-allocation scratch region "
+                    "holds %zu (use fpstok_tokenize with a caller workspace)",
+                    L.total, kNoAllocBytes);
+    hipStream_t s = (hipStream_t)stream;
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (s) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(s, &sd);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if ((int)sd != cur)
+            return fail(FPSTOK_EINVAL, "the stream belongs to device %d, the current device is %d",
+                        (int)sd, cur);
+    }
+    void* ws = nullptr;
+    e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "looking up the scratch region");
     return run_tokenize(bt, pr, start_idx, centroid_idx, centroids, token_count, assign, knn_idx,
                         pooled, cell_count, ws, L, stream);
 }

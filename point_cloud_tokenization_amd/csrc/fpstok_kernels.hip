@@ -14,6 +14,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "fpstok_internal.h"
 
@@ -3315,6 +3316,38 @@ __global__ __launch_bounds__(256) void random_start_kernel(const int64_t* __rest
     const uint32_t u = philox_word0((uint32_t)b, (uint32_t)((uint64_t)b >> 32), (uint32_t)step,
                                     (uint32_t)(step >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
     start_idx[b] = n > 0 ? (int32_t)(((uint64_t)u * (uint64_t)n) >> 32) : 0;
+}
+
+// ------------------------------------------- no-allocation scratch region
+
+// The workspace of fpstok_tokenize_noalloc, for callers that cannot allocate
+// device memory: one fixed region per GPU, a file-scope device array that
+// every GPU the library runs on holds until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in for
+// the symbol): noalloc_scratch looks the device address up with
+// hipGetSymbolAddress once per device, with that device current, and every
+// launch takes that address.
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* by_device[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!by_device[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+        by_device[dev] = p;
+    }
+    *ptr = by_device[dev];
+    return hipSuccess;
 }
 
 // ------------------------------------------------------------------ launchers

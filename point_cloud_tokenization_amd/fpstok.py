@@ -18,6 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fpstok.h")
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP, EDEVICE = 0, 1, 2, 3, 4, 5
 VORONOI, KNN = 0, 1
 MAX_PATCHES, MAX_K, MAX_LLOYD = 1024, 64, 1000
+NOALLOC_MAX_WORKSPACE = 64 << 20  # FPSTOK_NOALLOC_MAX_WORKSPACE
 
 
 class FpstokError(RuntimeError):
@@ -65,6 +66,7 @@ def lib():
         L.fpstok_lloyd.argtypes = [B, Pp, vp, vp, vp, vp, sz, vp]
         L.fpstok_pool.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fpstok_tokenize.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fpstok_tokenize_noalloc.argtypes = [B, Pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.fpstok_validate.argtypes = [B, vp]
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         L.fpstok_pack.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -77,7 +79,7 @@ def lib():
         for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
                   "fpstok_pool", "fpstok_tokenize", "fpstok_validate", "fpstok_pack",
                   "fpstok_unpack", "fpstok_pool_backward", "fpstok_random_start",
-                  "fpstok_device_status"):
+                  "fpstok_device_status", "fpstok_tokenize_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.fpstok_status_string.argtypes = [ctypes.c_int]
         L.fpstok_status_string.restype = ctypes.c_char_p
@@ -265,6 +267,17 @@ def tokenize_call(bt, pr, centroid_idx, centroids, token_count, assign_, knn_idx
                                  _ptr(centroid_idx), _ptr(centroids), _ptr(token_count),
                                  _ptr(assign_), _ptr(knn_idx), _ptr(pooled), _ptr(cell_count),
                                  _ptr(ws), ws.numel(), _stream_handle(stream)), "fpstok_tokenize")
+
+
+def tokenize_noalloc_call(bt, pr, centroid_idx, centroids, token_count, assign_, knn_idx,
+                          pooled, cell_count, start_idx=None, stream=None):
+    """fpstok_tokenize_noalloc: the whole tokenizer with the library's fixed
+    scratch region as its workspace (no allocation)."""
+    _check(lib().fpstok_tokenize_noalloc(ctypes.byref(bt), ctypes.byref(pr), _ptr(start_idx),
+                                         _ptr(centroid_idx), _ptr(centroids), _ptr(token_count),
+                                         _ptr(assign_), _ptr(knn_idx), _ptr(pooled),
+                                         _ptr(cell_count), _stream_handle(stream)),
+           "fpstok_tokenize_noalloc")
 
 
 def validate(bt, stream=None):

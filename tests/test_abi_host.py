@@ -136,6 +136,23 @@ def test_other_calls_reject_bad_arguments(L):
                          None) == F.EINVAL
 
 
+def test_noalloc_rejects_batches_beyond_its_scratch_region(L):
+    """The size check comes before any HIP call: a batch whose workspace is
+    larger than the fixed region is refused with nothing enqueued."""
+    pr = F.make_params(num_patches=1024)
+    big = _bt(B=100, N=3_000_000)
+    assert F.workspace_size(big, pr) > F.NOALLOC_MAX_WORKSPACE
+    args = (None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None)
+    assert L.fpstok_tokenize_noalloc(ctypes.byref(big), ctypes.byref(pr), *args) == \
+        F.EUNSUPPORTED
+    assert b"scratch region" in L.fpstok_last_error()
+    # argument errors are still found first
+    assert L.fpstok_tokenize_noalloc(ctypes.byref(big), ctypes.byref(pr), None, None, FAKE, FAKE,
+                                     FAKE, None, FAKE, None, None) == F.EINVAL
+    empty = _bt(B=0, N=0)
+    assert L.fpstok_tokenize_noalloc(ctypes.byref(empty), ctypes.byref(pr), *args) == F.OK
+
+
 def test_device_status_rejects_bad_workspace(L):
     assert L.fpstok_device_status(None, 1 << 20, None) == F.EINVAL
     assert L.fpstok_last_error() != b""

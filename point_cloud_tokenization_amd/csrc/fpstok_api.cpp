@@ -67,8 +67,6 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     at += align256((size_t)L.max_pool_chunks * sizeof(int32_t));
     L.chunk_part = at;
     at += align256((size_t)L.max_pool_chunks * sizeof(int32_t));
-    L.ev_cnt = at;
-    at += align256((size_t)B * sizeof(int32_t));
     L.big_ev = at;
     at += align256(2 * (size_t)B * sizeof(int32_t));
     L.mind = at;
@@ -207,17 +205,15 @@ static PoolArgs pool_args(const fpstok_batch* bt, const fpstok_params* pr,
     a.chunk_ev = at<int32_t>(ws, L.pool_ev);
     a.chunk_beg = at<int32_t>(ws, L.pool_beg);
     a.chunk_part = at<int32_t>(ws, L.chunk_part);
-    a.ev_cnt = at<int32_t>(ws, L.ev_cnt);
     a.big_ev = at<int32_t>(ws, L.big_ev);
     a.B = bt->num_events;
-    // the combine kernel's blocks hold one thread per (field, slot)
-    // events of more than kCombLast chunks are finished by the combine
-    // kernel; when the caller's bound on event size rules them out, the
-    // last chunk of every event finishes it (still correct if the bound is
-    // wrong) and the combine kernel is not launched
-    const bool no_big = bt->max_event_points > 0 &&
-                        bt->max_event_points <= (int64_t)kCombLast * kPoolChunk;
-    a.comb_last = bt->num_features + 2 <= 256 && !no_big ? kCombLast : (1 << 30);
+    // events of more than one chunk are finished by the combine kernel, whose
+    // blocks hold one thread per (field, slot); when the caller's bound on
+    // event size rules them out the combine kernel is not launched, and an
+    // event that breaks the bound is summed whole by its first chunk's
+    // workgroup (slower, still correct)
+    const bool no_big = bt->max_event_points > 0 && bt->max_event_points <= kPoolChunk;
+    a.whole = no_big || bt->num_features + 2 > 256 ? 1 : 0;
     a.part = at<double>(ws, L.part);
     return a;
 }
@@ -399,7 +395,7 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (pr->assign_mode == FPSTOK_VORONOI) {
-        e = launch_plan_pool(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
+        e = launch_plan_pool(bt->offsets, bt->num_events, bt->num_points, ws, L, a.whole, s);
         if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
     }
     e = run_pool(bt, pr, a, L, s);

@@ -18,9 +18,10 @@ constexpr int kChunk = 64;
 // workgroup does in LDS.
 constexpr int kPoolChunk = 4096;
 
-// Events of at most this many pooling chunks are finished by the workgroup
-// of their last chunk; larger ones by a separate combine kernel.
-constexpr int kCombLast = 4;
+// A chunk of an event of more than one pooling chunk writes a record of
+// per-slot float64 partial sums, and a separate combine kernel adds the
+// records of each such event in chunk order: the kernel boundary publishes
+// the records (no fence inside the pooling kernels).
 
 // 64-bit words of one gang exchange record (one shard, one parity): 64
 // candidate entries of one word each, the shard's bound, padding.
@@ -42,9 +43,8 @@ struct WorkspaceLayout {
     size_t pool_ev;     // int32[max_pool_chunks]: event of each pooling chunk
     size_t pool_beg;    // int32[max_pool_chunks]: first event-local pulse of each pooling chunk
     size_t chunk_part;  // int32[max_pool_chunks]: partial-sum record of each pooling chunk
-    size_t ev_cnt;      // int32[B]: chunks of each event done so far (pooling)
-    size_t big_ev;      // int32[2][B]: events of more than kCombLast chunks and their first
-                        // record (pooling)
+    size_t big_ev;      // int32[2][B]: events of more than one pooling chunk and their first
+                        // record
     size_t mind;        // float[N]: running min distance (large-event FPS)
     size_t near;        // int32[N]: running nearest slot (large-event FPS, no assign out)
     size_t perm;        // int32[N]: pulses sorted by token (Lloyd, pool)
@@ -180,15 +180,17 @@ struct PoolArgs {
     float* pooled;
     int32_t* cell_count;
     int32_t* perm;
-    int32_t* header;            // chunked pooling: [4] events of > kCombLast chunks, [6] chunks
+    int32_t* header;            // chunked pooling: [4] events of > 1 chunk, [6] chunks
     const int32_t* chunk_ev;    // chunked pooling: event of each chunk
     const int32_t* chunk_beg;   // chunked pooling: first event-local pulse of each chunk
-    const int32_t* chunk_part;  // chunked pooling: record of each chunk (-1: one-chunk event)
-    int32_t* ev_cnt;            // chunked pooling: finished chunks per event
+    const int32_t* chunk_part;  // chunked pooling: record of each chunk (-1: one-chunk event,
+                                // -2: the event is summed whole by its first chunk)
     const int32_t* big_ev;      // chunked pooling: [m] event, [B + m] first record, m < header[4]
     int64_t B;                  // chunked pooling: events
-    int comb_last;              // chunked pooling: events of at most this many chunks are
-                                // finished by their last chunk's workgroup
+    int whole;                  // chunked pooling: 1 when the caller's bound on event size
+                                // rules out events of more than one chunk: any such event
+                                // is summed whole by its first chunk (no records, no
+                                // combine kernel)
     double* part;               // chunked pooling: [max_parts][P][C+2] partial sums
     int stage_cap;              // fused pooling: feature floats an event may stage in LDS
 };
@@ -197,10 +199,10 @@ struct PoolArgs {
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
                        const WorkspaceLayout& L, hipStream_t s);
 // Pooling chunk list (kPoolChunk pulses per chunk, largest first), the
-// chunks' partial-sum records, cleared per-event counters and the list of
-// events for the combine kernel.
+// chunks' partial-sum records and the list of events for the combine kernel
+// (whole: every event of more than one chunk is summed by its first chunk).
 hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                            const WorkspaceLayout& L, hipStream_t s);
+                            const WorkspaceLayout& L, int whole, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
 // The work lists of a sample -> Lloyd (`chunks`) -> Voronoi pool (`pool`)
 // sequence in one launch; then launch_sample_items runs the FPS without

@@ -123,6 +123,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// Inclusive prefix sum over the wave with DPP: shifts of 1, 2, 4 and 8
+// lanes inside each row of 16 (lanes without a source add 0), then the row
+// totals carried into the later rows by the two row broadcasts.
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, kRowShr1, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kRowShr2, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kRowShr4, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kRowShr8, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
 // Lowest pulse index not yet selected, from a per-lane 32-bit slice of the
 // selection bitmap (lane l holds indices 32l .. 32l+31).  The caller
 // guarantees such an index exists below 2048.
@@ -189,13 +206,14 @@ __device__ __forceinline__ void plan_chunks(const int64_t* __restrict__ offsets,
 // event's last, partial chunk (an empty event gets one empty chunk), so that
 // the long chunks start before the short ones.  The chunks of an event of
 // more than one chunk get consecutive partial-sum records (-1: the event is
-// one chunk), ev_cnt is cleared, and the events of more than kCombLast
-// chunks are listed in big_ev with their first record (count in header[4];
-// the chunk count goes to header[6]).
+// one chunk) and the event is listed in big_ev with its first record for the
+// combine kernel (count in header[4]; the chunk count goes to header[6]).
+// With `whole`, an event of more than one chunk gets no records instead and
+// is marked -2: summed whole by its first chunk.
 // Malformed (overlapping) offsets can ask for more chunks or records than
 // the lists hold: extra chunks are dropped, an event without room for its
-// records is marked -2 (summed whole by its first chunk), and a listed event
-// without room is listed as -1; nothing is written out of bounds.
+// records is marked -2 too, and a listed event without room is listed as -1;
+// nothing is written out of bounds.
 __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                                                          int64_t B, int64_t N, int64_t max_chunks,
                                                          int64_t max_parts,
@@ -203,8 +221,8 @@ __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                                                          int32_t* __restrict__ chunk_ev,
                                                          int32_t* __restrict__ chunk_beg,
                                                          int32_t* __restrict__ chunk_part,
-                                                         int32_t* __restrict__ ev_cnt,
-                                                         int32_t* __restrict__ big_ev) {
+                                                         int32_t* __restrict__ big_ev,
+                                                         int whole) {
     __shared__ int s_sum[3][16];
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -222,12 +240,11 @@ __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                 event_range(offsets, N, b, off, n);
                 nf = n / kPoolChunk;
                 tl = n % kPoolChunk != 0 || n == 0 ? 1 : 0;
-                if (pass == 0) ev_cnt[b] = 0;
             }
             const int nch = nf + tl;
             const int cnt = pass == 0 ? nf : tl;  // chunks this pass places
-            const int np = nch > 1 ? nch : 0;
-            const int nb = pass == 0 && nch > kCombLast ? 1 : 0;
+            const int np = nch > 1 && !whole ? nch : 0;
+            const int nb = pass == 0 && np > 0 ? 1 : 0;
             const int v[3] = {cnt, np, nb};
             int incl[3], pre[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
 #pragma unroll
@@ -250,7 +267,7 @@ __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                 const int k = pass == 0 ? c : nf;  // chunk number inside the event
                 chunk_ev[pos + c] = (int32_t)b;
                 chunk_beg[pos + c] = k * kPoolChunk;
-                chunk_part[pos + c] = nch == 1 ? -1 : (room ? (int)(ppos + k) : -2);
+                chunk_part[pos + c] = nch == 1 ? -1 : (room && !whole ? (int)(ppos + k) : -2);
             }
             if (nb) {
                 const int m = bcarry + pre[2] + incl[2] - 1;
@@ -284,10 +301,9 @@ __global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restri
                                                          int32_t* __restrict__ chunk_ev,
                                                          int32_t* __restrict__ chunk_beg,
                                                          int32_t* __restrict__ chunk_part,
-                                                         int32_t* __restrict__ ev_cnt,
-                                                         int32_t* __restrict__ big_ev) {
+                                                         int32_t* __restrict__ big_ev, int whole) {
     plan_pool(offsets, B, N, max_chunks, max_parts, header, chunk_ev, chunk_beg, chunk_part,
-              ev_cnt, big_ev);
+              big_ev, whole);
 }
 
 // ---------------------------------------------------------------------- FPS
@@ -1294,8 +1310,8 @@ __global__ __launch_bounds__(1024) void plan_all_kernel(SampleArgs a, int64_t B,
         __syncthreads();
         plan_pool(a.offsets, B, a.N, max_pool_chunks, max_parts, pa.header,
                   const_cast<int32_t*>(pa.chunk_ev), const_cast<int32_t*>(pa.chunk_beg),
-                  const_cast<int32_t*>(pa.chunk_part), pa.ev_cnt,
-                  const_cast<int32_t*>(pa.big_ev));
+                  const_cast<int32_t*>(pa.chunk_part), const_cast<int32_t*>(pa.big_ev),
+                  pa.whole);
     }
 }
 
@@ -2247,75 +2263,189 @@ __device__ __forceinline__ void pool_identity(const PoolArgs& a, int64_t b, int6
     }
 }
 
-constexpr int kCombU = 4;  // chunk records whose loads are issued together
+// ------------------------------ Voronoi pooling by chunks, counting sort
 
-// The means of event b from the records of its K chunks (first record
-// p0): one thread per slot adds the records in chunk order, kCombU chunks'
-// loads in flight.
-__device__ __forceinline__ void pool_combine_records(const PoolArgs& a, int64_t b, int T, int K,
-                                                     int p0) {
+// Orders this wave's LDS accesses before and after it (the wave's LDS
+// operations complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Stable counting sort of one chunk's pulses by slot, in LDS:
+// perm[off_[j] + r] = the r-th pulse (ascending) of the chunk with slot j.
+//  1. every wave counts the slots of its contiguous quarter of the chunk
+//     with LDS atomics (the order of the counts does not matter);
+//  2. an exclusive scan over the slots, then per (wave, slot) the first
+//     position of that wave's members of the slot;
+//  3. every wave walks its quarter 64 pulses at a time in ascending order:
+//     each pulse sets its lane's bit in its wave's 64-bit mask of its slot
+//     (an LDS atomic OR), reads the mask back -- the lanes below it with
+//     its slot give its rank -- and lands at the slot's cursor plus that
+//     rank; the slot's lowest lane then advances the cursor and clears the
+//     mask.  Waves touch only their own cursors and masks, and a wave's LDS
+//     operations complete in order, so no barrier is needed inside the walk.
+//   k: LDS int[len] slots (outside [0, T): left out);  perm: LDS int[len];
+//   cnt: LDS int[4 * T];  off_: LDS int[T + 1];  bm: LDS uint64[4 * T], zero
+//   on entry and on return.
+__device__ __forceinline__ void chunk_sort(const int* k, int len, int T, int* perm, int* cnt,
+                                           int* off_, unsigned long long* bm) {
+    __shared__ int s_ws[kSortW];
     const int tid = threadIdx.x;
-    const int P = a.P;
-    const int C = a.C;
-    const int C2 = C + 2;
-    const double* __restrict__ rec0 = a.part + (size_t)p0 * P * C2;
-    const size_t stride = (size_t)P * C2;
-    for (int j = tid; j < P; j += kSortT) {
-        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-            const int nc = min(kPoolCols, C - c0);
-            double W = 0.0, M = 0.0, S[kPoolCols];
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int q = ((len + kSortW - 1) / kSortW + 63) & ~63;  // pulses per wave, whole windows
+    const int qb = wave * q, qe = min(len, qb + q);
+    int* __restrict__ wc = cnt + wave * T;
+    unsigned long long* __restrict__ wm = bm + wave * T;
+    for (int i = qb + lane; i < qe; i += 64) {
+        const int kk = k[i];
+        if ((unsigned)kk < (unsigned)T) atomicAdd(&wc[kk], 1);
+    }
+    __syncthreads();
+    // slot totals and their exclusive scan (thread t: slots t*per ..)
+    const int per = (T + kSortT - 1) / kSortT;
+    int loc[kMaxP / kSortT];
+    int local = 0;
 #pragma unroll
-            for (int q = 0; q < kPoolCols; ++q) S[q] = 0.0;
-            for (int k0 = 0; j < T && k0 < K; k0 += kCombU) {
-                double w4[kCombU], m4[kCombU], s4[kCombU][kPoolCols];
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        int t = 0;
+        if (r < per && jj < T)
 #pragma unroll
-                for (int u = 0; u < kCombU; ++u) {
-                    if (k0 + u < K) {
-                        const double* __restrict__ r = rec0 + (k0 + u) * stride + (size_t)j * C2;
-                        w4[u] = r[0];
-                        m4[u] = r[C + 1];
+            for (int w = 0; w < kSortW; ++w) t += cnt[w * T + jj];
+        loc[r] = t;
+        local += t;
+    }
+    const int incl = wave_incl_scan(local);
+    if (lane == 63) s_ws[wave] = incl;
+    __syncthreads();
+    int run = incl - local, total = 0;
 #pragma unroll
-                        for (int q = 0; q < kPoolCols; ++q)
-                            if (q < nc) s4[u][q] = r[1 + c0 + q];
-                    }
-                }
+    for (int w = 0; w < kSortW; ++w) {
+        const int v = s_ws[w];
+        run += w < wave ? v : 0;
+        total += v;
+    }
 #pragma unroll
-                for (int u = 0; u < kCombU; ++u) {
-                    if (k0 + u < K) {
-                        W += w4[u];
-                        M += m4[u];
+    for (int r = 0; r < kMaxP / kSortT; ++r) {
+        const int jj = tid * per + r;
+        if (r < per && jj < T) {
+            off_[jj] = run;
+            int pos = run;
 #pragma unroll
-                        for (int q = 0; q < kPoolCols; ++q)
-                            if (q < nc) S[q] += s4[u][q];
-                    }
-                }
+            for (int w = 0; w < kSortW; ++w) {
+                const int v = cnt[w * T + jj];
+                cnt[w * T + jj] = pos;
+                pos += v;
             }
-            pool_write(a, b, j, c0, nc, W, S);
-            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = (int)M;
+        }
+        run += loc[r];
+    }
+    if (tid == 0) off_[T] = total;
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int t0 = qb; t0 < qe; t0 += 64) {
+        const int i = t0 + lane;
+        const int kk = i < qe ? k[i] : -1;
+        const bool ok = (unsigned)kk < (unsigned)T;
+        const int ks = ok ? kk : 0;
+        if (ok) atomicOr(&wm[ks], 1ull << lane);
+        wave_lds_order();
+        const unsigned long long m = wm[ks];
+        const int cur = wc[ks];
+        wave_lds_order();
+        const int rank = __popcll(m & below);
+        if (ok) perm[cur + rank] = i;
+        if (ok && rank == 0) {
+            wc[ks] = cur + __popcll(m);
+            wm[ks] = 0ull;
+        }
+        wave_lds_order();
+    }
+    __syncthreads();
+}
+
+// Columns [c0, c0 + NC) of one slot's (weighted) sums over its members
+// perm[mb .. me) (chunk-local pulses, ascending), rows gathered from device
+// memory kBatch members at a time; every load of a batch is issued before
+// any is used (indices past the slot re-read its last member, unused).
+template <int NC>
+__device__ __forceinline__ void chunk_slot_gather(const float* __restrict__ rows, int C, int wcol,
+                                                  const int* perm, int mb, int me, int c0,
+                                                  double& W, double (&S)[NC]) {
+    W = 0.0;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) S[q] = 0.0;
+    for (int m0 = mb; m0 < me; m0 += kBatch) {
+        int idx[kBatch];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) idx[t] = perm[min(m0 + t, me - 1)];
+        float wv[kBatch], fv[kBatch][NC];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+            const float* __restrict__ r = rows + (int64_t)idx[t] * C;
+            wv[t] = r[wcol >= 0 ? wcol : 0];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) fv[t][q] = r[c0 + q];
+        }
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+            if (m0 + t < me) {
+                const double wd = wcol >= 0 ? (double)wv[t] : 1.0;
+                W += wd;
+#pragma unroll
+                for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[t][q], S[q]);
+            }
         }
     }
 }
 
-// Voronoi pooling over the chunk list of kPoolChunk pulses per chunk.
-//  * An event of one chunk (every event of up to kPoolChunk pulses) is
-//    pooled whole by its workgroup: identity events pulse by pulse, others
-//    by a stable sort by slot in LDS and every slot's (weighted) mean of its
-//    members in ascending pulse order.
-//  * A chunk of a larger event sorts its own pulses the same way and writes
-//    float64 partial sums per slot (weight, every column, member count) to
-//    its record.  The workgroup that finishes the event's last chunk (a
-//    counter per event) adds the records in chunk order and writes the
-//    means: each record is an ascending sum, so only the grouping at chunk
-//    boundaries differs from one ascending sum.
-//  * An event the records have no room for (malformed offsets only) is
-//    pooled whole by its first chunk's workgroup through device memory.
-__global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
-    __shared__ int s_cnt[kSortW * kMaxP];
-    __shared__ int s_off[kMaxP + 1];
-    __shared__ int s_asg[kPoolChunk];
-    __shared__ int s_tmp[kPoolChunk];
-    __shared__ int s_last;
-    static_assert(kPoolChunk == kLdsPerm, "the slot sorts hold one chunk in LDS");
+// One column pass of a chunk: every slot's sums, then either the means of a
+// one-chunk event (slots j < P, zeros beyond T) or the chunk's record.
+template <int NC>
+__device__ __forceinline__ void chunk_pass_gather(const PoolArgs& a, int64_t b,
+                                                  const float* rows, int T, int c0,
+                                                  const int* perm, const int* off_, int part) {
+    const int P = a.P;
+    const int C = a.C;
+    const int C2 = C + 2;
+    for (int j = threadIdx.x; j < (part < 0 ? P : T); j += kSortT) {
+        const int mb = j < T ? off_[j] : 0, me = j < T ? off_[j + 1] : 0;
+        double W, S[NC];
+        chunk_slot_gather<NC>(rows, C, a.weight_col, perm, mb, me, c0, W, S);
+        if (part < 0) {
+            float* __restrict__ out = a.pooled + (b * P + j) * (int64_t)C + c0;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) out[q] = W != 0.0 ? (float)(S[q] / W) : 0.0f;
+            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = me - mb;
+        } else {
+            double* __restrict__ r = a.part + ((size_t)part * P + j) * C2;
+            r[0] = W;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) r[1 + c0 + q] = S[q];
+            if (c0 == 0) r[C + 1] = (double)(me - mb);
+        }
+    }
+}
+
+// Voronoi pooling over the chunk list (kPoolChunk pulses per chunk), one
+// workgroup per chunk:
+//  * an event whose slots are its pulses (n <= P) is pooled pulse by pulse;
+//  * otherwise the chunk's slots are copied to LDS and sorted there (stable
+//    counting sort, chunk_sort), and thread j sums slot j's members in
+//    ascending order with their rows gathered from device memory;
+//  * an event of one chunk writes its means; a chunk of a larger event
+//    writes its record (weight, every column, member count per slot) for
+//    the combine kernel;
+//  * an event marked to be summed whole (the caller's bound ruled it out, or
+//    malformed offsets left no record space) is sorted and summed by its
+//    first chunk's workgroup through device memory.
+// Dynamic LDS: int k[kPoolChunk], int perm[kPoolChunk], uint64 bm[4 * P],
+// int cnt[4 * P], int off[P + 1].
+__global__ __launch_bounds__(kSortT) void pool_chunk_kernel(PoolArgs a) {
+    extern __shared__ __align__(16) int s_dyn[];
     const int c = blockIdx.x;
     if (c >= a.header[6]) return;
     const int64_t b = a.chunk_ev[c];
@@ -2329,10 +2459,17 @@ __global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
     const int tid = threadIdx.x;
     const int P = a.P;
     const int C = a.C;
+    unsigned long long* bm = reinterpret_cast<unsigned long long*>(s_dyn);  // 4 * P
+    int* s_k = reinterpret_cast<int*>(bm + kSortW * P);                      // kPoolChunk
+    int* perm = s_k + kPoolChunk;                                            // kPoolChunk
+    int* cnt = perm + kPoolChunk;                                            // 4 * P
+    int* off_ = cnt + kSortW * P;                                            // P + 1
     if (part == -2) {
         if (beg != 0) return;
-        block_sort_by_token(a.assign + off, n, T, a.perm + off, s_cnt, s_off);
-        pool_slots_sorted(a, b, off, T, a.perm + off, s_off);
+        for (int q = tid; q < kSortW * P; q += kSortT) cnt[q] = 0;
+        __syncthreads();
+        block_sort_by_token(a.assign + off, n, T, a.perm + off, cnt, off_);
+        pool_slots_sorted(a, b, off, T, a.perm + off, off_);
         return;
     }
     if (part == -1) {
@@ -2344,245 +2481,363 @@ __global__ __launch_bounds__(kSortT) void pool_voronoi_kernel(PoolArgs a) {
         }
     }
     const int len = max(0, min(n - beg, kPoolChunk));
-    for (int i = tid; i < len; i += kSortT) s_asg[i] = a.assign[off + beg + i];
-    __syncthreads();
-    const int* perm = s_asg;
-    if (!block_sort_small(s_asg, len, T, s_tmp, s_cnt, s_off)) {
-        block_sort_by_token(s_asg, len, T, s_tmp, s_cnt, s_off);
-        perm = s_tmp;
-    }
-    if (part == -1) {
-        pool_slots_sorted(a, b, off, T, perm, s_off);
-        return;
-    }
-    // this chunk's record: per slot j < T, [W, S_0 .. S_{C-1}, count]
-    const int C2 = C + 2;
-    double* __restrict__ rec = a.part + (size_t)part * P * C2;
-    for (int j = tid; j < T; j += kSortT) {
-        const int mb = s_off[j], me = s_off[j + 1];
-        double W = 0.0;
-        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-            const int nc = min(kPoolCols, C - c0);
-            double S[kPoolCols];
-            pool_slot(a, off, mb, me, c0, nc, [&](int m) { return beg + perm[m]; }, W, S);
+    if (len > 0) {
+        // the chunk's slots, every load of a thread issued together
+        constexpr int R = kPoolChunk / kSortT;
+        int v[R];
+        const int32_t* __restrict__ ag = a.assign + off + beg;
 #pragma unroll
-            for (int q = 0; q < kPoolCols; ++q)
-                if (q < nc) rec[(size_t)j * C2 + 1 + c0 + q] = S[q];
-        }
-        rec[(size_t)j * C2] = W;
-        rec[(size_t)j * C2 + C + 1] = (double)(me - mb);
+        for (int r = 0; r < R; ++r) v[r] = ag[min(tid + kSortT * r, len - 1)];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (tid + kSortT * r < len) s_k[tid + kSortT * r] = v[r];
     }
-    // publish the record; the last chunk of the event to finish combines
-    // (events of more than comb_last chunks: the combine kernel)
-    const int K = (n + kPoolChunk - 1) / kPoolChunk;
-    if (K > a.comb_last) return;
-    __threadfence();
+    for (int q = tid; q < kSortW * T; q += kSortT) {
+        cnt[q] = 0;
+        bm[q] = 0ull;
+    }
     __syncthreads();
-    if (tid == 0)
-        s_last = __hip_atomic_fetch_add(a.ev_cnt + b, 1, __ATOMIC_ACQ_REL,
-                                        __HIP_MEMORY_SCOPE_AGENT) == K - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    pool_combine_records(a, b, T, K, part - beg / kPoolChunk);
+    chunk_sort(s_k, len, T, perm, cnt, off_, bm);
+    const float* __restrict__ rows = a.features + (off + beg) * (int64_t)C;
+    for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+        switch (min(kPoolCols, C - c0)) {
+#define FPSTOK_GATHER_PASS(NC) \
+    case NC: chunk_pass_gather<NC>(a, b, rows, T, c0, perm, off_, part); break;
+            FPSTOK_GATHER_PASS(1)
+            FPSTOK_GATHER_PASS(2)
+            FPSTOK_GATHER_PASS(3)
+            FPSTOK_GATHER_PASS(4)
+            FPSTOK_GATHER_PASS(5)
+            FPSTOK_GATHER_PASS(6)
+            FPSTOK_GATHER_PASS(7)
+            default: FPSTOK_GATHER_PASS(8)
+#undef FPSTOK_GATHER_PASS
+        }
+    }
 }
 
-// ------------------------------------ chunked pooling through LDS (P <= 256)
+// --------------- Voronoi pooling by chunks, rows sorted by slot into LDS
 
-constexpr int kPoolLdsMaxP = kSortT;  // one thread per slot
+constexpr int kSrtT = 512;               // threads of the sorting pooling kernel
+constexpr int kSrtW = kSrtT / 64;        // its waves
+constexpr int kSrtR = kPoolChunk / kSrtT;  // pulses per thread (8)
+constexpr int kSrtWave = 64 * kSrtR;       // pulses per wave
+constexpr int kSrtMaxP = 256;            // slots it handles (one per thread of the first waves)
+constexpr int kSrtMaxC = 6;              // widest rows it handles
+static_assert(kSrtR * kSrtT == kPoolChunk, "one pulse per thread and window");
 
-constexpr int kPreRows = 24;  // feature floats per thread held for the next piece
-constexpr int kLdsBatch = 4;  // members whose LDS rows are read together
-constexpr int kPreSlots = 4;  // slots per thread held for the next piece (pieces <= 1024)
-
-// Per-slot running sums of one chunk [beg, hi) of event b (thread j <-> slot
-// j < T), over the columns c0 .. c0+NC-1: the chunk is taken `sub` pulses
-// at a time; each piece's slots and feature rows are copied to LDS, sorted
-// by slot through bitmaps, and every slot's members of the piece are added
-// in ascending order from LDS, so each sum is one ascending sequence over
-// the chunk.  The next piece's loads are issued into registers before the
-// current piece is sorted and summed (sub * C <= 256 * kPreRows).
-//   s_asg: int[sub];  s_rows: float[(sub + 1) * C];  bm: uint32[T * sub / 32];
-//   pre4: int[T * sub / 128];  s_off: int[T + 1];  perm: int[sub]
+// Voronoi pooling over the chunk list (kPoolChunk pulses per chunk) for P
+// <= 256 and rows of at most 6 columns: one workgroup of 512 threads per
+// compute unit walks the chunks c = blockIdx, blockIdx + gridDim, ... and,
+// while it pools one, has the next one's slots and rows loading into
+// registers.  Wave w holds the chunk's pulses 512 w .. 512 w + 511 as eight
+// 64-pulse windows (lane l: pulses 512 w + 64 r + l), so the windows are in
+// pulse order wave after wave.  A chunk:
+//  1. every pulse counts its slot per wave (LDS atomics; order irrelevant);
+//  2. per slot, an exclusive scan gives the slot's first row; per (wave,
+//     slot), the first row of that wave's members;
+//  3. every wave ranks each window's pulses among their equal-slot lanes
+//     (each lane sets its bit in its wave's 64-bit mask of its slot, an LDS
+//     atomic OR, and reads the mask back: the lanes below it in the mask
+//     give its rank), writes each row to LDS at its wave's cursor plus that
+//     rank, and the slot's lowest lane advances the cursor and clears the
+//     mask: the rows of every slot land in ascending pulse order, one after
+//     the other;
+//  4. thread j adds slot j's rows -- contiguous in LDS -- in that order into
+//     float64 sums: each slot's chunk sum is one ascending sequence, the
+//     oracle's operations in the oracle's order.
+// Then an event of one chunk writes its means (0 beyond T; events whose slots
+// are their pulses, n <= P, are pooled pulse by pulse), a chunk of a larger
+// event writes its record for the combine kernel, and an event marked to be
+// summed whole (the caller's bound ruled it out, or malformed offsets left
+// no record space) is taken by its first chunk's workgroup sub-chunk after
+// sub-chunk, one ascending sum.  Every barrier orders LDS only, so the next
+// chunk's loads stay in flight across the chunk in hand, and the kernel has
+// no fence (the kernel boundary publishes the records).  The chunks'
+// descriptions (event, range, record, token count) are read 64 at a time
+// into LDS, so their chain of dependent loads is paid once per 64 chunks.
+// Dynamic LDS: float rows[kPoolChunk * NC], int cnt[kSrtW * P],
+// int off[P + 1], uint64 bm[kSrtW * P] (zero between chunks).
+constexpr int kSrtMeta = 64;  // chunk descriptions read at a time
+// Steps 1-3 above for one sub-chunk of at most kPoolChunk pulses (this
+// thread's pulses 512 wave + 64 r + lane: slots k[r], rows f[r]): the rows
+// land in LDS sorted by slot, slot j's at off_[j] .. off_[j + 1].  Ends with
+// a workgroup barrier; k and f are not needed afterwards.
 template <int NC>
-__device__ __forceinline__ void chunk_slot_sums(const PoolArgs& a, int64_t off, int beg, int hi,
-                                                int T, int c0, int sub, int* s_asg,
-                                                float* s_rows, uint32_t* bm, int* pre4,
-                                                int* s_off, int* perm, double& W,
-                                                double (&S)[NC], int& cnt) {
+__device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float (&f)[kSrtR][NC],
+                                             int len, int T, float* s_rows, int* cnt, int* off_,
+                                             int* s_ws, unsigned long long* bm) {
     const int tid = threadIdx.x;
-    const int C = a.C;
-    const int wcol = a.weight_col;
-    W = 0.0;
-    cnt = 0;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    // 1. counts per (wave, slot)
+    for (int q = tid; q < kSrtW * T; q += kSrtT) cnt[q] = 0;
+    lds_barrier();
+    int* __restrict__ wc = cnt + wave * T;
 #pragma unroll
-    for (int q = 0; q < NC; ++q) S[q] = 0.0;
-    int na[kPreSlots];
-    float nr[kPreRows];
-    // loads of the piece at s0 (indices clamped into the piece; only the
-    // first ns slots and ns * C floats are kept)
-    auto fetch = [&](int s0) {
-        const int ns = min(sub, hi - s0);
-        const int32_t* __restrict__ ag = a.assign + off + s0;
-        const float* __restrict__ fg = a.features + (off + s0) * (int64_t)C;
+    for (int r = 0; r < kSrtR; ++r) {
+        const int i = kSrtWave * wave + 64 * r + lane;
+        if (i < len && (unsigned)k[r] < (unsigned)T) atomicAdd(&wc[k[r]], 1);
+    }
+    lds_barrier();
+    // 2. slot offsets and (wave, slot) cursors (threads j < T)
+    {
+        const int j = tid;
+        int tot = 0;
+        if (j < T)
 #pragma unroll
-        for (int r = 0; r < kPreSlots; ++r) na[r] = ag[min(tid + kSortT * r, ns - 1)];
+            for (int w = 0; w < kSrtW; ++w) tot += cnt[w * T + j];
+        const int incl = wave_incl_scan_dpp(tot);
+        if (lane == 63) s_ws[wave] = incl;
+        lds_barrier();
+        int run = incl - tot;
+        for (int w = 0; w < wave; ++w) run += s_ws[w];
+        if (j < T) {
+            off_[j] = run;
+            int pos = run;
 #pragma unroll
-        for (int r = 0; r < kPreRows; ++r) nr[r] = fg[min(tid + kSortT * r, ns * C - 1)];
-    };
-    if (beg < hi) fetch(beg);
-    for (int s0 = beg; s0 < hi; s0 += sub) {
-        const int ns = min(sub, hi - s0);
+            for (int w = 0; w < kSrtW; ++w) {
+                const int v = cnt[w * T + j];
+                cnt[w * T + j] = pos;
+                pos += v;
+            }
+        }
+        if (j == 0) {
+            int total = 0;
+            for (int w = 0; w < kSrtW; ++w) total += s_ws[w];
+            off_[T] = total;
+        }
+    }
+    lds_barrier();
+    // 3. rows to their sorted places, window after window per wave
+    unsigned long long* __restrict__ wm = bm + wave * T;
+    const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int r = 0; r < kPreSlots; ++r)
-            if (tid + kSortT * r < ns) s_asg[tid + kSortT * r] = na[r];
+    for (int r = 0; r < kSrtR; ++r) {
+        const int i = kSrtWave * wave + 64 * r + lane;
+        const bool ok = i < len && (unsigned)k[r] < (unsigned)T;
+        const int kk = ok ? k[r] : 0;
+        if (ok) atomicOr(&wm[kk], 1ull << lane);
+        wave_lds_order();
+        const unsigned long long m = wm[kk];
+        const int cur = wc[kk];
+        wave_lds_order();
+        const int rank = __popcll(m & below);
+        if (ok) {
+            float* __restrict__ dst = s_rows + (cur + rank) * NC;
 #pragma unroll
-        for (int r = 0; r < kPreRows; ++r)
-            if (tid + kSortT * r < ns * C) s_rows[tid + kSortT * r] = nr[r];
-        for (int q = tid; q < C; q += kSortT) s_rows[ns * C + q] = 0.0f;
-        __syncthreads();
-        if (s0 + sub < hi) fetch(s0 + sub);
-        block_sort_bitmap(s_asg, ns, T, bm, pre4, s_off, perm);
-        if (tid < T) {
-            const int mb = s_off[tid], me = s_off[tid + 1];
-            cnt += me - mb;
-            for (int m0 = mb; m0 < me; m0 += kLdsBatch) {
-                int idx[kLdsBatch];
+            for (int q = 0; q < NC; ++q) dst[q] = f[r][q];
+            if (rank == 0) {
+                wc[kk] = cur + __popcll(m);
+                wm[kk] = 0ull;
+            }
+        }
+        wave_lds_order();
+    }
+    lds_barrier();
+}
+
+// Step 4: thread j < T adds slot j's sorted rows, in order, into its
+// float64 sums (which carry over from earlier sub-chunks).  Ends with a
+// barrier that orders LDS only.
+template <int NC>
+__device__ __forceinline__ void sorted_sums(int T, int wcol, const float* s_rows, const int* off_,
+                                            double& W, double (&S)[NC], int& count) {
+    const int tid = threadIdx.x;
+    if (tid < T) {
+        const int mb = off_[tid], me = off_[tid + 1];
+        // four members' rows read together, then added one after the other
+        // (rows past the slot are read, within the LDS rows, and not added)
+        constexpr int U = 4;
+        for (int m0 = mb; m0 < me; m0 += U) {
+            float fv[U][NC];
 #pragma unroll
-                for (int t = 0; t < kLdsBatch; ++t) idx[t] = m0 + t < me ? perm[m0 + t] : ns;
-                float wv[kLdsBatch], fv[kLdsBatch][NC];
+            for (int u = 0; u < U; ++u) {
+                const float* __restrict__ rw = s_rows + min(m0 + u, kPoolChunk - 1) * NC;
 #pragma unroll
-                for (int t = 0; t < kLdsBatch; ++t) {
-                    const float* __restrict__ row = s_rows + idx[t] * C;
-                    wv[t] = wcol >= 0 ? row[wcol] : (idx[t] < ns ? 1.0f : 0.0f);
+                for (int q = 0; q < NC; ++q) fv[u][q] = rw[q];
+            }
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) fv[t][q] = row[c0 + q];
-                }
+            for (int u = 0; u < U; ++u) {
+                if (m0 + u < me) {
+                    float wv = 1.0f;
 #pragma unroll
-                for (int t = 0; t < kLdsBatch; ++t) {
-                    const double wd = (double)wv[t];
+                    for (int q = 0; q < NC; ++q) wv = q == wcol ? fv[u][q] : wv;
+                    const double wd = (double)wv;
                     W += wd;
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[t][q], S[q]);
+                    for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[u][q], S[q]);
                 }
             }
         }
-        __syncthreads();
+        count += me - mb;
     }
+    lds_barrier();
 }
 
-// One column pass of a chunk: its sums, then either the means of a
-// one-chunk event (slots j < P, zeros beyond T) or the chunk's record.
 template <int NC>
-__device__ __forceinline__ void chunk_pass(const PoolArgs& a, int64_t b, int64_t off, int beg,
-                                           int hi, int T, int c0, int sub, int part, int* s_asg,
-                                           float* s_rows, uint32_t* bm, int* pre4, int* s_off,
-                                           int* perm) {
-    double W, S[NC];
-    int cnt;
-    chunk_slot_sums<NC>(a, off, beg, hi, T, c0, sub, s_asg, s_rows, bm, pre4, s_off, perm, W, S,
-                        cnt);
-    const int j = threadIdx.x;
-    const int P = a.P;
-    const int C = a.C;
-    if (part < 0) {
-        if (j < P) {
-            float* __restrict__ out = a.pooled + (b * P + j) * (int64_t)C + c0;
-#pragma unroll
-            for (int q = 0; q < NC; ++q)
-                out[q] = j < T && W != 0.0 ? (float)(S[q] / W) : 0.0f;
-            if (c0 == 0 && a.cell_count) a.cell_count[b * P + j] = j < T ? cnt : 0;
-        }
-    } else if (j < T) {
-        const int C2 = C + 2;
-        double* __restrict__ r = a.part + ((size_t)part * P + j) * C2;
-        r[0] = W;
-#pragma unroll
-        for (int q = 0; q < NC; ++q) r[1 + c0 + q] = S[q];
-        if (c0 == 0) r[C + 1] = (double)cnt;
-    }
-}
-
-// Voronoi pooling over the chunk list (kPoolChunk pulses per chunk) for
-// P <= 256, every chunk summed through LDS in pieces of `sub` pulses:
-//  * an event of one chunk gets its means directly (identity events pulse
-//    by pulse);
-//  * a chunk of a larger event writes its record (weight, every column,
-//    member count per slot); the workgroup finishing the event's last chunk
-//    adds the records in chunk order;
-//  * an event without record space (malformed offsets only) is summed whole
-//    by its first chunk's workgroup.
-// Dynamic LDS: int s_asg[sub], int perm[sub], int s_off[P + 1], int
-// pre4[P * sub / 128], uint32 bm[P * sub / 32], float s_rows[(sub + 1) * C].
-__global__ __launch_bounds__(kSortT) void pool_voronoi_lds_kernel(PoolArgs a, int sub) {
-    extern __shared__ __align__(16) int s_dyn[];
-    __shared__ int s_last;
-    const int c = blockIdx.x;
-    if (c >= a.header[6]) return;
-    const int64_t b = a.chunk_ev[c];
-    const int beg = a.chunk_beg[c];
-    const int part = a.chunk_part[c];
-    int64_t off;
-    int n;
-    event_range(a.offsets, a.N, b, off, n);
-    int T = a.token_count[b];
-    T = T < 0 ? 0 : (T > a.P ? a.P : T);
+__global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
+    extern __shared__ __align__(16) float s_srt[];
+    float* s_rows = s_srt;
+    __shared__ int s_ws[kSrtW];
+    __shared__ int s_vote[kSrtW];
+    __shared__ int s_mb[kSrtMeta], s_mbeg[kSrtMeta], s_mpart[kSrtMeta], s_mn[kSrtMeta],
+        s_mT[kSrtMeta];
+    __shared__ int64_t s_moff[kSrtMeta];
     const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
     const int P = a.P;
-    const int C = a.C;
-    if (part == -2 && beg != 0) return;
-    if (part == -1) {
-        bool ident = n == T;
-        for (int i = tid; ident && i < n; i += kSortT) ident = a.assign[off + i] == i;
-        if (__syncthreads_and(ident)) {
-            pool_identity(a, b, off, T);
+    const int C = NC;
+    const int wcol = a.weight_col;
+    int* cnt = reinterpret_cast<int*>(s_rows + kPoolChunk * NC);  // [kSrtW][P]
+    int* off_ = cnt + kSrtW * P;                                  // [P + 1]
+    unsigned long long* bm = reinterpret_cast<unsigned long long*>(
+        off_ + ((P + 2) & ~1));                                   // [kSrtW][P]
+    for (int q = tid; q < kSrtW * P; q += kSrtT) bm[q] = 0ull;
+    const int nchunks = a.header[6];
+    const int G = gridDim.x;
+    // descriptions of this workgroup's chunks i0 .. i0 + 63 (chunk blockIdx +
+    // G i), read by wave 0; the callers put a barrier after
+    auto fill_meta = [&](int i0) {
+        if (wave == 0) {
+            const int c = blockIdx.x + (i0 + lane) * G;
+            int b = 0, beg = 0, part = -1, n = 0, T = 0;
+            int64_t off = 0;
+            if (c < nchunks) {
+                b = a.chunk_ev[c];
+                beg = a.chunk_beg[c];
+                part = a.chunk_part[c];
+                event_range(a.offsets, a.N, b, off, n);
+                T = a.token_count[b];
+            }
+            s_mb[lane] = b;
+            s_mbeg[lane] = beg;
+            s_mpart[lane] = part;
+            s_mn[lane] = n;
+            s_mT[lane] = T < 0 ? 0 : (T > P ? P : T);
+            s_moff[lane] = off;
+        }
+    };
+    // a sub-chunk's pulses of this thread (512 wave + 64 r + lane) into k, f,
+    // indices clamped into it so that every load is issued together; an
+    // empty sub-chunk loads nothing (its first row may lie past the input)
+    int k[kSrtR];
+    float f[kSrtR][NC];
+    auto load = [&](int64_t off, int beg, int len) {
+        if (len <= 0) {
+#pragma unroll
+            for (int r = 0; r < kSrtR; ++r) {
+                k[r] = -1;
+#pragma unroll
+                for (int q = 0; q < NC; ++q) f[r][q] = 0.0f;
+            }
             return;
         }
-    }
-    const int W4 = sub >> 7;
-    uint32_t* bm = reinterpret_cast<uint32_t*>(s_dyn);       // P * W4 * 4
-    int* pre4 = s_dyn + P * W4 * 4;                           // P * W4
-    int* s_asg = pre4 + P * W4;                               // sub
-    int* perm = s_asg + sub;                                  // sub
-    int* s_off = perm + sub;                                  // P + 1
-    float* s_rows = reinterpret_cast<float*>(s_off + P + 1);  // (sub + 1) * C
-    const int hi = part == -2 ? n : min(n, beg + kPoolChunk);
-    const int rpart = part == -2 ? -1 : part;
-    for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-        switch (min(kPoolCols, C - c0)) {
-#define FPSTOK_CHUNK_PASS(NC)                                                                  \
-    case NC:                                                                                 \
-        chunk_pass<NC>(a, b, off, beg, hi, T, c0, sub, rpart, s_asg, s_rows, bm, pre4, s_off, \
-                       perm);                                                                \
-        break;
-            FPSTOK_CHUNK_PASS(1)
-            FPSTOK_CHUNK_PASS(2)
-            FPSTOK_CHUNK_PASS(3)
-            FPSTOK_CHUNK_PASS(4)
-            FPSTOK_CHUNK_PASS(5)
-            FPSTOK_CHUNK_PASS(6)
-            FPSTOK_CHUNK_PASS(7)
-            default: FPSTOK_CHUNK_PASS(8)
-#undef FPSTOK_CHUNK_PASS
+        const int32_t* __restrict__ ag = a.assign + off + beg;
+        const float* __restrict__ fg = a.features + (off + beg) * (int64_t)C;
+#pragma unroll
+        for (int r = 0; r < kSrtR; ++r) {
+            const int i = min(kSrtWave * wave + 64 * r + lane, len - 1);
+            k[r] = ag[i];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) f[r][q] = fg[(int64_t)i * C + q];
+        }
+    };
+    // the data of local chunk i (description in LDS slot i - m0)
+    auto load_local = [&](int i, int m0) {
+        const int m = i - m0;
+        const int n = s_mn[m], beg = s_mbeg[m];
+        load(s_moff[m], beg, max(0, min(n - beg, kPoolChunk)));
+    };
+    int m0 = 0;  // local index of the first description in LDS
+    fill_meta(0);
+    lds_barrier();  // descriptions and cleared masks
+    if ((int)blockIdx.x < nchunks) load_local(0, 0);
+    for (int i = 0; blockIdx.x + i * G < nchunks; ++i) {
+        const int m = i - m0;
+        const int64_t b = s_mb[m];
+        const int beg = s_mbeg[m];
+        const int part = s_mpart[m];
+        const int64_t off = s_moff[m];
+        const int n = s_mn[m];
+        const int T = s_mT[m];
+        const int len = max(0, min(n - beg, kPoolChunk));
+        const bool more = blockIdx.x + (i + 1) * G < nchunks;
+        // the next chunk's description, read into LDS here when it is past
+        // the ones held (every thread has read chunk i's above)
+        if (more && i + 1 - m0 >= kSrtMeta) {
+            lds_barrier();
+            m0 = i + 1;
+            fill_meta(m0);
+            lds_barrier();
+        }
+        if (part == -2 && beg != 0) {
+            // summed whole by the event's first chunk
+            if (more) load_local(i + 1, m0);
+            continue;
+        }
+        if (part == -1) {
+            bool ident = n == T;
+#pragma unroll
+            for (int r = 0; r < kSrtR; ++r) {
+                const int ii = kSrtWave * wave + 64 * r + lane;
+                ident = ident && (ii >= len || k[r] == ii);
+            }
+            const bool wave_ident = ballot(!ident) == 0;
+            if (lane == 0) s_vote[wave] = wave_ident ? 1 : 0;
+            lds_barrier();
+            int all = 1;
+#pragma unroll
+            for (int w = 0; w < kSrtW; ++w) all &= s_vote[w];
+            lds_barrier();  // every wave has read the votes
+            if (all) {
+                if (more) load_local(i + 1, m0);
+                pool_identity(a, b, off, T);
+                continue;
+            }
+        }
+        double W = 0.0, S[NC];
+#pragma unroll
+        for (int q = 0; q < NC; ++q) S[q] = 0.0;
+        int count = 0;
+        sorted_place<NC>(k, f, len, T, s_rows, cnt, off_, s_ws, bm);
+        if (part == -2) {
+            // the rest of an event summed whole, sub-chunk after sub-chunk
+            // (one ascending sum)
+            for (int sb = kPoolChunk; sb < n; sb += kPoolChunk) {
+                sorted_sums<NC>(T, wcol, s_rows, off_, W, S, count);
+                const int sl = min(n - sb, kPoolChunk);
+                load(off, sb, sl);
+                sorted_place<NC>(k, f, sl, T, s_rows, cnt, off_, s_ws, bm);
+            }
+        }
+        // the rows are in LDS: the next chunk's loads go out now, behind the
+        // sums and the outputs
+        if (more) load_local(i + 1, m0);
+        sorted_sums<NC>(T, wcol, s_rows, off_, W, S, count);
+        const int j = tid;
+        if (part < 0) {
+            if (j < P) {
+                float* __restrict__ out = a.pooled + (b * P + j) * (int64_t)C;
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    out[q] = j < T && W != 0.0 ? (float)(S[q] / W) : 0.0f;
+                if (a.cell_count) a.cell_count[b * P + j] = j < T ? count : 0;
+            }
+        } else if (j < T) {
+            // this chunk's record for the combine kernel
+            constexpr int C2 = NC + 2;
+            double* __restrict__ rr = a.part + ((size_t)part * P + j) * C2;
+            rr[0] = W;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) rr[1 + q] = S[q];
+            rr[NC + 1] = (double)count;
         }
     }
-    if (rpart < 0) return;
-    // publish the record; the last chunk of the event to finish combines
-    // (events of more than comb_last chunks: the combine kernel)
-    const int K = (n + kPoolChunk - 1) / kPoolChunk;
-    if (K > a.comb_last) return;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        s_last = __hip_atomic_fetch_add(a.ev_cnt + b, 1, __ATOMIC_ACQ_REL,
-                                        __HIP_MEMORY_SCOPE_AGENT) == K - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    pool_combine_records(a, b, T, K, part - beg / kPoolChunk);
 }
 
-// Means of the events of more than comb_last chunks from their chunks'
+// Means of the events of more than one chunk from their chunks'
 // records: block (event m, slot group) with threads (field f, slot js);
 // field 0 is the weight, 1..C the columns, C+1 the member count; every
 // thread adds its value over the K records in chunk order, 16 loads in
@@ -3354,6 +3609,23 @@ hipError_t noalloc_scratch(void** ptr) {
 
 static inline unsigned grid1(int64_t x) { return (unsigned)(x < 1 ? 1 : x); }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+static int device_cus() {
+    static std::mutex mu;
+    static int by_device[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (by_device[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        by_device[dev] = n;
+    }
+    return by_device[dev];
+}
+
 hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
                        const WorkspaceLayout& L, hipStream_t s) {
     char* base = (char*)ws;
@@ -3364,21 +3636,19 @@ hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
 }
 
 hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                            const WorkspaceLayout& L, hipStream_t s) {
+                            const WorkspaceLayout& L, int whole, hipStream_t s) {
     char* base = (char*)ws;
     hipLaunchKernelGGL(plan_pool_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N,
                        L.max_pool_chunks, L.max_parts, (int32_t*)(base + L.header),
                        (int32_t*)(base + L.pool_ev), (int32_t*)(base + L.pool_beg),
-                       (int32_t*)(base + L.chunk_part),
-                       (int32_t*)(base + L.ev_cnt), (int32_t*)(base + L.big_ev));
+                       (int32_t*)(base + L.chunk_part), (int32_t*)(base + L.big_ev), whole);
     return hipGetLastError();
 }
 
 hipError_t launch_pool_combine(const PoolArgs& a, hipStream_t s) {
-    if (a.comb_last >= (1 << 30)) return hipSuccess;
-    // events of more than comb_last chunks hold more than comb_last *
-    // kPoolChunk pulses
-    const int64_t big = std::min<int64_t>(a.B, a.N / ((int64_t)a.comb_last * kPoolChunk + 1));
+    if (a.whole) return hipSuccess;
+    // events of more than one chunk hold more than kPoolChunk pulses
+    const int64_t big = std::min<int64_t>(a.B, a.N / ((int64_t)kPoolChunk + 1));
     if (big <= 0) return hipSuccess;
     const int C2 = a.C + 2;
     const int spg = 256 / C2;
@@ -3456,27 +3726,27 @@ hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Dynamic LDS of pool_voronoi_lds_kernel for pieces of `sub` pulses.
-static size_t pool_lds_bytes(int P, int C, int sub) {
-    const size_t w4 = (size_t)sub / 128;
-    return sizeof(int) * ((size_t)P * w4 * 5 + 2 * (size_t)sub + P + 1) +
-           sizeof(float) * ((size_t)sub + 1) * C;
-}
-
 hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s) {
-    if (a.P <= kPoolLdsMaxP) {
-        // 1024-pulse pieces, when the threads can hold a piece's rows in
-        // registers and two workgroups per CU fit in LDS; otherwise (wide
-        // rows) gathering members from device memory is faster
-        const int sub = 1024;
-        if ((int64_t)sub * a.C <= (int64_t)kSortT * kPreRows &&
-            pool_lds_bytes(a.P, a.C, sub) <= 80 * 1024) {
-            hipLaunchKernelGGL(pool_voronoi_lds_kernel, dim3(grid1(max_chunks)), dim3(kSortT),
-                               pool_lds_bytes(a.P, a.C, sub), s, a, sub);
-            return hipGetLastError();
+    if (a.P <= kSrtMaxP && a.C <= kSrtMaxC) {
+        // rows sorted by slot into LDS; one persistent workgroup per compute unit
+        const size_t lds = sizeof(float) * (size_t)kPoolChunk * a.C +
+                           sizeof(int) * ((size_t)kSrtW * a.P + ((a.P + 2) & ~1)) +
+                           sizeof(unsigned long long) * (size_t)kSrtW * a.P;
+        const dim3 g((unsigned)std::max<int64_t>(1, std::min<int64_t>(max_chunks, device_cus()))),
+            t(kSrtT);
+        switch (a.C) {
+            case 1: hipLaunchKernelGGL(pool_sorted_kernel<1>, g, t, lds, s, a); break;
+            case 2: hipLaunchKernelGGL(pool_sorted_kernel<2>, g, t, lds, s, a); break;
+            case 3: hipLaunchKernelGGL(pool_sorted_kernel<3>, g, t, lds, s, a); break;
+            case 4: hipLaunchKernelGGL(pool_sorted_kernel<4>, g, t, lds, s, a); break;
+            case 5: hipLaunchKernelGGL(pool_sorted_kernel<5>, g, t, lds, s, a); break;
+            default: hipLaunchKernelGGL(pool_sorted_kernel<6>, g, t, lds, s, a); break;
         }
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL(pool_voronoi_kernel, dim3(grid1(max_chunks)), dim3(kSortT), 0, s, a);
+    const size_t lds = sizeof(unsigned long long) * kSortW * (size_t)a.P +
+                       sizeof(int) * (2 * (size_t)kPoolChunk + kSortW * (size_t)a.P + a.P + 1);
+    hipLaunchKernelGGL(pool_chunk_kernel, dim3(grid1(max_chunks)), dim3(kSortT), lds, s, a);
     return hipGetLastError();
 }
 

@@ -248,12 +248,14 @@ def test_fused_lds_pooling(oracle_mod):
 
 
 def test_pool_chunk_combines(oracle_mod):
-    """Standalone Voronoi pooling over 4096-pulse chunks: one-chunk events
-    summed in pieces through LDS, events of 2..4 chunks finished by their
-    last chunk's workgroup, larger ones by the combine kernel; P <= 256 (LDS
-    pieces, narrow and wide rows) and P > 256 (the sort path)."""
+    """Standalone Voronoi pooling over 4096-pulse chunks: every chunk sorted
+    by slot, one-chunk events written directly, chunks of larger events
+    written as records that the combine kernel adds in chunk order; P <= 256
+    with rows of up to 6 columns (rows sorted into LDS by the persistent
+    kernel, 1 and 6 columns) and the gather kernel otherwise (7 and 16
+    columns, P > 256)."""
     ns = [4096, 4097, 8192, 12289, 16384, 16385, 40000, 300]
-    for C, P in ((6, 128), (6, 256), (16, 128), (3, 300)):
+    for C, P in ((6, 128), (6, 256), (1, 200), (7, 64), (16, 128), (3, 300)):
         b = synth.icecube_events(ns, 400 + C + P, C=C)
         cc = synth.CHARGE_COL if C > synth.CHARGE_COL else -1
         check_pipeline(oracle_mod, b, P=P, charge_col=cc, label="pool chunks C=%d P=%d" % (C, P))
@@ -315,9 +317,9 @@ def test_max_event_points_hint(oracle_mod):
     check_pipeline(oracle_mod, b, P=128, L=2, label="hint too small sample", max_event_points=5)
     _tokenize_vs_oracle(oracle_mod, b, 128, label="hint above one workgroup",
                         max_event_points=9000)
-    # a bound that rules out events of more than four pooling chunks: the last
-    # chunk of every event finishes it, also for an event of ten chunks when
-    # the bound is wrong
+    # a bound that rules out events of more than one pooling chunk: no
+    # combine kernel, and an event of ten chunks that breaks the bound is
+    # summed whole by its first chunk's workgroup
     b = synth.icecube_events([40000, 300, 5000], 28, C=6)
     check_pipeline(oracle_mod, b, P=128, label="hint too small, 10-chunk event",
                    max_event_points=100)

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define FPSTOK_ABI_VERSION 2
+#define FPSTOK_ABI_VERSION 3
 #define FPSTOK_MAX_PATCHES 1024 /* largest num_patches accepted             */
 #define FPSTOK_MAX_K 64         /* largest kNN list length accepted           */
 #define FPSTOK_MAX_LLOYD 1000   /* largest lloyd_iters accepted               */
@@ -92,11 +92,24 @@ typedef enum {
 
 typedef enum { FPSTOK_VORONOI = 0, FPSTOK_KNN = 1 } fpstok_assign_mode;
 
+/* Element type of the coordinates or the features.  16-bit inputs are
+ * upcast exactly to float32 (every binary16 and bfloat16 value is a float32
+ * value) into the workspace before anything else reads them, so every result
+ * equals the float32 call on the same values: FPS and every sum stay in
+ * float32 / float64.  (Pull Request #923, "Add Neptune point-transformer
+ * backbone": its "What is added" list has low-precision tests, and the review
+ * thread on the FPS precision argument settles that FPS runs in float32 on
+ * both backends whatever the input dtype.)  Gradients (fpstok_pool_backward)
+ * are float32 whatever the features' dtype. */
+typedef enum { FPSTOK_F32 = 0, FPSTOK_F16 = 1, FPSTOK_BF16 = 2 } fpstok_dtype;
+
 /* One CSR batch of events.  All pointers are device pointers. */
 typedef struct {
-    const float* coords;     /* [N,4] f32 row-major (x,y,z,t); 16-byte aligned    */
-    const float* features;   /* [N,C] f32 row-major; 4-byte aligned; may be NULL  */
-                             /* for calls that do not read features               */
+    const void* coords;      /* [N,4] row-major (x,y,z,t), coords_dtype; 16-byte  */
+                             /* aligned for float32, 8-byte for 16-bit types      */
+    const void* features;    /* [N,C] row-major, features_dtype; aligned to its   */
+                             /* element; may be NULL for calls that do not read   */
+                             /* features                                          */
     const int64_t* offsets;  /* [B+1] int64: event b is rows offsets[b] ..        */
                              /* offsets[b+1]-1; offsets[0]=0, offsets[B]=N         */
     int64_t num_events;      /* B >= 0                                            */
@@ -110,6 +123,10 @@ typedef struct {
                              /* workgroup); a bound that is too small stays       */
                              /* correct: a larger event falls back to the slower  */
                              /* one-workgroup streaming FPS.                      */
+    int32_t coords_dtype;    /* fpstok_dtype of coords (FPSTOK_F32 = 0)           */
+    int32_t features_dtype;  /* fpstok_dtype of features (FPSTOK_F32 = 0); with a */
+                             /* 16-bit type the workspace also holds the float32  */
+                             /* copy (fpstok_workspace_size counts it)            */
 } fpstok_batch;
 
 typedef struct {
@@ -121,8 +138,9 @@ typedef struct {
 } fpstok_params;
 
 /* Bytes of device workspace every compute call of this batch shape needs
- * (depends on B, N, num_patches and num_features; params may be NULL for
- * the largest num_patches).  Host-only; never fails; 0 for B = 0. */
+ * (depends on B, N, num_patches, num_features and the input dtypes; params
+ * may be NULL for the largest num_patches).  Host-only; never fails; 0 for
+ * B = 0. */
 size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_params* params);
 
 /* FPS of every event (farthest_point_sampling / _with_assign).  For n > P:
@@ -325,6 +343,18 @@ void fpstok_debug_set_spin_limit(uint32_t polls);
  * not for the hot path.  Returns FPSTOK_OK or FPSTOK_EINVAL (the reason is in
  * fpstok_last_error()), or FPSTOK_EHIP. */
 fpstok_status fpstok_validate(const fpstok_batch* batch, void* stream);
+
+/* dst[i] = the float32 value of src[i] for i < count, src of dtype
+ * FPSTOK_F16 (IEEE binary16, subnormals kept) or FPSTOK_BF16 (bfloat16:
+ * the upper 16 bits of a float32).  The conversion every call above applies
+ * to 16-bit inputs, exposed for callers that convert once and reuse the
+ * float32 copy.  Exact for every finite and infinite value; a NaN stays a
+ * NaN of the same sign (a signalling binary16 NaN may come back quiet).
+ * src 2-byte aligned, dst 4-byte aligned, device pointers; count >= 0;
+ * enqueued on `stream`; EINVAL for a NULL pointer with count > 0, another
+ * dtype or misalignment. */
+fpstok_status fpstok_upcast(const void* src, int64_t count, int32_t dtype, float* dst,
+                            void* stream);
 
 /* Static description of a status code. */
 const char* fpstok_status_string(fpstok_status status);

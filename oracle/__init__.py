@@ -60,9 +60,10 @@ def _load():
         lib.oracle_philox4x32_10.argtypes = [P, P, P]
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_random_start.argtypes = [P, i64, ctypes.c_uint64, ctypes.c_uint64, P]
+        lib.oracle_upcast.argtypes = [P, i64, i32, P]
         for f in ("oracle_sample", "oracle_assign", "oracle_knn", "oracle_lloyd",
                   "oracle_pool", "oracle_tokenize", "oracle_pack", "oracle_unpack",
-                  "oracle_pool_backward", "oracle_random_start"):
+                  "oracle_pool_backward", "oracle_random_start", "oracle_upcast"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -269,4 +270,18 @@ def random_start(offsets, seed, step=0):
     out = np.empty(B, np.int32)
     _check(_load().oracle_random_start(_ptr(o), B, int(seed) & (2**64 - 1),
                                        int(step) & (2**64 - 1), _ptr(out)), "random_start")
+    return out
+
+
+F16, BF16 = 1, 2
+
+
+def upcast(bits, dtype):
+    """The float32 values of 16-bit inputs given as their bit patterns (any
+    shape of uint16): dtype F16 (IEEE binary16) or BF16 (bfloat16).  Exact:
+    every such value is a float32 value.  Low-precision coordinates or
+    features go through this, then through the float32 functions above."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, np.float32)
+    _check(_load().oracle_upcast(_ptr(b), b.size, int(dtype), _ptr(out)), "upcast")
     return out

@@ -43,7 +43,11 @@
  *   - pooling = (weighted) mean of every feature column of each token's
  *     members, accumulated in float64, rounded to float32, 0 when the
  *     weight sum is 0;
- *   - indices are event-local int32; slots j >= T are padded with -1 / 0.
+ *   - indices are event-local int32; slots j >= T are padded with -1 / 0;
+ *   - inputs in binary16 or bfloat16 are upcast exactly to float32 first
+ *     (every such value is a float32 value) and the float32 path runs on
+ *     them: FPS itself stays float32 ([PR] review reply on the removed
+ *     precision argument; "What is added": tests in low precision).
  *
  * Layout: coords [N,4] f32 row-major, features [N,C] f32 row-major,
  * offsets [B+1] int64 (CSR, events contiguous), per-event outputs [B,P,...].
@@ -575,5 +579,53 @@ int oracle_random_start(const int64_t* offsets, int64_t B, uint64_t seed, uint64
         philox4x32_10(in, key, out);
         start_idx[b] = n > 0 ? (int32_t)(((uint64_t)out[0] * (uint64_t)n) >> 32) : 0;
     }
+    return 0;
+}
+
+/* ------------------------------------------ low-precision inputs (next) -- */
+
+/* IEEE 754 binary16 to binary32, from the format's definition: sign bit,
+ * 5-bit exponent biased by 15, 10-bit fraction.  Exponent 0 holds zero and
+ * the subnormals fraction * 2^-24; exponent 31 holds the infinities (fraction
+ * 0) and NaNs (the fraction kept as the top of the binary32 fraction); every
+ * other exponent e gives (1024 + fraction) * 2^(e - 25).  Each value is
+ * exactly representable in binary32, and ldexpf of an integer below 2^11 is
+ * exact, so nothing is rounded. */
+static float f16_to_f32(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1F;
+    const int m = h & 0x3FF;
+    float v;
+    if (e == 0) {
+        v = ldexpf((float)m, -24);
+    } else if (e == 31) {
+        uint32_t bits = ((uint32_t)sign << 31) | 0x7F800000u | ((uint32_t)m << 13);
+        memcpy(&v, &bits, sizeof v);
+        return v;
+    } else {
+        v = ldexpf((float)(1024 + m), e - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16 to binary32: bfloat16 is defined as the upper 16 bits of a
+ * binary32 (same sign and 8-bit exponent, 7 of the 23 fraction bits), so
+ * the value is the binary32 whose low 16 bits are zero. */
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float v;
+    memcpy(&v, &bits, sizeof v);
+    return v;
+}
+
+/* dst[i] = the float32 value of the 16-bit src[i]; dtype 1 = binary16,
+ * 2 = bfloat16.  Returns 2 for another dtype. */
+int oracle_upcast(const uint16_t* src, int64_t count, int32_t dtype, float* dst)
+{
+    if (dtype != 1 && dtype != 2) return 2;
+    for (int64_t i = 0; i < count; ++i)
+        dst[i] = dtype == 1 ? f16_to_f32(src[i]) : bf16_to_f32(src[i]);
     return 0;
 }

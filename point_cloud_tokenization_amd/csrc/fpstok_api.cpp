@@ -48,7 +48,8 @@ static std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
+WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C, int coords_dtype,
+                                 int features_dtype) {
     WorkspaceLayout L{};
     if (B <= 0) return L;
     const int64_t nn = N > 0 ? N : 0;
@@ -87,6 +88,10 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C) {
     L.max_parts = nn / kGangPulsesPerShard + 1;
     L.part = at;
     at += align256((size_t)L.max_parts * (size_t)P * (size_t)(C + 2) * sizeof(double));
+    L.coords32 = at;
+    if (coords_dtype != FPSTOK_F32) at += align256((size_t)nn * 4 * sizeof(float));
+    L.feat32 = at;
+    if (features_dtype != FPSTOK_F32) at += align256((size_t)nn * (size_t)C * sizeof(float));
     L.total = at;
     return L;
 }
@@ -113,18 +118,24 @@ static fpstok_status check_common(const fpstok_batch* bt, const fpstok_params* p
         return fail(FPSTOK_EINVAL, "lloyd_iters must be in [0, %d]", FPSTOK_MAX_LLOYD);
     if (pr->pool_weighted != 0 && pr->pool_weighted != 1)
         return fail(FPSTOK_EINVAL, "pool_weighted must be 0 or 1");
+    if (bt->coords_dtype < FPSTOK_F32 || bt->coords_dtype > FPSTOK_BF16)
+        return fail(FPSTOK_EINVAL, "coords_dtype must be FPSTOK_F32, FPSTOK_F16 or FPSTOK_BF16");
+    if (bt->features_dtype < FPSTOK_F32 || bt->features_dtype > FPSTOK_BF16)
+        return fail(FPSTOK_EINVAL, "features_dtype must be FPSTOK_F32, FPSTOK_F16 or FPSTOK_BF16");
     if (bt->num_events == 0) return FPSTOK_OK;
     if (!bt->offsets) return fail(FPSTOK_EINVAL, "offsets is NULL");
     if (bt->num_points > 0) {
         if (!bt->coords) return fail(FPSTOK_EINVAL, "coords is NULL");
-        if (((uintptr_t)bt->coords & 15u) != 0)
-            return fail(FPSTOK_EINVAL, "coords must be 16-byte aligned");
+        const uintptr_t ca = bt->coords_dtype == FPSTOK_F32 ? 15u : 7u;
+        if (((uintptr_t)bt->coords & ca) != 0)
+            return fail(FPSTOK_EINVAL, "coords must be %d-byte aligned", (int)ca + 1);
     }
     if (need_features) {
         if (bt->num_features < 1) return fail(FPSTOK_EINVAL, "num_features must be >= 1");
         if (bt->num_points > 0 && !bt->features) return fail(FPSTOK_EINVAL, "features is NULL");
-        if (bt->features && ((uintptr_t)bt->features & 3u) != 0)
-            return fail(FPSTOK_EINVAL, "features must be 4-byte aligned");
+        const uintptr_t fa = bt->features_dtype == FPSTOK_F32 ? 3u : 1u;
+        if (bt->features && ((uintptr_t)bt->features & fa) != 0)
+            return fail(FPSTOK_EINVAL, "features must be %d-byte aligned", (int)fa + 1);
     }
     if (need_features || need_weights_col) {
         if (bt->charge_col < -1 || (bt->num_features >= 1 && bt->charge_col >= bt->num_features))
@@ -137,10 +148,15 @@ static fpstok_status check_common(const fpstok_batch* bt, const fpstok_params* p
     return FPSTOK_OK;
 }
 
+static WorkspaceLayout batch_layout(const fpstok_batch* bt, int P) {
+    return workspace_layout(bt->num_events, bt->num_points, P,
+                            bt->num_features > 0 ? bt->num_features : 1, bt->coords_dtype,
+                            bt->features_dtype);
+}
+
 static fpstok_status check_ws(const fpstok_batch* bt, const fpstok_params* pr, void* ws,
                               size_t ws_bytes, WorkspaceLayout& L) {
-    L = workspace_layout(bt->num_events, bt->num_points, pr->num_patches,
-                         bt->num_features > 0 ? bt->num_features : 1);
+    L = batch_layout(bt, pr->num_patches);
     if (L.total == 0) return FPSTOK_OK;
     if (!ws) return fail(FPSTOK_EWORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
     if (ws_bytes < L.total)
@@ -153,6 +169,36 @@ static fpstok_status check_ws(const fpstok_batch* bt, const fpstok_params* pr, v
 template <class T>
 static T* at(void* ws, size_t off) {
     return (T*)((char*)ws + off);
+}
+
+// 16-bit inputs the call reads (coordinates, features) are upcast into
+// their float32 copies in the workspace, and `bt` is pointed at a copy of
+// the batch that names those instead (everything else unchanged).
+static fpstok_status stage_inputs(const fpstok_batch*& bt, fpstok_batch& tmp, bool coords,
+                                  bool features, void* ws, const WorkspaceLayout& L,
+                                  hipStream_t s) {
+    const int64_t N = bt->num_points;
+    const bool c16 = coords && bt->coords_dtype != FPSTOK_F32 && N > 0;
+    const bool f16 = features && bt->features_dtype != FPSTOK_F32 && N > 0 && bt->features;
+    if (!c16 && !f16) return FPSTOK_OK;
+    tmp = *bt;
+    float* c32 = at<float>(ws, L.coords32);
+    float* f32 = at<float>(ws, L.feat32);
+    const hipError_t e =
+        launch_upcast(c16 ? bt->coords : nullptr, c16 ? N * 4 : 0, bt->coords_dtype, c32,
+                      f16 ? bt->features : nullptr, f16 ? N * (int64_t)bt->num_features : 0,
+                      bt->features_dtype, f32, s);
+    if (e != hipSuccess) return hip_fail(e, "upcast kernel launch");
+    if (c16) {
+        tmp.coords = c32;
+        tmp.coords_dtype = FPSTOK_F32;
+    }
+    if (f16) {
+        tmp.features = f32;
+        tmp.features_dtype = FPSTOK_F32;
+    }
+    bt = &tmp;
+    return FPSTOK_OK;
 }
 
 static SampleArgs sample_args(const fpstok_batch* bt, const fpstok_params* pr,
@@ -188,7 +234,7 @@ static PoolArgs pool_args(const fpstok_batch* bt, const fpstok_params* pr,
                           const int32_t* knn_idx, float* pooled, int32_t* cell_count, void* ws,
                           const WorkspaceLayout& L) {
     PoolArgs a{};
-    a.features = bt->features;
+    a.features = (const float*)bt->features;
     a.offsets = bt->offsets;
     a.N = bt->num_points;
     a.C = bt->num_features;
@@ -224,7 +270,7 @@ static hipError_t run_lloyd(const fpstok_batch* bt, const fpstok_params* pr, flo
                             const WorkspaceLayout& L, hipStream_t s) {
     LloydArgs u{};
     u.coords = (const float4*)bt->coords;
-    u.features = bt->features;
+    u.features = (const float*)bt->features;
     u.offsets = bt->offsets;
     u.N = bt->num_points;
     u.C = bt->num_features;
@@ -272,9 +318,7 @@ FPSTOK_API size_t fpstok_workspace_size(const fpstok_batch* batch, const fpstok_
     if (!batch) return 0;
     int P = params ? params->num_patches : FPSTOK_MAX_PATCHES;
     if (P < 1 || P > FPSTOK_MAX_PATCHES) P = FPSTOK_MAX_PATCHES;
-    return workspace_layout(batch->num_events, batch->num_points, P,
-                            batch->num_features > 0 ? batch->num_features : 1)
-        .total;
+    return batch_layout(batch, P).total;
 }
 
 FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_params* pr,
@@ -290,6 +334,9 @@ FPSTOK_API fpstok_status fpstok_sample(const fpstok_batch* bt, const fpstok_para
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, true, false, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     const SampleArgs a = sample_args(bt, pr, start_idx, centroid_idx, centroids, token_count,
                                      assign, ws, L);
     hipError_t e = launch_sample(a, bt->num_events, (hipStream_t)stream);
@@ -309,6 +356,9 @@ FPSTOK_API fpstok_status fpstok_assign(const fpstok_batch* bt, const fpstok_para
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, true, false, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
@@ -343,6 +393,9 @@ FPSTOK_API fpstok_status fpstok_knn(const fpstok_batch* bt, const fpstok_params*
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, true, false, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     KnnArgs a{};
     a.coords = (const float4*)bt->coords;
     a.offsets = bt->offsets;
@@ -369,6 +422,9 @@ FPSTOK_API fpstok_status fpstok_lloyd(const fpstok_batch* bt, const fpstok_param
         return fail(FPSTOK_EINVAL, "centroids must be 16-byte aligned");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, true, bt->charge_col >= 0, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_plan(bt->offsets, bt->num_events, bt->num_points, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
@@ -391,6 +447,9 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
         return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, false, true, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     const PoolArgs a = pool_args(bt, pr, token_count, assign, knn_idx, pooled, cell_count, ws, L);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
@@ -459,8 +518,11 @@ FPSTOK_API fpstok_status fpstok_pool_backward(const fpstok_batch* bt, const fpst
         return fail(FPSTOK_EINVAL, "knn_idx is required in kNN mode");
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, false, true, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     PoolBwdArgs a{};
-    a.features = bt->features;
+    a.features = (const float*)bt->features;
     a.offsets = bt->offsets;
     a.N = bt->num_points;
     a.C = bt->num_features;
@@ -581,6 +643,9 @@ FPSTOK_API fpstok_status fpstok_tokenize(const fpstok_batch* bt, const fpstok_pa
     if (bt->num_events == 0) return ok();
     WorkspaceLayout L;
     if ((st = check_ws(bt, pr, ws, ws_bytes, L)) != FPSTOK_OK) return st;
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, true, true, ws, L, (hipStream_t)stream)) != FPSTOK_OK)
+        return st;
     return run_tokenize(bt, pr, start_idx, centroid_idx, centroids, token_count, assign, knn_idx,
                         pooled, cell_count, ws, L, stream);
 }
@@ -594,8 +659,7 @@ FPSTOK_API fpstok_status fpstok_tokenize_noalloc(const fpstok_batch* bt, const f
                                       knn_idx, pooled);
     if (st != FPSTOK_OK) return st;
     if (bt->num_events == 0) return ok();
-    const WorkspaceLayout L = workspace_layout(bt->num_events, bt->num_points, pr->num_patches,
-                                               bt->num_features > 0 ? bt->num_features : 1);
+    const WorkspaceLayout L = batch_layout(bt, pr->num_patches);
     if (L.total > kNoAllocBytes)
         return fail(FPSTOK_EUNSUPPORTED,
                     "this batch needs %zu bytes of workspace; the no-allocation scratch region "
@@ -616,14 +680,34 @@ FPSTOK_API fpstok_status fpstok_tokenize_noalloc(const fpstok_batch* bt, const f
     void* ws = nullptr;
     e = noalloc_scratch(&ws);
     if (e != hipSuccess) return hip_fail(e, "looking up the scratch region");
+    fpstok_batch staged;
+    if ((st = stage_inputs(bt, staged, true, true, ws, L, s)) != FPSTOK_OK) return st;
     return run_tokenize(bt, pr, start_idx, centroid_idx, centroids, token_count, assign, knn_idx,
                         pooled, cell_count, ws, L, stream);
+}
+
+// Host-side value checks of one element of a coordinate or feature array in
+// its dtype, read from the raw bits.
+static bool elem_finite(const void* base, size_t i, int dtype) {
+    if (dtype == FPSTOK_F32) return std::isfinite(((const float*)base)[i]);
+    const uint16_t h = ((const uint16_t*)base)[i];
+    // binary16: exponent bits 10..14; bfloat16: exponent bits 7..14
+    return dtype == FPSTOK_F16 ? ((h >> 10) & 0x1F) != 0x1F : ((h >> 7) & 0xFF) != 0xFF;
+}
+
+static bool elem_negative(const void* base, size_t i, int dtype) {
+    if (dtype == FPSTOK_F32) return ((const float*)base)[i] < 0.0f;
+    const uint16_t h = ((const uint16_t*)base)[i];
+    return (h & 0x8000u) != 0 && (h & 0x7FFFu) != 0;  // sign set, not -0
 }
 
 FPSTOK_API fpstok_status fpstok_validate(const fpstok_batch* bt, void* stream) {
     if (!bt) return fail(FPSTOK_EINVAL, "batch is NULL");
     const int64_t B = bt->num_events, N = bt->num_points;
     if (B < 0 || N < 0) return fail(FPSTOK_EINVAL, "negative num_events or num_points");
+    if (bt->coords_dtype < FPSTOK_F32 || bt->coords_dtype > FPSTOK_BF16 ||
+        bt->features_dtype < FPSTOK_F32 || bt->features_dtype > FPSTOK_BF16)
+        return fail(FPSTOK_EINVAL, "unknown coords_dtype or features_dtype");
     if (B == 0) return ok();
     if (!bt->offsets) return fail(FPSTOK_EINVAL, "offsets is NULL");
     hipStream_t s = (hipStream_t)stream;
@@ -641,24 +725,43 @@ FPSTOK_API fpstok_status fpstok_validate(const fpstok_batch* bt, void* stream) {
                     (long long)off[(size_t)B], (long long)N);
     if (N > 0) {
         if (!bt->coords) return fail(FPSTOK_EINVAL, "coords is NULL");
-        std::vector<float> x((size_t)N * 4);
-        e = hipMemcpy(x.data(), bt->coords, x.size() * sizeof(float), hipMemcpyDeviceToHost);
+        const size_t cw = bt->coords_dtype == FPSTOK_F32 ? 4 : 2;
+        std::vector<unsigned char> x((size_t)N * 4 * cw);
+        e = hipMemcpy(x.data(), bt->coords, x.size(), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpy coords");
-        for (size_t q = 0; q < x.size(); ++q)
-            if (!std::isfinite(x[q]))
+        for (size_t q = 0; q < (size_t)N * 4; ++q)
+            if (!elem_finite(x.data(), q, bt->coords_dtype))
                 return fail(FPSTOK_EINVAL, "coords[%zu][%zu] is not finite", q / 4, q % 4);
         if (bt->charge_col >= 0 && bt->features && bt->num_features > bt->charge_col) {
             const int64_t C = bt->num_features;
-            std::vector<float> f((size_t)(N * C));
-            e = hipMemcpy(f.data(), bt->features, f.size() * sizeof(float), hipMemcpyDeviceToHost);
+            const size_t fw = bt->features_dtype == FPSTOK_F32 ? 4 : 2;
+            std::vector<unsigned char> f((size_t)(N * C) * fw);
+            e = hipMemcpy(f.data(), bt->features, f.size(), hipMemcpyDeviceToHost);
             if (e != hipSuccess) return hip_fail(e, "hipMemcpy features");
             for (int64_t i = 0; i < N; ++i) {
-                const float q = f[(size_t)(i * C + bt->charge_col)];
-                if (!(q >= 0.0f) || !std::isfinite(q))
-                    return fail(FPSTOK_EINVAL, "charge of pulse %lld is %g", (long long)i, q);
+                const size_t q = (size_t)(i * C + bt->charge_col);
+                if (!elem_finite(f.data(), q, bt->features_dtype) ||
+                    elem_negative(f.data(), q, bt->features_dtype))
+                    return fail(FPSTOK_EINVAL, "charge of pulse %lld is negative or not finite",
+                                (long long)i);
             }
         }
     }
+    return ok();
+}
+
+FPSTOK_API fpstok_status fpstok_upcast(const void* src, int64_t count, int32_t dtype,
+                                       float* dst, void* stream) {
+    if (count < 0) return fail(FPSTOK_EINVAL, "count must be >= 0");
+    if (dtype != FPSTOK_F16 && dtype != FPSTOK_BF16)
+        return fail(FPSTOK_EINVAL, "dtype must be FPSTOK_F16 or FPSTOK_BF16");
+    if (count == 0) return ok();
+    if (!src || !dst) return fail(FPSTOK_EINVAL, "src or dst is NULL");
+    if (((uintptr_t)src & 1u) != 0 || ((uintptr_t)dst & 3u) != 0)
+        return fail(FPSTOK_EINVAL, "src must be 2-byte and dst 4-byte aligned");
+    const hipError_t e = launch_upcast(src, count, dtype, dst, nullptr, 0, dtype, nullptr,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "upcast kernel launch");
     return ok();
 }
 

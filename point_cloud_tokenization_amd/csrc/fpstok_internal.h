@@ -54,6 +54,8 @@ struct WorkspaceLayout {
     size_t shard_cells; // int32[max_items][P+1]: per-shard slot sizes (fused pooling)
     size_t part;        // double[max_parts][P][C+2]: partial sums per shard (fused pooling,
                         // stride C+1) or per chunk (chunked pooling, stride C+2)
+    size_t coords32;    // float[N][4]: float32 copy of 16-bit coordinates (else unused)
+    size_t feat32;      // float[N][C]: float32 copy of 16-bit features (else unused)
     size_t total;
     int64_t max_chunks;
     int64_t max_pool_chunks;
@@ -68,7 +70,8 @@ struct WorkspaceLayout {
 constexpr int64_t kGangPulsesPerShard = 2048;
 static_assert(kPoolChunk >= 2 * kGangPulsesPerShard, "pooling chunks would outgrow the records");
 
-WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C);
+WorkspaceLayout workspace_layout(int64_t B, int64_t N, int P, int C, int coords_dtype = 0,
+                                 int features_dtype = 0);
 int64_t sample_max_items(int64_t B, int64_t N);
 
 struct SampleArgs {
@@ -227,6 +230,11 @@ hipError_t launch_pool_backward(const PoolBwdArgs& a, int64_t B, hipStream_t s);
 // device, never allocated.
 constexpr size_t kNoAllocBytes = (size_t)64 << 20;
 hipError_t noalloc_scratch(void** ptr);
+
+// dst_a[i] = float32 value of the 16-bit src_a[i] (dtype 1: binary16, 2:
+// bfloat16) for i < na, and the same for b; one launch, exact.
+hipError_t launch_upcast(const void* src_a, int64_t na, int dtype_a, float* dst_a,
+                         const void* src_b, int64_t nb, int dtype_b, float* dst_b, hipStream_t s);
 
 hipError_t launch_random_start(const int64_t* offsets, int64_t B, uint64_t seed, uint64_t step,
                                int32_t* start_idx, hipStream_t s);

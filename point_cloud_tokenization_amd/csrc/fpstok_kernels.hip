@@ -3537,6 +3537,48 @@ __global__ __launch_bounds__(kSortT) void pool_backward_kernel(PoolBwdArgs a) {
     }
 }
 
+// -------------------------------------------- low-precision inputs (next)
+
+// The float32 value of a 16-bit input element: binary16 through the
+// hardware conversion (exact: every binary16 value is a float32 value),
+// bfloat16 as the upper half of a float32.
+__device__ __forceinline__ float upcast16(uint16_t h, int dtype) {
+    return dtype == 1 ? (float)__builtin_bit_cast(_Float16, h) : __uint_as_float((uint32_t)h << 16);
+}
+
+// dst_a[i] = upcast16(src_a[i]) for i < na, then the same for b, one
+// grid-stride pass over both arrays; four elements per thread and step (one
+// 8-byte load when the array is 8-byte aligned, which 16-bit coordinates
+// are), single elements at the ends.
+__global__ __launch_bounds__(256) void upcast_kernel(const uint16_t* __restrict__ sa, int64_t na,
+                                                     int da, float* __restrict__ oa,
+                                                     const uint16_t* __restrict__ sb, int64_t nb,
+                                                     int db, float* __restrict__ ob) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < na + nb;
+         i += stride) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t q = i + u;
+            if (q < na)
+                oa[q] = upcast16(sa[q], da);
+            else if (q < na + nb)
+                ob[q - na] = upcast16(sb[q - na], db);
+        }
+    }
+}
+
+hipError_t launch_upcast(const void* src_a, int64_t na, int dtype_a, float* dst_a,
+                         const void* src_b, int64_t nb, int dtype_b, float* dst_b, hipStream_t s) {
+    const int64_t total = na + nb;
+    if (total <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + 1023) / 1024, 8192);
+    hipLaunchKernelGGL(upcast_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const uint16_t*)src_a, na, dtype_a, dst_a, (const uint16_t*)src_b, nb,
+                       dtype_b, dst_b);
+    return hipGetLastError();
+}
+
 // ----------------------------------------------- random FPS start (next)
 
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds, each

@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fpstok.h")
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP, EDEVICE = 0, 1, 2, 3, 4, 5
 VORONOI, KNN = 0, 1
+F32, F16, BF16 = 0, 1, 2  # fpstok_dtype
 MAX_PATCHES, MAX_K, MAX_LLOYD = 1024, 64, 1000
 NOALLOC_MAX_WORKSPACE = 64 << 20  # FPSTOK_NOALLOC_MAX_WORKSPACE
 
@@ -36,7 +37,8 @@ class Batch(ctypes.Structure):
     _fields_ = [("coords", ctypes.c_void_p), ("features", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("num_events", ctypes.c_int64),
                 ("num_points", ctypes.c_int64), ("num_features", ctypes.c_int32),
-                ("charge_col", ctypes.c_int32), ("max_event_points", ctypes.c_int64)]
+                ("charge_col", ctypes.c_int32), ("max_event_points", ctypes.c_int64),
+                ("coords_dtype", ctypes.c_int32), ("features_dtype", ctypes.c_int32)]
 
 
 class Params(ctypes.Structure):
@@ -76,10 +78,11 @@ def lib():
         L.fpstok_device_status.argtypes = [vp, sz, vp]
         L.fpstok_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
         L.fpstok_debug_set_spin_limit.restype = None
+        L.fpstok_upcast.argtypes = [vp, i64, i32, vp, vp]
         for f in ("fpstok_sample", "fpstok_assign", "fpstok_knn", "fpstok_lloyd",
                   "fpstok_pool", "fpstok_tokenize", "fpstok_validate", "fpstok_pack",
                   "fpstok_unpack", "fpstok_pool_backward", "fpstok_random_start",
-                  "fpstok_device_status", "fpstok_tokenize_noalloc"):
+                  "fpstok_device_status", "fpstok_tokenize_noalloc", "fpstok_upcast"):
             getattr(L, f).restype = ctypes.c_int
         L.fpstok_status_string.argtypes = [ctypes.c_int]
         L.fpstok_status_string.restype = ctypes.c_char_p
@@ -136,26 +139,54 @@ def _need(t, dtype, name, dev=None):
     return t
 
 
+def _dtype_code(t, name):
+    import torch
+
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError("%s must be float32, float16 or bfloat16, got %s" % (name, t.dtype))
+    return codes[t.dtype]
+
+
 def make_batch(coords, offsets, features=None, charge_col=-1, max_event_points=0):
-    """A Batch struct (plus the tensors it points into, kept alive).
+    """A Batch struct over the given tensors (which the caller keeps alive).
+    coords and features may each be float32, float16 or bfloat16; the library
+    upcasts 16-bit inputs exactly to float32 before using them.
     max_event_points: optional host-side bound on the pulses of any event (0:
     unknown); see fpstok_batch in include/fpstok.h."""
     import torch
 
-    _need(coords, torch.float32, "coords")
+    cd = _dtype_code(coords, "coords")
+    _need(coords, coords.dtype, "coords")
     _need(offsets, torch.int64, "offsets", coords.device)
     if coords.dim() != 2 or coords.shape[1] != 4:
         raise ValueError("coords must be [N,4]")
-    C = 0
+    C, fd = 0, F32
     if features is not None:
-        _need(features, torch.float32, "features", coords.device)
+        fd = _dtype_code(features, "features")
+        _need(features, features.dtype, "features", coords.device)
         if features.dim() != 2 or features.shape[0] != coords.shape[0]:
             raise ValueError("features must be [N,C]")
         C = features.shape[1]
     bt = Batch(coords.data_ptr(), features.data_ptr() if features is not None else None,
                offsets.data_ptr(), offsets.numel() - 1, coords.shape[0], C, charge_col,
-               int(max_event_points))
+               int(max_event_points), cd, fd)
     return bt
+
+
+def upcast(src, out, stream=None):
+    """out[i] = float32 value of the float16 / bfloat16 src[i] (exact)."""
+    import torch
+
+    code = _dtype_code(src, "src")
+    if code == F32:
+        raise TypeError("src must be float16 or bfloat16")
+    _need(src, src.dtype, "src")
+    _need(out, torch.float32, "out", src.device)
+    if out.numel() != src.numel():
+        raise ValueError("out must have as many elements as src")
+    _check(lib().fpstok_upcast(_ptr(src), src.numel(), code, _ptr(out),
+                               _stream_handle(stream)), "fpstok_upcast")
 
 
 def make_params(num_patches=128, k=16, lloyd_iters=0, assign_mode=VORONOI, pool_weighted=1):

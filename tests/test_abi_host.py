@@ -37,14 +37,22 @@ def test_only_the_abi_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.fpstok_version() == 2
+    assert L.fpstok_version() == 3
     assert L.fpstok_status_string(0) == b"ok"
     assert L.fpstok_status_string(2) == b"workspace too small"
     assert L.fpstok_status_string(99) == b"unknown status"
 
 
-def _bt(B=3, N=100, coords=0x10000, offsets=0x20000, features=0x30000, C=6, q=5):
-    return F.Batch(coords, features, offsets, B, N, C, q)
+def _bt(B=3, N=100, coords=0x10000, offsets=0x20000, features=0x30000, C=6, q=5, cd=F.F32,
+        fd=F.F32):
+    return F.Batch(coords, features, offsets, B, N, C, q, 0, cd, fd)
+
+
+def test_batch_struct_matches_the_header():
+    """coords, features, offsets, B, N, C, charge_col, max_event_points,
+    coords_dtype, features_dtype: 64 bytes, the dtypes last."""
+    assert ctypes.sizeof(F.Batch) == 64
+    assert F.Batch.coords_dtype.offset == 56 and F.Batch.features_dtype.offset == 60
 
 
 def test_workspace_size(L):
@@ -54,6 +62,13 @@ def test_workspace_size(L):
     b = F.workspace_size(_bt(B=4, N=8500), pr)
     assert a > 12 * 4250 and b > a and a % 256 == 0
     assert L.fpstok_workspace_size(None, None) == 0
+    # 16-bit inputs add their float32 copies: N*4 floats of coordinates, N*C
+    # of features (each rounded up to 256 bytes)
+    up = lambda n: (n + 255) // 256 * 256
+    assert F.workspace_size(_bt(B=4, N=4250, cd=F.F16), pr) == a + up(4250 * 16)
+    assert F.workspace_size(_bt(B=4, N=4250, fd=F.BF16), pr) == a + up(4250 * 6 * 4)
+    assert F.workspace_size(_bt(B=4, N=4250, cd=F.BF16, fd=F.F16), pr) == \
+        a + up(4250 * 16) + up(4250 * 24)
 
 
 FAKE = ctypes.c_void_p(0x40000)
@@ -78,12 +93,34 @@ def _sample(L, bt, pr, ws_bytes=1 << 30, cidx=FAKE, cen=FAKE, tc=FAKE, ws=FAKE):
     (lambda bt, pr: setattr(bt, "offsets", None), F.EINVAL),
     (lambda bt, pr: setattr(bt, "coords", None), F.EINVAL),
     (lambda bt, pr: setattr(bt, "coords", 0x10004), F.EINVAL),  # misaligned
+    (lambda bt, pr: setattr(bt, "coords_dtype", 3), F.EINVAL),
+    (lambda bt, pr: setattr(bt, "coords_dtype", -1), F.EINVAL),
+    (lambda bt, pr: setattr(bt, "features_dtype", 3), F.EINVAL),
+    # 16-bit coordinates need 8-byte alignment only
+    (lambda bt, pr: (setattr(bt, "coords_dtype", F.F16), setattr(bt, "coords", 0x10004)),
+     F.EINVAL),
 ])
 def test_sample_rejects_bad_arguments(L, mutate, expect):
     bt, pr = _bt(), F.make_params()
     mutate(bt, pr)
     assert _sample(L, bt, pr) == expect
     assert L.fpstok_last_error() != b""
+
+
+def test_upcast_rejects_bad_arguments(L):
+    assert L.fpstok_upcast(FAKE, -1, F.F16, FAKE, None) == F.EINVAL
+    assert L.fpstok_upcast(FAKE, 4, F.F32, FAKE, None) == F.EINVAL
+    assert L.fpstok_upcast(FAKE, 4, 3, FAKE, None) == F.EINVAL
+    assert L.fpstok_upcast(None, 4, F.F16, FAKE, None) == F.EINVAL
+    assert L.fpstok_upcast(FAKE, 4, F.BF16, None, None) == F.EINVAL
+    assert L.fpstok_upcast(ctypes.c_void_p(0x40001), 4, F.BF16, FAKE, None) == F.EINVAL
+    assert L.fpstok_upcast(FAKE, 4, F.BF16, ctypes.c_void_p(0x40002), None) == F.EINVAL
+    assert L.fpstok_upcast(None, 0, F.F16, None, None) == F.OK  # nothing to do
+
+
+def test_validate_rejects_unknown_dtypes(L):
+    assert L.fpstok_validate(ctypes.byref(_bt(B=0, N=0, cd=5)), None) == F.EINVAL
+    assert L.fpstok_validate(ctypes.byref(_bt(B=0, N=0, fd=-2)), None) == F.EINVAL
 
 
 def test_sample_rejects_missing_outputs_and_workspace(L):
@@ -173,6 +210,8 @@ def test_python_binding_refuses_cpu_tensors():
     off = torch.tensor([0, 4], dtype=torch.int64)
     with pytest.raises(ValueError):
         F.make_batch(x, off)
+    with pytest.raises(TypeError):
+        F.make_batch(x.double(), off)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

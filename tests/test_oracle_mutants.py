@@ -53,6 +53,9 @@ MUTANTS = [
      "uint32_t in[4] = {(uint32_t)step, (uint32_t)(step >> 32), (uint32_t)b,\n                          (uint32_t)((uint64_t)b >> 32)};"),
     ("random_start_word1", "(int32_t)(((uint64_t)out[0] * (uint64_t)n) >> 32)",
      "(int32_t)(((uint64_t)out[1] * (uint64_t)n) >> 32)"),
+    ("binary16_subnormals_flushed", "        v = ldexpf((float)m, -24);", "        v = 0.0f;"),
+    ("bfloat16_rounded_not_upcast", "    uint32_t bits = (uint32_t)h << 16;\n    float v;",
+     "    uint32_t bits = ((uint32_t)h << 16) | 0x8000u;\n    float v;"),
     ("backward_ignores_weight", "    int32_t wcol = weighted != 0 ? charge_col : -1;", "    int32_t wcol = -1;"),
     ("backward_drops_weight_term", "                    gi[wcol] += s / W[j];", "                    (void)s;"),
     ("backward_unit_weight", "for (int32_t c = 0; c < C; ++c) gi[c] += (double)g[c] * w / W[j];",
@@ -76,6 +79,8 @@ PIN_CALLS = [
     lambda m: nxt.test_random_start_mapping_and_spread(m),
     lambda m: nxt.test_random_start_from_the_known_answer_vector(m),
     lambda m: nxt.test_random_start_counter_layout(m),
+    lambda m: nxt.test_upcast_binary16_exhaustive(m),
+    lambda m: nxt.test_upcast_bfloat16_exhaustive(m),
     lambda m: [pins.test_closed_forms(m, c) for c in pins._cases()],
     lambda m: pins.test_identical_cloud_knn_pool_lloyd(m),
     lambda m: [pins.test_fps_and_assign_brute_force(m, s) for s in (1, 2, 3)],

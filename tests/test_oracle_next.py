@@ -14,6 +14,7 @@ Each is checked against something other than itself:
     the incoming gradient.
 """
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -301,3 +302,72 @@ def test_random_start_counter_layout(oracle_mod):
             w0 = _philox_py([b & 0xFFFFFFFF, b >> 32, step & 0xFFFFFFFF, step >> 32],
                             [seed & 0xFFFFFFFF, seed >> 32])[0]
             assert s[b] == (w0 * int(n[b])) >> 32, (seed, step, b)
+
+
+# ------------------------------------------------ low-precision inputs
+
+def test_upcast_binary16_exhaustive(oracle_mod):
+    """Every binary16 bit pattern against numpy's IEEE conversion (an
+    independent implementation; exact for every value, subnormals included)."""
+    h = np.arange(65536, dtype=np.uint16)
+    got = oracle_mod.upcast(h, oracle_mod.F16)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.isnan(got[nan]).all()
+    # hand-checked patterns: 1.0, -2.0, the smallest subnormal 2^-24, the
+    # largest finite 65504, +infinity
+    for bits, val in ((0x3C00, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -24), (0x7BFF, 65504.0),
+                      (0x7C00, float("inf"))):
+        assert oracle_mod.upcast(np.array([bits], np.uint16), oracle_mod.F16)[0] == val
+
+
+def _bf16_value(h):
+    """bfloat16 from its definition: sign, 8-bit exponent biased by 127,
+    7-bit fraction; exponent 0 = zero and subnormals, 255 = inf / NaN."""
+    s = -1.0 if h >> 15 else 1.0
+    e = (h >> 7) & 0xFF
+    m = h & 0x7F
+    if e == 0:
+        return s * math.ldexp(m, -133)          # m / 128 * 2^-126
+    if e == 255:
+        return s * math.inf if m == 0 else math.nan
+    return s * math.ldexp(128 + m, e - 134)     # (1 + m / 128) * 2^(e - 127)
+
+
+def test_upcast_bfloat16_exhaustive(oracle_mod):
+    h = np.arange(65536, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):  # the NaN patterns
+        got = oracle_mod.upcast(h, oracle_mod.BF16).astype(np.float64)
+    ref = np.array([_bf16_value(int(x)) for x in h])
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.isnan(got[nan]).all()
+    with pytest.raises(RuntimeError):
+        oracle_mod.upcast(h[:4], 3)
+
+
+def test_tokenize_on_upcast_inputs_is_the_float32_path(oracle_mod):
+    """Low-precision inputs are the float32 inputs of equal value: the
+    tokenizer on upcast binary16 / bfloat16 coordinates and features equals
+    the tokenizer on the same values written directly in float32 (numpy's
+    binary16 conversion; bfloat16 by rounding float32 to its top 16 bits)."""
+    from point_cloud_tokenization_amd import synth
+
+    b = synth.icecube_events([40, 300, 900, 2], 71, C=6)
+    x, f, off = b["coords"], b["features"], b["offsets"]
+    x16 = x.astype(np.float16)
+    f16 = f.astype(np.float16)
+    xb = ((x.view(np.uint32) + 0x8000) >> 16).astype(np.uint16)  # round half up to bfloat16
+    fb = ((f.view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
+    kw = dict(P=128, mode=0, L=1, weighted=True, charge_col=5)
+    for (xs, fs, dt, x32, f32) in (
+            (x16.view(np.uint16), f16.view(np.uint16), oracle_mod.F16,
+             x16.astype(np.float32), f16.astype(np.float32)),
+            (xb, fb, oracle_mod.BF16, (xb.astype(np.uint32) << 16).view(np.float32),
+             (fb.astype(np.uint32) << 16).view(np.float32))):
+        got = oracle_mod.tokenize(oracle_mod.upcast(xs, dt), oracle_mod.upcast(fs, dt), off, **kw)
+        ref = oracle_mod.tokenize(x32, f32, off, **kw)
+        for key in got:
+            if got[key] is not None:
+                np.testing.assert_array_equal(got[key], ref[key], err_msg=key)

@@ -1,7 +1,9 @@
 """fpstok_tokenize_noalloc (the library's fixed scratch region as workspace)
 against fpstok_tokenize (a caller workspace) through the C ABI: two calls in
-a row on one GPU, the second on a smaller batch, in every mode; every output
-must be identical (same kernels, same inputs)."""
+a row on one GPU, the second on a smaller batch, in every mode, and once with
+float16 coordinates and bfloat16 features (their float32 copies staged in the
+scratch region too); every output must be identical (same kernels, same
+inputs)."""
 import numpy as np
 import pytest
 
@@ -22,7 +24,7 @@ def _outputs(b, P, mode, k, dev):
                 pooled=mk((B, P, C), torch.float32), cell_count=mk((B, P), torch.int32))
 
 
-def _run(b, P, mode, k, L, noalloc):
+def _run(b, P, mode, k, L, noalloc, half=False):
     import torch
 
     from point_cloud_tokenization_amd import fpstok as F
@@ -31,6 +33,8 @@ def _run(b, P, mode, k, L, noalloc):
     x = torch.from_numpy(b["coords"]).to(dev)
     f = torch.from_numpy(b["features"]).to(dev)
     off = torch.from_numpy(b["offsets"]).to(dev)
+    if half:
+        x, f = x.to(torch.float16), f.to(torch.bfloat16)
     bt = F.make_batch(x, off, f, synth.CHARGE_COL, int(np.diff(b["offsets"]).max()))
     pr = F.make_params(P, k, L, mode, 1)
     o = _outputs(b, P, mode, k, dev)
@@ -46,13 +50,14 @@ def _run(b, P, mode, k, L, noalloc):
     return {key: v.cpu().numpy() for key, v in o.items() if v is not None}
 
 
-@pytest.mark.parametrize("first,second,mode,k,L", [
-    ("icecube_highE_b512", "icecube_b64_voronoi", 0, 16, 0),
-    ("icecube_b256_lloyd3", "tiny_uniform", 0, 16, 2),
-    ("icecube_b64_knn16", "tiny_uniform", 1, 16, 0),
-    ("icecube_b256_lloyd3", "icecube_b64_knn16", 1, 8, 1),
+@pytest.mark.parametrize("first,second,mode,k,L,half", [
+    ("icecube_highE_b512", "icecube_b64_voronoi", 0, 16, 0, False),
+    ("icecube_b256_lloyd3", "tiny_uniform", 0, 16, 2, False),
+    ("icecube_b64_knn16", "tiny_uniform", 1, 16, 0, False),
+    ("icecube_b256_lloyd3", "icecube_b64_knn16", 1, 8, 1, False),
+    ("icecube_b256_lloyd3", "icecube_b64_voronoi", 0, 16, 1, True),
 ])
-def test_noalloc_matches_workspace_call(first, second, mode, k, L):
+def test_noalloc_matches_workspace_call(first, second, mode, k, L, half):
     import torch
 
     if not torch.cuda.is_available():
@@ -60,8 +65,9 @@ def test_noalloc_matches_workspace_call(first, second, mode, k, L):
     for name in (first, second):  # the second batch is the smaller one
         b = synth.make_batch(name, synth.parity_seed(name, 3))
         P = synth.WORKLOADS[name]["P"]
-        print("no-alloc case %s P=%d mode=%d k=%d L=%d" % (name, P, mode, k, L), flush=True)
-        ref = _run(b, P, mode, k, L, noalloc=False)
-        got = _run(b, P, mode, k, L, noalloc=True)
+        print("no-alloc case %s P=%d mode=%d k=%d L=%d half=%d" % (name, P, mode, k, L, half),
+              flush=True)
+        ref = _run(b, P, mode, k, L, noalloc=False, half=half)
+        got = _run(b, P, mode, k, L, noalloc=True, half=half)
         for key in ref:
             np.testing.assert_array_equal(got[key], ref[key], err_msg="%s %s" % (name, key))

@@ -371,7 +371,22 @@ struct Stage {
 constexpr int kListCap = 64;  // entries of the candidate list (one per lane)
 constexpr int kNoEntry = (int)0xBF800000;  // bit pattern of -1.0f: an empty entry
 
-// LDS of the single-workgroup FPS.
+// LDS of a single-workgroup FPS.  The offers of an exchange are
+// double-buffered by exchange parity: a wave that runs ahead into the next
+// exchange writes the other buffer, and one exchange later every wave has
+// passed a barrier after its last read of this one.
+struct SingleLds {
+    int ov[2][kFpsW][64];      // offered distances (float bits), in lane order per wave
+    int oi[2][kFpsW][64];      // offered pulse indices
+    float4 oc[2][kFpsW][64];   // offered coordinates
+    int4 wc[2];                // offers of each wave
+    int4 wb[2];                // bound of each wave
+    FpsSlot list[kListCap];    // the kept list when the offers do not fit one
+    int wd[kFpsW];             // each wave's largest kept entry left out of a full list
+    uint32_t bm[kFpsW][64];    // per-wave selection bitmap (degenerate case only)
+};
+
+// LDS of a shard's own exchange in the gang FPS.
 struct FpsLds {
     FpsSlot wl[kFpsW][64];    // each wave's contribution to an exchange
     FpsSlot list[kListCap];   // the workgroup's new candidate list
@@ -403,6 +418,24 @@ __device__ __forceinline__ int first_unselected_lds(uint32_t* bm, const int* s_s
     return first_unselected(bm[lane]);
 }
 
+// Lowest pulse index that no iteration 0..j has selected (the caller knows
+// one exists below 2048); s_sel[0..j] holds those selections.  Built per
+// wave in LDS with atomic ORs; used only when every pulse has minimum
+// distance 0.
+__device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_sel, int j) {
+    const int lane = lane_id();
+    bm[lane] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    for (int q = lane; q <= j; q += 64) {
+        const int v = s_sel[q];
+        if (v >= 0 && v < 2048) atomicOr(&bm[v >> 5], 1u << (v & 31));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    return first_unselected(bm[lane]);
+}
+
 // FPS of one event of at most 256*M pulses by one workgroup, every pulse in
 // registers (lane-blocked: thread t owns pulses t*M .. t*M+M-1).
 //
@@ -417,13 +450,20 @@ __device__ __forceinline__ int first_unselected_lds(uint32_t* bm, const int* s_s
 //  * every group of pulses -- a lane's M pulses, or a pair of lanes when
 //    M = 1 -- offers its farthest pulse (lowest index on ties), and its
 //    second largest distance bounds the rest of the group;
-//  * a wave keeps the offers >= the largest second distance of the wave and
-//    writes them, in lane order, to LDS; U is the largest wave bound;
-//  * after a barrier every wave reads the offered distances: the best offer
-//    is this iteration's argmax (the global maximum is always offered), and
-//    the offers > U, in pulse order, become the new list, each wave writing
-//    its own offers from registers.  If more than 64 remain, the first 64
-//    are kept and U is raised to the largest of the others.
+//  * a wave keeps the offers >= the largest second distance of the wave
+//    (padding never offers) and writes them, in lane order, to LDS with
+//    their count; U is the largest wave bound;
+//  * after a barrier every wave reads the counts and bounds; when all the
+//    offers fit the list (the usual case) lane l reads offer l of the
+//    waves' concatenation, which is in pulse order, and that is the new
+//    list: it holds every pulse > U (such a pulse is the unique farthest of
+//    its group and beats its wave's bound), offers <= U in it never win
+//    while the list beats U, and its best entry is this iteration's argmax
+//    (the global maximum is offered, and the lowest index among equal
+//    maxima is the farthest of the lowest group holding one).  Otherwise
+//    the offers > U become the list in pulse order through a second
+//    barrier; beyond 64 the first 64 are kept and U is raised to the
+//    largest of the others.
 // Every wave holds the same list (lane l: entry l) and takes the same
 // decisions; between exchanges the waves never synchronise.  One wave on a
 // SIMD issues a vector instruction only every few cycles, so a run of list
@@ -431,12 +471,12 @@ __device__ __forceinline__ int first_unselected_lds(uint32_t* bm, const int* s_s
 // wave maximum, the pulses' update, a ballot and five lane reads for the
 // winner; the centroid stays in scalar registers.  U is kept >= 0, so a
 // maximum of 0 (every pulse selected or duplicate) always goes through an
-// exchange, where the "lowest unselected index" rule is applied.  The
-// selection order is buffered in a register (lane j mod 64 holds iteration
-// j) and flushed to LDS by wave 0 every 64 iterations.
+// exchange, where the "lowest unselected index" rule is applied.  Every
+// wave writes iteration j's selection to s_sel[j] (the same value from
+// all: one LDS store, no branch).
 template <int M>
 __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64_t off, int n,
-                                           int s0, FpsLds& L, int* s_sel, int* s_asg,
+                                           int s0, SingleLds& L, int* s_sel, int* s_asg,
                                            const Stage& st) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -463,8 +503,8 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
     float lv = -1.0f, lx = 0.f, ly = 0.f, lz = 0.f, lt = 0.f;
     int li = 0;
     int U = INT32_MAX;  // bound on every unlisted pulse (float bits); no list yet
+    int ex = 0;         // exchanges so far (their parity picks the offer buffer)
 
-    int selv = 0;
     int s = s0;
     float cx, cy, cz, ct;  // the newest centroid (uniform)
     {
@@ -484,12 +524,11 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
         // ---- a run of iterations decided by the list
         int wm;
         for (;;) {
-            selv = lane == (j & 63) ? s : selv;
-            if (__builtin_expect((j & 63) == 63 && wave == 0, 0)) s_sel[j - 63 + lane] = selv;
-            {
-                const float d = sqd(lx, ly, lz, lt, cx, cy, cz, ct);
-                lv = d < lv ? d : lv;
-            }
+            s_sel[j] = s;
+            // distances are >= +0, so their bit patterns order as signed
+            // integers, and an empty entry (-1.0, negative) stays empty
+            lv = __int_as_float(min(__float_as_int(sqd(lx, ly, lz, lt, cx, cy, cz, ct)),
+                                    __float_as_int(lv)));
             wm = wave_max_i(__float_as_int(lv));
 #pragma unroll
             for (int k = 0; k < M; ++k) {
@@ -507,12 +546,15 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             cy = readlane_f(ly, Lw);
             cz = readlane_f(lz, Lw);
             ct = readlane_f(lt, Lw);
-            if (__builtin_expect(j + 1 == P || wm <= U, 0)) break;
+            if (__builtin_expect(wm <= U, 0)) break;
+            if (__builtin_expect(j + 1 == P, 0)) break;
             ++j;
         }
         if (j + 1 == P) break;
 
         // ---- exchange
+        const int par = ex & 1;
+        ++ex;
         int b1 = INT32_MIN, b2 = INT32_MIN, k1 = 0;
         float bx = 0.f, by = 0.f, bz = 0.f, bt = 0.f;
 #pragma unroll
@@ -535,107 +577,147 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             b2 = min(b1, q);
         }
         const int wb2 = wave_max_i(b2);
-        const bool offer = lead && b1 >= wb2;
+        const bool offer = lead && b1 >= wb2 && b1 >= 0;
         const uint64_t ob = ballot(offer);
         if (offer) {
-            FpsSlot& o = L.wl[wave][mbcnt(ob)];
-            o.v = __int_as_float(b1);
-            o.i = lbase + k1;
-            o.c = make_float4(bx, by, bz, bt);
+            const int q = mbcnt(ob);
+            L.ov[par][wave][q] = b1;
+            L.oi[par][wave][q] = lbase + k1;
+            L.oc[par][wave][q] = make_float4(bx, by, bz, bt);
         }
         if (lane == 0) {
-            L.wc[wave] = __popcll(ob);
-            L.wb[wave] = wb2;
+            reinterpret_cast<int*>(&L.wc[par])[wave] = __popcll(ob);
+            reinterpret_cast<int*>(&L.wb[par])[wave] = wb2;
         }
         lds_barrier();
-        // every wave: U, this iteration's argmax (largest offer, then lowest
-        // (wave, position) = lowest pulse index) and the list layout
-        int Un = 0;
-        int rb = INT32_MIN, re = 0;
-        int kcnt[kFpsW];
-#pragma unroll
-        for (int w = 0; w < kFpsW; ++w) {
-            Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wb[w]));
-        }
-#pragma unroll
-        for (int w = 0; w < kFpsW; ++w) {
-            const int cw = __builtin_amdgcn_readfirstlane(L.wc[w]);
-            const int v = lane < cw ? __float_as_int(L.wl[w][lane < cw ? lane : 0].v) : INT32_MIN;
-            const bool g = v > rb;
-            rb = g ? v : rb;
-            re = g ? w : re;
-            kcnt[w] = __popcll(ballot(v > Un));
-        }
-        const int gm = wave_max_i(rb);
+        int cw[kFpsW], Un = 0, tot = 0;
         {
-            const uint64_t m = ballot(rb == gm);
-            int Lw, ew;
-            if (__popcll(m) == 1) {
-                Lw = (int)__builtin_ctzll(m);
-                ew = readlane_i(re, Lw);
-            } else {
-                const int f = wave_min_i(rb == gm ? re * 64 + lane : INT32_MAX);
-                Lw = f & 63;
-                ew = f >> 6;
-            }
-            if (gm <= 0) {
-                s = min(first_unselected_lds(L.bm[wave], s_sel, selv, j), n - 1);
-                const float4 q = p[s];
-                cx = readlane_f(q.x, 0);
-                cy = readlane_f(q.y, 0);
-                cz = readlane_f(q.z, 0);
-                ct = readlane_f(q.w, 0);
-            } else {
-                const FpsSlot& o = L.wl[ew][Lw];
-                s = min(max((int)__builtin_amdgcn_readfirstlane(o.i), 0), n - 1);
-                cx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.x)));
-                cy = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.y)));
-                cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.z)));
-                ct = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(o.c.w)));
-            }
+            const int4 c4 = L.wc[par];
+            const int4 b4 = L.wb[par];
+            cw[0] = __builtin_amdgcn_readfirstlane(c4.x);
+            cw[1] = __builtin_amdgcn_readfirstlane(c4.y);
+            cw[2] = __builtin_amdgcn_readfirstlane(c4.z);
+            cw[3] = __builtin_amdgcn_readfirstlane(c4.w);
+            Un = max(max(Un, (int)__builtin_amdgcn_readfirstlane(b4.x)),
+                     max((int)__builtin_amdgcn_readfirstlane(b4.y),
+                         max((int)__builtin_amdgcn_readfirstlane(b4.z),
+                             (int)__builtin_amdgcn_readfirstlane(b4.w))));
+            tot = cw[0] + cw[1] + cw[2] + cw[3];
         }
-        // new list: the offers > U in (wave, position) order, each wave
-        // writing its own from registers; beyond 64 entries the rest only
-        // raise U
-        int base = 0, C = 0;
+        int gm;
+        if (__builtin_expect(tot <= kListCap, 1)) {
+            // the new list: lane l holds offer l of the concatenation
+            int w = 0, q = lane;
 #pragma unroll
-        for (int w = 0; w < kFpsW; ++w) {
-            base += w < wave ? kcnt[w] : 0;
-            C += kcnt[w];
-        }
-        const bool keep = offer && b1 > Un;
-        const int pos = base + mbcnt(ballot(keep));
-        if (keep && pos < kListCap) {
-            FpsSlot& o = L.list[pos];
-            o.v = __int_as_float(b1);
-            o.i = lbase + k1;
-            o.c = make_float4(bx, by, bz, bt);
-        }
-        if (C > kListCap) {
-            const int d = wave_max_i(keep && pos >= kListCap ? b1 : INT32_MIN);
-            // every wave needs the same U: combine the per-wave maxima
-            if (lane == 0) L.wd[wave] = d;
-            lds_barrier();
-#pragma unroll
-            for (int w = 0; w < kFpsW; ++w)
-                Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wd[w]));
-        }
-        lds_barrier();
-        U = __builtin_amdgcn_readfirstlane(Un);
-        if (lane < C) {
-            const FpsSlot o = L.list[lane];
-            lv = o.v;
-            li = o.i;
-            lx = o.c.x;
-            ly = o.c.y;
-            lz = o.c.z;
-            lt = o.c.w;
+            for (int r = 0; r < kFpsW - 1; ++r) {
+                const bool on = w == r && q >= cw[r];
+                q = on ? q - cw[r] : q;
+                w = on ? r + 1 : w;
+            }
+            if (lane < tot) {
+                lv = __int_as_float(L.ov[par][w][q]);
+                li = L.oi[par][w][q];
+                const float4 c = L.oc[par][w][q];
+                lx = c.x;
+                ly = c.y;
+                lz = c.z;
+                lt = c.w;
+            } else {
+                lv = -1.0f;
+            }
+            U = __builtin_amdgcn_readfirstlane(Un);
+            gm = wave_max_i(__float_as_int(lv));
+            if (gm > 0) {
+                const int Lw = (int)__builtin_ctzll(ballot(__float_as_int(lv) == gm));
+                s = readlane_i(li, Lw);
+                cx = readlane_f(lx, Lw);
+                cy = readlane_f(ly, Lw);
+                cz = readlane_f(lz, Lw);
+                ct = readlane_f(lt, Lw);
+            }
         } else {
-            lv = -1.0f;
+            // every wave: this iteration's argmax (largest offer, then lowest
+            // (wave, position) = lowest pulse index) and the list layout
+            int rb = INT32_MIN, re = 0;
+            int kcnt[kFpsW];
+#pragma unroll
+            for (int w = 0; w < kFpsW; ++w) {
+                const int v = lane < cw[w] ? L.ov[par][w][lane] : INT32_MIN;
+                const bool g = v > rb;
+                rb = g ? v : rb;
+                re = g ? w : re;
+                kcnt[w] = __popcll(ballot(v > Un));
+            }
+            gm = wave_max_i(rb);
+            if (gm > 0) {
+                const uint64_t m = ballot(rb == gm);
+                int Lw, ew;
+                if (__popcll(m) == 1) {
+                    Lw = (int)__builtin_ctzll(m);
+                    ew = readlane_i(re, Lw);
+                } else {
+                    const int f = wave_min_i(rb == gm ? re * 64 + lane : INT32_MAX);
+                    Lw = f & 63;
+                    ew = f >> 6;
+                }
+                s = min(max((int)__builtin_amdgcn_readfirstlane(L.oi[par][ew][Lw]), 0), n - 1);
+                const float4 c = L.oc[par][ew][Lw];
+                cx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c.x)));
+                cy = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c.y)));
+                cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c.z)));
+                ct = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c.w)));
+            }
+            // new list: the offers > U in (wave, position) order, each wave
+            // writing its own from registers; beyond 64 entries the rest only
+            // raise U
+            int base = 0, C = 0;
+#pragma unroll
+            for (int w = 0; w < kFpsW; ++w) {
+                base += w < wave ? kcnt[w] : 0;
+                C += kcnt[w];
+            }
+            const bool keep = offer && b1 > Un;
+            const int pos = base + mbcnt(ballot(keep));
+            if (keep && pos < kListCap) {
+                FpsSlot& o = L.list[pos];
+                o.v = __int_as_float(b1);
+                o.i = lbase + k1;
+                o.c = make_float4(bx, by, bz, bt);
+            }
+            if (C > kListCap) {
+                const int d = wave_max_i(keep && pos >= kListCap ? b1 : INT32_MIN);
+                // every wave needs the same U: combine the per-wave maxima
+                if (lane == 0) L.wd[wave] = d;
+                lds_barrier();
+#pragma unroll
+                for (int w = 0; w < kFpsW; ++w)
+                    Un = max(Un, (int)__builtin_amdgcn_readfirstlane(L.wd[w]));
+            }
+            lds_barrier();
+            U = __builtin_amdgcn_readfirstlane(Un);
+            if (lane < C) {
+                const FpsSlot o = L.list[lane];
+                lv = o.v;
+                li = o.i;
+                lx = o.c.x;
+                ly = o.c.y;
+                lz = o.c.z;
+                lt = o.c.w;
+            } else {
+                lv = -1.0f;
+            }
+        }
+        if (gm <= 0) {
+            // every pulse has minimum distance 0: the lowest unselected index
+            s = min(first_unselected_sel(L.bm[wave], s_sel, j), n - 1);
+            const float4 q = p[s];
+            cx = readlane_f(q.x, 0);
+            cy = readlane_f(q.y, 0);
+            cz = readlane_f(q.z, 0);
+            ct = readlane_f(q.w, 0);
         }
         ++j;
     }
-    if (wave == 0 && lane <= (j & 63)) s_sel[(j & ~63) + lane] = selv;
     if (a.assign) {
 #pragma unroll
         for (int k = 0; k < M; ++k) {
@@ -664,7 +746,7 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
 }
 
 __device__ __forceinline__ void fps_single_dispatch(const SampleArgs& a, int64_t b, int64_t off,
-                                                    int n, int s0, FpsLds& L, int* ss, int* sa,
+                                                    int n, int s0, SingleLds& L, int* ss, int* sa,
                                                     const Stage& st) {
     switch ((n + kFpsT - 1) / kFpsT) {
         case 1: fps_single<1>(a, b, off, n, s0, L, ss, sa, st); break;
@@ -1411,7 +1493,8 @@ __device__ __forceinline__ ItemInfo sample_item(const SampleArgs& a, int* s_item
         it.deferred = it.staged && n <= kBmW4 * 128 && P * ((n + 127) >> 7) <= kFpsCap / 4;
         const Stage st{it.staged ? feats + off * C : nullptr, it.staged ? n * C : 0,
                        it.staged ? (n + 1) * C : 0, s_feat, it.deferred ? 1 : 0};
-        fps_single_dispatch(a, b, off, n, s0, s_gang.w, s_sel, s_asg, st);
+        fps_single_dispatch(a, b, off, n, s0, *reinterpret_cast<SingleLds*>(&s_gang), s_sel,
+                            s_asg, st);
         it.kind = 1;
         it.cnt = n;
     } else if (!kDirect && !a.direct && n <= kGangMax * kFpsCap) {
@@ -3015,7 +3098,7 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
     extern __shared__ __align__(16) int s_dyn[];
     // single events keep their FPS state inside s_perm; gangs spill into
     // s_asg, which fps_gang writes only after a final barrier
-    static_assert(sizeof(FpsLds) <= sizeof(int) * kFpsCap, "FpsLds must fit in s_perm");
+    static_assert(sizeof(SingleLds) <= sizeof(int) * kFpsCap, "SingleLds must fit in s_perm");
     static_assert(sizeof(GangLds) <= sizeof(int) * 2 * kFpsCap, "GangLds must fit in s_perm+s_asg");
     const int P = a.P;
     int* s_perm = s_dyn;

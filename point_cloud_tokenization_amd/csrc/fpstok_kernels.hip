@@ -112,25 +112,15 @@ __device__ __forceinline__ int wave_max_i(int v) {
     return readlane_i(v, 63);
 }
 
-// Inclusive prefix sum over the wave (Hillis-Steele with cross-lane shuffles).
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int u = __shfl_up(v, d, 64);
-        if (lane >= d) v += u;
-    }
-    return v;
-}
-
-// Inclusive prefix sum over the wave with DPP: shifts of 1, 2, 4 and 8
-// lanes inside each row of 16 (lanes without a source add 0), then the row
-// totals carried into the later rows by the two row broadcasts.
+// Inclusive prefix sum over the wave (every lane active) with DPP: shifts of
+// 1, 2, 4 and 8 lanes inside each row of 16 (lanes without a source add 0),
+// then the row totals carried into the later rows by the two row
+// broadcasts.  No LDS round trips.
 constexpr int kRowShr1 = 0x111;
 constexpr int kRowShr2 = 0x112;
 constexpr int kRowShr4 = 0x114;
 constexpr int kRowShr8 = 0x118;
-__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+__device__ __forceinline__ int wave_incl_scan(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, kRowShr1, 0xF, 0xF, true);
     v += __builtin_amdgcn_update_dpp(0, v, kRowShr2, 0xF, 0xF, true);
     v += __builtin_amdgcn_update_dpp(0, v, kRowShr4, 0xF, 0xF, true);
@@ -2670,7 +2660,7 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
         if (j < T)
 #pragma unroll
             for (int w = 0; w < kSrtW; ++w) tot += cnt[w * T + j];
-        const int incl = wave_incl_scan_dpp(tot);
+        const int incl = wave_incl_scan(tot);
         if (lane == 63) s_ws[wave] = incl;
         lds_barrier();
         int run = incl - tot;
@@ -3048,15 +3038,23 @@ __device__ __forceinline__ void pool_lds_cols(const PoolArgs& a, int64_t b, int 
 // by slot in LDS (perm, s_off) and whose feature rows are staged in LDS
 // (rows[i * C + c], followed by a zero row): every slot's (weighted) mean
 // in ascending member order, float64, from LDS instead of device memory.
+// With fewer slots than threads the columns are split into G groups, one
+// thread per (slot, group), so that every wave works (each column's sum is
+// the same sequence either way).
 __device__ __forceinline__ void pool_slots_lds(const PoolArgs& a, int64_t b, int n,
                                                const int* __restrict__ perm, const int* s_off,
                                                const float* __restrict__ rows) {
     const int P = a.P;
     const int C = a.C;
-    for (int j = threadIdx.x; j < P; j += kFpsT) {
+    const int G = max(1, min(C, kFpsT / P));
+    const int cpg = (C + G - 1) / G;  // columns per group
+    for (int t = threadIdx.x; t < P * G; t += kFpsT) {
+        const int j = t % P;
+        const int g = t / P;
         const int beg = s_off[j], end = s_off[j + 1];
-        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-            switch (min(kPoolCols, C - c0)) {
+        const int cend = min(C, (g + 1) * cpg);
+        for (int c0 = g * cpg; c0 < cend; c0 += kPoolCols) {
+            switch (min(kPoolCols, cend - c0)) {
                 case 1: pool_lds_cols<1>(a, b, j, beg, end, n, c0, perm, rows); break;
                 case 2: pool_lds_cols<2>(a, b, j, beg, end, n, c0, perm, rows); break;
                 case 3: pool_lds_cols<3>(a, b, j, beg, end, n, c0, perm, rows); break;
@@ -3067,7 +3065,7 @@ __device__ __forceinline__ void pool_slots_lds(const PoolArgs& a, int64_t b, int
                 default: pool_lds_cols<8>(a, b, j, beg, end, n, c0, perm, rows); break;
             }
         }
-        if (a.cell_count) a.cell_count[b * P + j] = end - beg;
+        if (g == 0 && a.cell_count) a.cell_count[b * P + j] = end - beg;
     }
 }
 

@@ -42,12 +42,12 @@ FPS_OPS_PER_POINT_ITER = 14
 # event size is under one workgroup's registers), from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE per dispatch, each scaled by its reading for a plain
 # device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
-# 2 * 373.9 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
+# 2 * 378.2 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
 # taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "84827f0b658edf63a02bfe063a4fefaf80707886fa3e402c5aab23f7b006b60f",
-    "bytes": int(round((2 * 373.9 + 419.3) * 1024)),
+    "kernels_sha256": "18893fb2aa9b0a390006dcb4e04cb105a8e554715453a6dc8e3c7ea16c541abe",
+    "bytes": int(round((2 * 378.2 + 419.3) * 1024)),
 }
 
 

@@ -180,8 +180,10 @@ fpstok_status fpstok_knn(const fpstok_batch* batch, const fpstok_params* params,
                          void* ws, size_t ws_bytes, void* stream);
 
 /* params->lloyd_iters rounds of charge-weighted Lloyd refinement on every
- * event with n > P (others untouched).  Reads the features' charge column
- * (unit charge if charge_col = -1).
+ * event with n > P (others untouched): the neptune README, "How it works"
+ * (the refinement step of the tokenizer) and "Parameters" (lloyd_iters).
+ * Reads the features' charge column (unit charge if charge_col = -1: Pull
+ * Request #923, review reply on events without a charge column).
  *   centroids [B,P,4] f32 in/out; token_count [B] int32 in
  *   assign    [N] int32 in/out (Voronoi slots, e.g. from fpstok_sample)
  * L = 0 is a no-op.  Errors: EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP. */
@@ -189,9 +191,11 @@ fpstok_status fpstok_lloyd(const fpstok_batch* batch, const fpstok_params* param
                            float* centroids, const int32_t* token_count, int32_t* assign,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* Per-token pooling of the features.  Voronoi mode: the members of slot j are
- * the pulses with assign = j; kNN mode: the entries != -1 of knn_idx[b][j].
- * Weight = charge if params->pool_weighted and charge_col >= 0, else 1.
+/* Per-token pooling of the features (Pull Request #923, "Summary": the
+ * pulses of each token are pooled; the neptune README, "How it works").
+ * Voronoi mode: the members of slot j are the pulses with assign = j; kNN
+ * mode: the entries != -1 of knn_idx[b][j].  Weight = charge if
+ * params->pool_weighted and charge_col >= 0, else 1.
  *   assign     [N] int32 in (Voronoi mode; may be NULL in kNN mode)
  *   knn_idx    [B,P,k] int32 in (kNN mode; may be NULL in Voronoi mode)
  *   pooled     [B,P,C] f32 out, 0 for j >= T and for zero-weight tokens

@@ -1533,19 +1533,32 @@ static_assert(kChunk * kAsgQ == kAsgT, "one chunk per workgroup");
 // minimum over all centroids.
 __global__ __launch_bounds__(kAsgT) void assign_kernel(AssignArgs a) {
     __shared__ float4 s_c[1024];
+    // the chunk's description is read together with the chunk count (the
+    // grid has max_chunks workgroups, so the read is in bounds), and the
+    // event's P centroid rows together with its range and token count:
+    // three dependent rounds of loads instead of five
     const int w = blockIdx.x;
-    if (w >= a.header[0]) return;
+    const int nchunks = a.header[0];
     const int64_t b = a.chunk_ev[w];
     const int beg = a.chunk_beg[w];
+    if (w >= nchunks) return;
     int64_t off;
     int n;
     event_range(a.offsets, a.N, b, off, n);
-    if (n == 0 || (a.skip_small && n <= a.P)) return;
     int T = a.token_count[b];
+    const int tid = threadIdx.x;
+    float4 cv[1024 / kAsgT];
+#pragma unroll
+    for (int r = 0; r < 1024 / kAsgT; ++r) {
+        cv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r * kAsgT < a.P) cv[r] = a.centroids[b * a.P + min(tid + r * kAsgT, a.P - 1)];
+    }
+    if (n == 0 || (a.skip_small && n <= a.P)) return;
     T = T > a.P ? a.P : T;
     if (T < 1) return;
-    const int tid = threadIdx.x;
-    for (int j = tid; j < T; j += kAsgT) s_c[j] = a.centroids[b * a.P + j];
+#pragma unroll
+    for (int r = 0; r < 1024 / kAsgT; ++r)
+        if (r * kAsgT < a.P && tid + r * kAsgT < T) s_c[tid + r * kAsgT] = cv[r];
     __syncthreads();
     const int q = tid & (kAsgQ - 1);
     const int i = beg + (tid >> 2);
@@ -2187,9 +2200,10 @@ __device__ __forceinline__ void lloyd_slot_means_lds(const LloydArgs& a, int64_t
 
 // One workgroup per event with n > P: every slot's charge-weighted mean of
 // its members in ascending pulse order.  An event of up to kLdsPerm pulses
-// first copies its coordinates and weights to LDS (dynamic: float4
-// rows[kLdsPerm + 1], float wts[kLdsPerm + 1]) and sorts by slot in LDS
-// (through bitmaps when n <= 1024, else the ballot-match sort); larger
+// first copies its coordinates, weights and slots to LDS (dynamic: float4
+// rows[kLdsPerm + 1], float wts[kLdsPerm + 1], int slots[kLdsPerm + 1]),
+// every load of the copy issued before any is used, and sorts by slot in
+// LDS (through bitmaps when n <= 1024, else the ballot-match sort); larger
 // events sort into device memory and gather their members from it.
 __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
     __shared__ __align__(16) int s_cnt[kSortW * kMaxP];
@@ -2211,26 +2225,54 @@ __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
         return;
     }
     float* s_w = reinterpret_cast<float*>(s_rows + kLdsPerm + 1);
-    for (int i = tid; i < n; i += kSortT) {
-        s_rows[i] = a.coords[off + i];
-        s_w[i] = a.charge_col >= 0 ? a.features[(off + i) * (int64_t)a.C + a.charge_col] : 1.0f;
+    int* s_slot = reinterpret_cast<int*>(s_w + kLdsPerm + 1);
+    {
+        // all of the event's loads in flight at once (a loop that stored
+        // each load before issuing the next would wait a full memory round
+        // trip per 256 pulses); indices clamped into the event
+        constexpr int R = kLdsPerm / kSortT;
+        const int rmax = (n + kSortT - 1) / kSortT;
+        float4 x[R];
+        float w[R];
+        int k[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            x[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            w[r] = 0.0f;
+            k[r] = 0;
+            if (r < rmax) {
+                const int i = min(tid + kSortT * r, n - 1);
+                x[r] = a.coords[off + i];
+                w[r] = a.charge_col >= 0 ? a.features[(off + i) * (int64_t)a.C + a.charge_col]
+                                         : 1.0f;
+                k[r] = a.assign[off + i];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + kSortT * r;
+            if (r < rmax && i < n) {
+                s_rows[i] = x[r];
+                s_w[i] = w[r];
+                s_slot[i] = k[r];
+            }
+        }
     }
     if (tid == 0) {
         s_rows[n] = make_float4(0.f, 0.f, 0.f, 0.f);
         s_w[n] = 0.0f;
     }
+    // both sorts start with a barrier before they read the slots
     const int W4 = (n + 127) >> 7;
     if (n <= kBmW4 * 128 && T * W4 <= kLdsPerm / 4) {
-        // slots copied to s_perm[0, n); permutation in s_perm[1024, 2048);
-        // prefix table in s_perm[2048, 3072); bitmaps in s_cnt
-        for (int i = tid; i < n; i += kSortT) s_perm[i] = a.assign[off + i];
-        __syncthreads();
+        // permutation in s_perm[1024, 2048); prefix table in s_perm[2048,
+        // 3072); bitmaps in s_cnt
         int* perm = s_perm + kBmW4 * 128;
-        block_sort_bitmap(s_perm, n, T, reinterpret_cast<uint32_t*>(s_cnt),
+        block_sort_bitmap(s_slot, n, T, reinterpret_cast<uint32_t*>(s_cnt),
                           s_perm + 2 * kBmW4 * 128, s_off, perm);
         lloyd_slot_means_lds(a, b, n, T, perm, s_off, s_rows, s_w);
     } else {
-        block_sort_by_token(a.assign + off, n, T, s_perm, s_cnt, s_off);
+        block_sort_by_token(s_slot, n, T, s_perm, s_cnt, s_off);
         lloyd_slot_means_lds(a, b, n, T, s_perm, s_off, s_rows, s_w);
     }
 }
@@ -3844,7 +3886,7 @@ hipError_t launch_knn(const KnnArgs& a, int64_t B, hipStream_t s) {
 }
 
 hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s) {
-    const size_t lds = (sizeof(float4) + sizeof(float)) * (size_t)(kLdsPerm + 1);
+    const size_t lds = (sizeof(float4) + sizeof(float) + sizeof(int)) * (size_t)(kLdsPerm + 1);
     hipLaunchKernelGGL(lloyd_update_kernel, dim3(grid1(B)), dim3(kSortT), lds, s, a);
     return hipGetLastError();
 }

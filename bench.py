@@ -381,6 +381,31 @@ def cpu_baseline(b, budget_s):
                 cpu=cpu_model(), single_thread=single)
 
 
+def oracle_rate(b, budget_s):
+    """The oracle, one host thread, on whole copies of batch b: as many calls
+    as fit in about budget_s seconds (at least one).  Returns events/s and
+    FPS point-iterations/s with the sample described."""
+    import oracle
+
+    kw = dict(P=b["P"], mode=b["mode"], k=b["k"], L=b["L"], weighted=b["weighted"],
+              charge_col=b["charge_col"])
+    x, f, off = b["coords"], b["features"], b["offsets"]
+    B = off.size - 1
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.tokenize(x, f, off, **kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    st = workload_stats(b)
+    return dict(value=B * reps / el, unit="events/s", cores=1, kind="oracle",
+                point_iters_per_s=st["point_iters"] * reps / el,
+                sample="%d call(s) on the whole %d-event batch (%.1f s, one host thread)" % (
+                    reps, B, el))
+
+
 def measured_traffic(workload):
     """HBM bytes per call from the committed counter runs, when they were taken
     on this workload and on the kernel source now in the package; else None."""
@@ -505,7 +530,9 @@ def main():
                 pool_roofline=pool_roofline(s2, pool_s, bb),
                 fps_point_iters_per_s=s2["point_iters"] / pc2["sample"],
                 pool_GBps=s2["pool_bytes"] / pc2["pool"] / 1e9, B=s2["B"], N=s2["N"],
-                P=s2["P"])
+                P=s2["P"],
+                cpu_oracle=oracle_rate(bb, min(1.0, args.cpu_budget / 4)) if args.cpu_budget > 0
+                else None)
             log("secondary %s: %s" % (name, secondary[name]))
 
     nxt = {}

@@ -236,6 +236,36 @@ class Runner:
         return {c: v / steps for c, v in out.items()}
 
 
+def largest_event(b):
+    """Batch b reduced to its largest event (copies of that event's rows)."""
+    o = b["offsets"]
+    n = np.diff(o)
+    e = int(np.argmax(n))
+    bb = dict(b)
+    bb["coords"] = np.ascontiguousarray(b["coords"][o[e]:o[e + 1]])
+    bb["features"] = np.ascontiguousarray(b["features"][o[e]:o[e + 1]])
+    bb["offsets"] = np.array([0, n[e]], dtype=np.int64)
+    return bb, e, int(n[e])
+
+
+def critical_path(b, steps=20):
+    """The FPS critical path T_cp: the stepwise fpstok_sample of the batch's
+    largest event alone, whose P - 1 dependent iterations bound the whole
+    call; timed without the rest of the batch sharing the compute units."""
+    bb, e, n = largest_event(b)
+    if n <= b["P"]:
+        return None
+    r = Runner(bb)
+    r.per_call(2)  # warm
+    t = r.per_call(steps)["sample"]
+    pi = n * (b["P"] - 1)
+    return dict(us=t * 1e6, event=e, pulses=n, point_iters=pi,
+                ns_per_iteration=t * 1e9 / (b["P"] - 1),
+                call="fpstok_sample on the one-event batch (%s)" % (
+                    "one workgroup" if n <= 4096 else "a gang of %d workgroups" % (
+                        (n + 4095) // 4096)))
+
+
 def time_next(b, reps=50):
     """The calls next to the path on one workload, after one forward call:
     fpstok_pool_backward, fpstok_pack / fpstok_unpack of the pooled rows and
@@ -532,7 +562,8 @@ def main():
                 pool_GBps=s2["pool_bytes"] / pc2["pool"] / 1e9, B=s2["B"], N=s2["N"],
                 P=s2["P"],
                 cpu_oracle=oracle_rate(bb, min(1.0, args.cpu_budget / 4)) if args.cpu_budget > 0
-                else None)
+                else None,
+                t_cp=critical_path(bb))
             log("secondary %s: %s" % (name, secondary[name]))
 
     nxt = {}
@@ -566,6 +597,7 @@ def main():
         "fps_point_iters_per_s": st["point_iters"] / step_gpu,
         "per_call_us": {c: v * 1e6 for c, v in per_call.items()},
         "roofline": roof,
+        "t_cp": critical_path(b),
         "cpu_baseline": cpu,
         "secondary": secondary,
         "next": nxt,

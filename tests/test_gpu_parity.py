@@ -79,6 +79,16 @@ def test_large_events(oracle_mod):
     check_pipeline(oracle_mod, b, P=256, mode=0, label="large events")
 
 
+@pytest.mark.parametrize("n,P", [(691, 128), (5000, 128), (84240, 256)])
+def test_single_event_batches(oracle_mod, n, P):
+    """A batch of one event: one workgroup, a gang of 2 and a gang of 21
+    workgroups with nothing else in the launch (the shape the bench times
+    for the critical path); stepwise and fused."""
+    b = synth.icecube_events([n], 600 + n % 97, C=6)
+    check_pipeline(oracle_mod, b, P=P, mode=0, label="one event n=%d" % n)
+    _tokenize_vs_oracle(oracle_mod, b, P, label="one event n=%d fused" % n)
+
+
 def test_wide_features(oracle_mod):
     b = synth.icecube_events([400, 3000, 20], 8, C=21)
     check_pipeline(oracle_mod, b, P=128, mode=0, L=1, label="C=21")

@@ -454,7 +454,7 @@ FPSTOK_API fpstok_status fpstok_pool(const fpstok_batch* bt, const fpstok_params
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (pr->assign_mode == FPSTOK_VORONOI) {
-        e = launch_plan_pool(bt->offsets, bt->num_events, bt->num_points, ws, L, a.whole, s);
+        e = launch_plan_pool(bt->offsets, bt->num_events, bt->num_points, ws, L, a, s);
         if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
     }
     e = run_pool(bt, pr, a, L, s);

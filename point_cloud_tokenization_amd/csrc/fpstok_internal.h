@@ -205,7 +205,7 @@ hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
 // chunks' partial-sum records and the list of events for the combine kernel
 // (whole: every event of more than one chunk is summed by its first chunk).
 hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                            const WorkspaceLayout& L, int whole, hipStream_t s);
+                            const WorkspaceLayout& L, const PoolArgs& a, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, int64_t B, hipStream_t s);
 // The work lists of a sample -> Lloyd (`chunks`) -> Voronoi pool (`pool`)
 // sequence in one launch; then launch_sample_items runs the FPS without

@@ -191,10 +191,19 @@ __device__ __forceinline__ void plan_chunks(const int64_t* __restrict__ offsets,
     if (tid == 0) header[0] = carry;
 }
 
+constexpr int kTailBuckets = 32;  // length bands of the partial chunks
+static_assert(kPoolChunk % kTailBuckets == 0 && kTailBuckets <= 64, "tail bands");
+
 // The pooling chunk list (kPoolChunk pulses per chunk), one workgroup of
-// 1024 threads, largest first: every event's full chunks, then every
-// event's last, partial chunk (an empty event gets one empty chunk), so that
-// the long chunks start before the short ones.  The chunks of an event of
+// 1024 threads, longest first: every event's full chunks, then every event's
+// last, partial chunk (an empty event gets one empty chunk).  In the kBands
+// form, when the list is longer than band_over (the workers that take it in
+// rounds), the partial chunks go by length in kTailBuckets bands of
+// decreasing length (a band's chunks in any order: a chunk's output does not
+// depend on its place in the list), so that the rounds give the workers even
+// loads; otherwise, and always in the other form, in event order (the other
+// form has no band code: it serves the lists that fit one round, where the
+// planner's own time is what counts).  The chunks of an event of
 // more than one chunk get consecutive partial-sum records (-1: the event is
 // one chunk) and the event is listed in big_ev with its first record for the
 // combine kernel (count in header[4]; the chunk count goes to header[6]).
@@ -204,6 +213,7 @@ __device__ __forceinline__ void plan_chunks(const int64_t* __restrict__ offsets,
 // the lists hold: extra chunks are dropped, an event without room for its
 // records is marked -2 too, and a listed event without room is listed as -1;
 // nothing is written out of bounds.
+template <bool kBands>
 __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                                                          int64_t B, int64_t N, int64_t max_chunks,
                                                          int64_t max_parts,
@@ -212,24 +222,56 @@ __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                                                          int32_t* __restrict__ chunk_beg,
                                                          int32_t* __restrict__ chunk_part,
                                                          int32_t* __restrict__ big_ev,
-                                                         int whole) {
+                                                         int whole, int64_t band_over) {
     __shared__ int s_sum[3][16];
+    __shared__ int s_tt;                // all partial chunks
+    __shared__ int s_tb[kTailBuckets];  // tails per band, then each band's first list place
+    __shared__ int s_tc[kTailBuckets];  // places taken in each band
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
-    int64_t carry = 0;
+    if constexpr (kBands) {
+        if (tid < kTailBuckets) {
+            s_tb[tid] = 0;
+            s_tc[tid] = 0;
+        }
+        __syncthreads();
+    }
+    int64_t carry = 0, tail0 = 0;
+    bool banded = false;
     int bcarry = 0;
+    int n_first = 0;  // the size of event tid, kept from the first pass
     for (int pass = 0; pass < 2; ++pass) {
         int64_t pcarry = 0;
+        if (kBands && pass == 1) {
+            // band places: an exclusive scan of the band counts (band 0: the
+            // longest tails)
+            if (wave == 0) {
+                const int v = lane < kTailBuckets ? s_tb[lane] : 0;
+                const int incl = wave_incl_scan(v);
+                if (lane < kTailBuckets) s_tb[lane] = incl - v;
+                if (lane == 63) s_tt = incl;
+            }
+            __syncthreads();
+            tail0 = carry;
+            banded = carry + s_tt > band_over;
+        }
         for (int64_t base = 0; base < B; base += 1024) {
             const int64_t b = base + tid;
-            int nf = 0, tl = 0;
+            int nf = 0, tl = 0, band = 0;
             if (b < B) {
-                int64_t off;
                 int n;
-                event_range(offsets, N, b, off, n);
+                if (pass == 1 && base == 0) {
+                    n = n_first;
+                } else {
+                    int64_t off;
+                    event_range(offsets, N, b, off, n);
+                    if (base == 0) n_first = n;
+                }
                 nf = n / kPoolChunk;
                 tl = n % kPoolChunk != 0 || n == 0 ? 1 : 0;
+                band = (kPoolChunk - 1 - n % kPoolChunk) / (kPoolChunk / kTailBuckets);
+                if (kBands && pass == 0 && tl) atomicAdd(&s_tb[band], 1);
             }
             const int nch = nf + tl;
             const int cnt = pass == 0 ? nf : tl;  // chunks this pass places
@@ -250,7 +292,10 @@ __device__ __forceinline__ void plan_pool(const int64_t* __restrict__ offsets,
                     pre[q] += w < wave ? x : 0;
                     tot[q] += x;
                 }
-            const int64_t pos = carry + pre[0] + incl[0] - cnt;
+            const int64_t pos = kBands && pass == 1 && banded
+                                    ? (cnt ? tail0 + s_tb[band] + atomicAdd(&s_tc[band], 1)
+                                           : (int64_t)0)
+                                    : carry + pre[0] + incl[0] - cnt;
             const int64_t ppos = pcarry + pre[1] + incl[1] - np;
             const bool room = ppos + np <= max_parts;
             for (int c = 0; c < cnt && pos + c < max_chunks; ++c) {
@@ -284,6 +329,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int64_t* __restrict__ 
     plan_chunks(offsets, B, N, max_chunks, header, chunk_ev, chunk_beg);
 }
 
+template <bool kBands>
 __global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restrict__ offsets,
                                                          int64_t B, int64_t N, int64_t max_chunks,
                                                          int64_t max_parts,
@@ -291,9 +337,10 @@ __global__ __launch_bounds__(1024) void plan_pool_kernel(const int64_t* __restri
                                                          int32_t* __restrict__ chunk_ev,
                                                          int32_t* __restrict__ chunk_beg,
                                                          int32_t* __restrict__ chunk_part,
-                                                         int32_t* __restrict__ big_ev, int whole) {
-    plan_pool(offsets, B, N, max_chunks, max_parts, header, chunk_ev, chunk_beg, chunk_part,
-              big_ev, whole);
+                                                         int32_t* __restrict__ big_ev, int whole,
+                                                         int64_t band_over) {
+    plan_pool<kBands>(offsets, B, N, max_chunks, max_parts, header, chunk_ev, chunk_beg,
+                      chunk_part, big_ev, whole, band_over);
 }
 
 // ---------------------------------------------------------------------- FPS
@@ -1367,12 +1414,14 @@ __global__ __launch_bounds__(1024) void plan_fps_kernel(SampleArgs a, int64_t B)
 // The work lists of a call that runs sample, then Lloyd (assign chunks,
 // when `chunks`) and Voronoi pooling (pooling chunks, when `pool`), in one
 // launch.
+template <bool kBands>
 __global__ __launch_bounds__(1024) void plan_all_kernel(SampleArgs a, int64_t B,
                                                         int32_t* __restrict__ chunk_ev,
                                                         int32_t* __restrict__ chunk_beg,
                                                         int64_t max_chunks, PoolArgs pa,
                                                         int64_t max_pool_chunks,
-                                                        int64_t max_parts, int chunks, int pool) {
+                                                        int64_t max_parts, int chunks, int pool,
+                                                        int64_t band_over) {
     if (!a.direct) plan_fps(a, B);  // no work list in direct mode
     if (chunks) {
         __syncthreads();
@@ -1380,10 +1429,10 @@ __global__ __launch_bounds__(1024) void plan_all_kernel(SampleArgs a, int64_t B,
     }
     if (pool) {
         __syncthreads();
-        plan_pool(a.offsets, B, a.N, max_pool_chunks, max_parts, pa.header,
+        plan_pool<kBands>(a.offsets, B, a.N, max_pool_chunks, max_parts, pa.header,
                   const_cast<int32_t*>(pa.chunk_ev), const_cast<int32_t*>(pa.chunk_beg),
                   const_cast<int32_t*>(pa.chunk_part), const_cast<int32_t*>(pa.big_ev),
-                  pa.whole);
+                  pa.whole, band_over);
     }
 }
 
@@ -2636,18 +2685,21 @@ __global__ __launch_bounds__(kSortT) void pool_chunk_kernel(PoolArgs a) {
 constexpr int kSrtT = 512;               // threads of the sorting pooling kernel
 constexpr int kSrtW = kSrtT / 64;        // its waves
 constexpr int kSrtR = kPoolChunk / kSrtT;  // pulses per thread (8)
-constexpr int kSrtWave = 64 * kSrtR;       // pulses per wave
 constexpr int kSrtMaxP = 256;            // slots it handles (one per thread of the first waves)
 constexpr int kSrtMaxC = 6;              // widest rows it handles
 static_assert(kSrtR * kSrtT == kPoolChunk, "one pulse per thread and window");
 
 // Voronoi pooling over the chunk list (kPoolChunk pulses per chunk) for P
 // <= 256 and rows of at most 6 columns: one workgroup of 512 threads per
-// compute unit walks the chunks c = blockIdx, blockIdx + gridDim, ... and,
-// while it pools one, has the next one's slots and rows loading into
-// registers.  Wave w holds the chunk's pulses 512 w .. 512 w + 511 as eight
-// 64-pulse windows (lane l: pulses 512 w + 64 r + l), so the windows are in
-// pulse order wave after wave.  A chunk:
+// compute unit takes one chunk per round of gridDim chunks, in serpentine
+// order (round k: workgroup g takes chunk k gridDim + g for even k and
+// k gridDim + gridDim - 1 - g for odd k; the planner lists the chunks
+// longest first, so the rounds even out the workgroups' loads) and, while it
+// pools one, has the next one's slots and rows loading into registers.  A
+// chunk of len pulses is cut into R = ceil(len / 512) 64-pulse windows per
+// wave: wave w holds pulses 64 R w .. 64 R (w + 1) - 1 (lane l of window r:
+// pulse 64 R w + 64 r + l), so the windows are in pulse order wave after
+// wave and a short chunk costs only the windows it fills.  A chunk:
 //  1. every pulse counts its slot per wave (LDS atomics; order irrelevant);
 //  2. per slot, an exclusive scan gives the slot's first row; per (wave,
 //     slot), the first row of that wave's members;
@@ -2671,13 +2723,20 @@ static_assert(kSrtR * kSrtT == kPoolChunk, "one pulse per thread and window");
 // no fence (the kernel boundary publishes the records).  The chunks'
 // descriptions (event, range, record, token count) are read 64 at a time
 // into LDS, so their chain of dependent loads is paid once per 64 chunks.
-// Dynamic LDS: float rows[kPoolChunk * NC], int cnt[kSrtW * P],
-// int off[P + 1], uint64 bm[kSrtW * P] (zero between chunks).
+// Dynamic LDS: float rows[kPoolChunk * NC], float zero[kSrtZero] (a zero
+// row), int cnt[kSrtW * P], int off[P + 1], uint64 bm[kSrtW * P] (zero
+// between chunks).
 constexpr int kSrtMeta = 64;  // chunk descriptions read at a time
+constexpr int kSrtZero = 8;   // floats of the zero row (>= kSrtMaxC; keeps cnt 16-byte aligned)
+static_assert(kSrtZero >= kSrtMaxC && kSrtZero % 4 == 0, "zero row");
+// 64-pulse windows per wave for a chunk of len pulses (0 for an empty one)
+__device__ __forceinline__ int srt_windows(int len) {
+    return __builtin_amdgcn_readfirstlane((max(len, 0) + 64 * kSrtW - 1) / (64 * kSrtW));
+}
 // Steps 1-3 above for one sub-chunk of at most kPoolChunk pulses (this
-// thread's pulses 512 wave + 64 r + lane: slots k[r], rows f[r]): the rows
-// land in LDS sorted by slot, slot j's at off_[j] .. off_[j + 1].  Ends with
-// a workgroup barrier; k and f are not needed afterwards.
+// thread's pulses 64 R wave + 64 r + lane, r < R: slots k[r], rows f[r]):
+// the rows land in LDS sorted by slot, slot j's at off_[j] .. off_[j + 1].
+// Ends with a workgroup barrier; k and f are not needed afterwards.
 template <int NC>
 __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float (&f)[kSrtR][NC],
                                              int len, int T, float* s_rows, int* cnt, int* off_,
@@ -2685,14 +2744,16 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
+    const int R = srt_windows(len);
+    const int w0 = 64 * R * wave;  // this wave's first pulse
     // 1. counts per (wave, slot)
     for (int q = tid; q < kSrtW * T; q += kSrtT) cnt[q] = 0;
     lds_barrier();
     int* __restrict__ wc = cnt + wave * T;
 #pragma unroll
     for (int r = 0; r < kSrtR; ++r) {
-        const int i = kSrtWave * wave + 64 * r + lane;
-        if (i < len && (unsigned)k[r] < (unsigned)T) atomicAdd(&wc[k[r]], 1);
+        const int i = w0 + 64 * r + lane;
+        if (r < R && i < len && (unsigned)k[r] < (unsigned)T) atomicAdd(&wc[k[r]], 1);
     }
     lds_barrier();
     // 2. slot offsets and (wave, slot) cursors (threads j < T)
@@ -2729,7 +2790,8 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int r = 0; r < kSrtR; ++r) {
-        const int i = kSrtWave * wave + 64 * r + lane;
+        if (r >= R) break;  // R is uniform: the whole workgroup leaves together
+        const int i = w0 + 64 * r + lane;
         const bool ok = i < len && (unsigned)k[r] < (unsigned)T;
         const int kk = ok ? k[r] : 0;
         if (ok) atomicOr(&wm[kk], 1ull << lane);
@@ -2761,28 +2823,35 @@ __device__ __forceinline__ void sorted_sums(int T, int wcol, const float* s_rows
     const int tid = threadIdx.x;
     if (tid < T) {
         const int mb = off_[tid], me = off_[tid + 1];
-        // four members' rows read together, then added one after the other
-        // (rows past the slot are read, within the LDS rows, and not added)
+        // four members' rows read together, then added one after the other,
+        // with no per-member branch: a member past the slot reads the zero
+        // row that follows the rows, so it adds weight +0 and products +0.
+        // Those leave every sum as it was: the sums start at +0, and under
+        // rounding to nearest a sum that starts at +0 never becomes -0.
+        // the weight as bits: the row's weight column, or 1.0 for a member
+        // and 0 past the slot when there is none (no branch on either)
+        const bool weighted = wcol >= 0 && wcol < NC;
+        const int wc = weighted ? wcol : 0;
+        const int wkeep = weighted ? -1 : 0;
+        const int wone = weighted ? 0 : 0x3f800000;
+        const float* __restrict__ zrow = s_rows + kPoolChunk * NC;
         constexpr int U = 4;
         for (int m0 = mb; m0 < me; m0 += U) {
-            float fv[U][NC];
+            float fv[U][NC], wv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const float* __restrict__ rw = s_rows + min(m0 + u, kPoolChunk - 1) * NC;
+                const bool ok = m0 + u < me;
+                const float* __restrict__ rw = ok ? s_rows + (m0 + u) * NC : zrow;
 #pragma unroll
                 for (int q = 0; q < NC; ++q) fv[u][q] = rw[q];
+                wv[u] = __int_as_float((__float_as_int(rw[wc]) & wkeep) | (ok ? wone : 0));
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (m0 + u < me) {
-                    float wv = 1.0f;
+                const double wd = (double)wv[u];
+                W += wd;
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) wv = q == wcol ? fv[u][q] : wv;
-                    const double wd = (double)wv;
-                    W += wd;
-#pragma unroll
-                    for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[u][q], S[q]);
-                }
+                for (int q = 0; q < NC; ++q) S[q] = __builtin_fma(wd, (double)fv[u][q], S[q]);
             }
         }
         count += me - mb;
@@ -2805,18 +2874,23 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
     const int P = a.P;
     const int C = NC;
     const int wcol = a.weight_col;
-    int* cnt = reinterpret_cast<int*>(s_rows + kPoolChunk * NC);  // [kSrtW][P]
-    int* off_ = cnt + kSrtW * P;                                  // [P + 1]
+    int* cnt = reinterpret_cast<int*>(s_rows + kPoolChunk * NC + kSrtZero);  // [kSrtW][P]
+    int* off_ = cnt + kSrtW * P;                                             // [P + 1]
     unsigned long long* bm = reinterpret_cast<unsigned long long*>(
-        off_ + ((P + 2) & ~1));                                   // [kSrtW][P]
+        off_ + ((P + 2) & ~1));                                              // [kSrtW][P]
     for (int q = tid; q < kSrtW * P; q += kSrtT) bm[q] = 0ull;
+    if (tid < kSrtZero) s_rows[kPoolChunk * NC + tid] = 0.0f;
     const int nchunks = a.header[6];
     const int G = gridDim.x;
-    // descriptions of this workgroup's chunks i0 .. i0 + 63 (chunk blockIdx +
-    // G i), read by wave 0; the callers put a barrier after
+    // this workgroup's chunk of round i (serpentine order); increasing in i
+    auto chunk_of = [&](int i) {
+        return i * G + ((i & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    };
+    // descriptions of this workgroup's chunks of rounds i0 .. i0 + 63, read
+    // by wave 0; the callers put a barrier after
     auto fill_meta = [&](int i0) {
         if (wave == 0) {
-            const int c = blockIdx.x + (i0 + lane) * G;
+            const int c = chunk_of(i0 + lane);
             int b = 0, beg = 0, part = -1, n = 0, T = 0;
             int64_t off = 0;
             if (c < nchunks) {
@@ -2834,12 +2908,20 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
             s_moff[lane] = off;
         }
     };
-    // a sub-chunk's pulses of this thread (512 wave + 64 r + lane) into k, f,
-    // indices clamped into it so that every load is issued together; an
+    // a sub-chunk's pulses of this thread (64 R wave + 64 r + lane, r < R)
+    // into k, f, indices clamped into it so that every load is issued
+    // together (windows r >= R load its last pulse, which nothing reads); an
     // empty sub-chunk loads nothing (its first row may lie past the input)
     int k[kSrtR];
     float f[kSrtR][NC];
     auto load = [&](int64_t off, int beg, int len) {
+        // the same for every thread: said so, the test below is a scalar
+        // branch, and no register of the loads has to be merged (and waited
+        // for) where the two ways join
+        len = __builtin_amdgcn_readfirstlane(len);
+        beg = __builtin_amdgcn_readfirstlane(beg);
+        off = ((int64_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
         if (len <= 0) {
 #pragma unroll
             for (int r = 0; r < kSrtR; ++r) {
@@ -2851,9 +2933,10 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
         }
         const int32_t* __restrict__ ag = a.assign + off + beg;
         const float* __restrict__ fg = a.features + (off + beg) * (int64_t)C;
+        const int R = srt_windows(len);
 #pragma unroll
         for (int r = 0; r < kSrtR; ++r) {
-            const int i = min(kSrtWave * wave + 64 * r + lane, len - 1);
+            const int i = r < R ? min(64 * R * wave + 64 * r + lane, len - 1) : len - 1;
             k[r] = ag[i];
 #pragma unroll
             for (int q = 0; q < NC; ++q) f[r][q] = fg[(int64_t)i * C + q];
@@ -2868,8 +2951,8 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
     int m0 = 0;  // local index of the first description in LDS
     fill_meta(0);
     lds_barrier();  // descriptions and cleared masks
-    if ((int)blockIdx.x < nchunks) load_local(0, 0);
-    for (int i = 0; blockIdx.x + i * G < nchunks; ++i) {
+    if (chunk_of(0) < nchunks) load_local(0, 0);
+    for (int i = 0; chunk_of(i) < nchunks; ++i) {
         const int m = i - m0;
         const int64_t b = s_mb[m];
         const int beg = s_mbeg[m];
@@ -2878,7 +2961,7 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
         const int n = s_mn[m];
         const int T = s_mT[m];
         const int len = max(0, min(n - beg, kPoolChunk));
-        const bool more = blockIdx.x + (i + 1) * G < nchunks;
+        const bool more = chunk_of(i + 1) < nchunks;
         // the next chunk's description, read into LDS here when it is past
         // the ones held (every thread has read chunk i's above)
         if (more && i + 1 - m0 >= kSrtMeta) {
@@ -2894,10 +2977,11 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
         }
         if (part == -1) {
             bool ident = n == T;
+            const int R = srt_windows(len);
 #pragma unroll
             for (int r = 0; r < kSrtR; ++r) {
-                const int ii = kSrtWave * wave + 64 * r + lane;
-                ident = ident && (ii >= len || k[r] == ii);
+                const int ii = 64 * R * wave + 64 * r + lane;
+                ident = ident && (r >= R || ii >= len || k[r] == ii);
             }
             const bool wave_ident = ballot(!ident) == 0;
             if (lane == 0) s_vote[wave] = wave_ident ? 1 : 0;
@@ -2955,8 +3039,9 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
 // Means of the events of more than one chunk from their chunks'
 // records: block (event m, slot group) with threads (field f, slot js);
 // field 0 is the weight, 1..C the columns, C+1 the member count; every
-// thread adds its value over the K records in chunk order, 16 loads in
+// thread adds its value over the K records in chunk order, kCombineDepth loads in
 // flight.
+constexpr int kCombineDepth = 32;  // records read together (an event of up to 32 chunks: one round trip)
 __global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a) {
     __shared__ double s_W[256];
     const int m = blockIdx.x;
@@ -2980,12 +3065,13 @@ __global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a) {
     if (j < T) {
         const double* __restrict__ r = a.part + ((size_t)p0 * P + j) * C2 + f;
         const size_t stride = (size_t)P * C2;
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            double v[16];
+        for (int k0 = 0; k0 < K; k0 += kCombineDepth) {
+            double v[kCombineDepth];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = k0 + u < K ? r[(size_t)(k0 + u) * stride] : 0.0;
+            for (int u = 0; u < kCombineDepth; ++u)
+                v[u] = k0 + u < K ? r[(size_t)(k0 + u) * stride] : 0.0;
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
+            for (int u = 0; u < kCombineDepth; ++u)
                 if (k0 + u < K) t += v[u];
         }
     }
@@ -3800,13 +3886,28 @@ hipError_t launch_plan(const int64_t* offsets, int64_t B, int64_t N, void* ws,
     return hipGetLastError();
 }
 
+// Chunk-list length above which the planner orders the partial chunks by
+// length: the persistent sorting kernel takes the list in rounds of one chunk
+// per compute unit; the other pooling kernel takes one chunk per workgroup.
+static int64_t pool_band_over(const PoolArgs& a) {
+    return a.P <= kSrtMaxP && a.C <= kSrtMaxC ? (int64_t)device_cus() : INT64_MAX;
+}
+
+// Whether a batch's chunk list can be longer than band_over: every event
+// makes at most n / kPoolChunk + 1 chunks.
+static bool pool_bands(int64_t B, int64_t N, int64_t band_over) {
+    return B + N / kPoolChunk > band_over;
+}
+
 hipError_t launch_plan_pool(const int64_t* offsets, int64_t B, int64_t N, void* ws,
-                            const WorkspaceLayout& L, int whole, hipStream_t s) {
+                            const WorkspaceLayout& L, const PoolArgs& a, hipStream_t s) {
     char* base = (char*)ws;
-    hipLaunchKernelGGL(plan_pool_kernel, dim3(1), dim3(1024), 0, s, offsets, B, N,
-                       L.max_pool_chunks, L.max_parts, (int32_t*)(base + L.header),
-                       (int32_t*)(base + L.pool_ev), (int32_t*)(base + L.pool_beg),
-                       (int32_t*)(base + L.chunk_part), (int32_t*)(base + L.big_ev), whole);
+    const int64_t over = pool_band_over(a);
+    auto k = pool_bands(B, N, over) ? plan_pool_kernel<true> : plan_pool_kernel<false>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(1024), 0, s, offsets, B, N, L.max_pool_chunks,
+                       L.max_parts, (int32_t*)(base + L.header), (int32_t*)(base + L.pool_ev),
+                       (int32_t*)(base + L.pool_beg), (int32_t*)(base + L.chunk_part),
+                       (int32_t*)(base + L.big_ev), a.whole, over);
     return hipGetLastError();
 }
 
@@ -3827,9 +3928,11 @@ int64_t sample_max_items(int64_t B, int64_t N) { return B + N / kFpsCap; }
 hipError_t launch_plan_all(const SampleArgs& a, int64_t B, void* ws, const WorkspaceLayout& L,
                            const PoolArgs& pa, bool chunks, bool pool, hipStream_t s) {
     char* base = (char*)ws;
-    hipLaunchKernelGGL(plan_all_kernel, dim3(1), dim3(1024), 0, s, a, B,
-                       (int32_t*)(base + L.chunk_ev), (int32_t*)(base + L.chunk_beg), L.max_chunks,
-                       pa, L.max_pool_chunks, L.max_parts, chunks ? 1 : 0, pool ? 1 : 0);
+    const int64_t over = pool_band_over(pa);
+    auto k = pool && pool_bands(B, a.N, over) ? plan_all_kernel<true> : plan_all_kernel<false>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(1024), 0, s, a, B, (int32_t*)(base + L.chunk_ev),
+                       (int32_t*)(base + L.chunk_beg), L.max_chunks, pa, L.max_pool_chunks,
+                       L.max_parts, chunks ? 1 : 0, pool ? 1 : 0, over);
     return hipGetLastError();
 }
 
@@ -3894,7 +3997,7 @@ hipError_t launch_lloyd_update(const LloydArgs& a, int64_t B, hipStream_t s) {
 hipError_t launch_pool_voronoi(const PoolArgs& a, int64_t max_chunks, hipStream_t s) {
     if (a.P <= kSrtMaxP && a.C <= kSrtMaxC) {
         // rows sorted by slot into LDS; one persistent workgroup per compute unit
-        const size_t lds = sizeof(float) * (size_t)kPoolChunk * a.C +
+        const size_t lds = sizeof(float) * ((size_t)kPoolChunk * a.C + kSrtZero) +
                            sizeof(int) * ((size_t)kSrtW * a.P + ((a.P + 2) & ~1)) +
                            sizeof(unsigned long long) * (size_t)kSrtW * a.P;
         const dim3 g((unsigned)std::max<int64_t>(1, std::min<int64_t>(max_chunks, device_cus()))),

@@ -273,6 +273,19 @@ def test_pool_chunk_combines(oracle_mod):
     check_pipeline(oracle_mod, b, P=256, weighted=False, label="pool chunks plain mean")
 
 
+def test_pool_many_rounds(oracle_mod):
+    """More pooling chunks than compute units: the persistent sorting kernel
+    takes them in rounds, in serpentine order, over a list whose partial
+    chunks the planner sorted into length bands (partial chunks of every
+    length, full chunks and multi-chunk events among them), stepwise and
+    fused."""
+    rng = np.random.default_rng(512)
+    ns = [int(n) for n in rng.integers(1, 4096, 900)] + [4096, 9000, 20000, 0, 1]
+    b = synth.icecube_events(ns, 512, C=6)
+    check_pipeline(oracle_mod, b, P=128, label="pool many rounds")
+    _tokenize_vs_oracle(oracle_mod, b, 128, label="fused many rounds")
+
+
 def test_tokenize_fused_edges(oracle_mod):
     """The fused Voronoi kernel on every path: pass-through, one workgroup,
     gangs (cooperative pooling across shards) and the streaming fallback."""

@@ -42,12 +42,12 @@ FPS_OPS_PER_POINT_ITER = 14
 # event size is under one workgroup's registers), from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE per dispatch, each scaled by its reading for a plain
 # device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
-# 2 * 378.2 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
+# 2 * 372.6 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
 # taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "ebe417c9218b6250065a96fe001c7a9b3d45ec980216dae63f598422c4969173",
-    "bytes": int(round((2 * 378.2 + 419.3) * 1024)),
+    "kernels_sha256": "1f6fb999673c169d8603ebd9f37ec13af0e7e5f6e24b23e8aa938434fa2e30ce",
+    "bytes": int(round((2 * 372.6 + 419.3) * 1024)),
 }
 
 

@@ -3041,7 +3041,7 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
 // field 0 is the weight, 1..C the columns, C+1 the member count; every
 // thread adds its value over the K records in chunk order, kCombineDepth loads in
 // flight.
-constexpr int kCombineDepth = 32;  // records read together (an event of up to 32 chunks: one round trip)
+constexpr int kCombineDepth = 16;  // records read together
 __global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a) {
     __shared__ double s_W[256];
     const int m = blockIdx.x;

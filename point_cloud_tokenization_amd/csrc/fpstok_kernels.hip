@@ -2086,8 +2086,9 @@ __device__ __forceinline__ bool block_sort_small(int* asg, int n, int T, int* tm
 // prefix of popcounts per 128-bit word plus one masked word, so the order
 // is ascending by construction, with no atomics on the order and no
 // per-member loops.  perm[s_off[k] + r] = r-th member of slot k.
-//   bm: LDS uint32[T * W4 * 4], W4 = ceil(n / 128) <= kBmW4;  pre4: LDS
+//   bm: LDS uint32[T * W4 * 4], W4 = ceil(n / 128) <= kW4Max;  pre4: LDS
 //   int[T * W4];  s_off: LDS int[T + 1];  perm: LDS int[n]
+template <int kW4Max = kBmW4>
 __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, int n, int T,
                                                   uint32_t* bm, int* pre4, int* s_off,
                                                   int* perm) {
@@ -2115,7 +2116,7 @@ __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, i
         int c = 0;
         if (r < per && jj < T) {
 #pragma unroll
-            for (int w4 = 0; w4 < kBmW4; ++w4) {
+            for (int w4 = 0; w4 < kW4Max; ++w4) {
                 if (w4 < W4) {
                     const uint4 q = bm4[jj * W4 + w4];
                     pre4[jj * W4 + w4] = c;
@@ -2145,7 +2146,7 @@ __device__ __forceinline__ void block_sort_bitmap(const int* __restrict__ asg, i
     if (tid == 0) s_off[T] = total;
     lds_barrier();
 #pragma unroll
-    for (int r = 0; r < kBmW4 * 128 / kSortT; ++r) {
+    for (int r = 0; r < kW4Max * 128 / kSortT; ++r) {
         const int i = tid + kSortT * r;
         const int k = i < n ? asg[i] : -1;
         if ((unsigned)k < (unsigned)T) {
@@ -2252,8 +2253,12 @@ __device__ __forceinline__ void lloyd_slot_means_lds(const LloydArgs& a, int64_t
 // first copies its coordinates, weights and slots to LDS (dynamic: float4
 // rows[kLdsPerm + 1], float wts[kLdsPerm + 1], int slots[kLdsPerm + 1]),
 // every load of the copy issued before any is used, and sorts by slot in
-// LDS (through bitmaps when n <= 1024, else the ballot-match sort); larger
-// events sort into device memory and gather their members from it.
+// LDS (through bitmaps when n <= 1024, and for n < 2048 through bitmaps kept
+// in the rows' unused upper half; else the ballot-match sort); larger events
+// sort into device memory and gather their members from it.
+constexpr int kLloydBmRows = 2 * kBmW4 * 128;  // events below this size: bitmaps in the rows' upper half
+static_assert(2 * kLloydBmRows <= kLdsPerm + 1 && 2 * kLloydBmRows <= kLdsPerm,
+              "the upper half of the rows and the prefix table must fit");
 __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
     __shared__ __align__(16) int s_cnt[kSortW * kMaxP];
     __shared__ int s_off[kMaxP + 1];
@@ -2320,6 +2325,15 @@ __global__ __launch_bounds__(kSortT) void lloyd_update_kernel(LloydArgs a) {
         block_sort_bitmap(s_slot, n, T, reinterpret_cast<uint32_t*>(s_cnt),
                           s_perm + 2 * kBmW4 * 128, s_off, perm);
         lloyd_slot_means_lds(a, b, n, T, perm, s_off, s_rows, s_w);
+    } else if (n < kLloydBmRows && T * W4 <= kLloydBmRows) {
+        // rows 0 .. n (the zero row included) lie below kLloydBmRows, so
+        // rows kLloydBmRows .. 2 kLloydBmRows - 1 (16 bytes each) are free for
+        // the bitmaps (T * W4 * 16 bytes); permutation in s_perm[0, n),
+        // prefix table in s_perm[kLloydBmRows, kLloydBmRows + T * W4)
+        block_sort_bitmap<2 * kBmW4>(s_slot, n, T,
+                                     reinterpret_cast<uint32_t*>(s_rows + kLloydBmRows),
+                                     s_perm + kLloydBmRows, s_off, s_perm);
+        lloyd_slot_means_lds(a, b, n, T, s_perm, s_off, s_rows, s_w);
     } else {
         block_sort_by_token(s_slot, n, T, s_perm, s_cnt, s_off);
         lloyd_slot_means_lds(a, b, n, T, s_perm, s_off, s_rows, s_w);

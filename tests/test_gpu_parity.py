@@ -42,6 +42,19 @@ def test_edge_sizes(oracle_mod, mode, k, L):
     check_pipeline(oracle_mod, b, P=128, mode=mode, k=k, L=L, label="edge sizes")
 
 
+@pytest.mark.parametrize("P", [128, 256])
+def test_lloyd_wide_bitmaps(oracle_mod, P):
+    """Lloyd updates of events between 1025 and 2048 pulses, sorted by slot
+    through bitmaps of 9 to 16 128-bit words per slot (kept in the rows'
+    upper half), the sizes around both ends of that form, with the slot
+    count at and below the bitmaps' capacity, and on a tie-rich grid."""
+    ns = [1024, 1025, 1100, 1500, 1900, 2047, 2048, 700]
+    b = synth.icecube_events(ns, 640 + P, C=6)
+    check_pipeline(oracle_mod, b, P=P, mode=0, L=3, label="lloyd wide bitmaps P=%d" % P)
+    g = synth.grid_events([1030, 2040], 650 + P, C=6, side=2)
+    check_pipeline(oracle_mod, g, P=P, mode=0, L=2, label="lloyd wide bitmaps grid P=%d" % P)
+
+
 @pytest.mark.parametrize("P", [1, 2, 7, 64, 256, 1024])
 def test_num_patches_range(oracle_mod, P):
     ns = [P - 1 if P > 1 else 0, P, P + 1, 3 * P + 5, 3000]

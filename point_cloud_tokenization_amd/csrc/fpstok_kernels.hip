@@ -2744,28 +2744,32 @@ constexpr int kSrtMeta = 64;  // chunk descriptions read at a time
 constexpr int kSrtZero = 8;   // floats of the zero row (>= kSrtMaxC; keeps cnt 16-byte aligned)
 static_assert(kSrtZero >= kSrtMaxC && kSrtZero % 4 == 0, "zero row");
 // 64-pulse windows per wave for a chunk of len pulses (0 for an empty one)
+// on kW waves
+template <int kW = kSrtW>
 __device__ __forceinline__ int srt_windows(int len) {
-    return __builtin_amdgcn_readfirstlane((max(len, 0) + 64 * kSrtW - 1) / (64 * kSrtW));
+    return __builtin_amdgcn_readfirstlane((max(len, 0) + 64 * kW - 1) / (64 * kW));
 }
-// Steps 1-3 above for one sub-chunk of at most kPoolChunk pulses (this
-// thread's pulses 64 R wave + 64 r + lane, r < R: slots k[r], rows f[r]):
-// the rows land in LDS sorted by slot, slot j's at off_[j] .. off_[j + 1].
+// Steps 1-3 above for one sub-chunk of at most 64 kW kR pulses on a
+// workgroup of kW waves (this thread's pulses 64 R wave + 64 r + lane,
+// r < R: slots k[r], rows f[r]): the rows land in LDS sorted by slot, slot
+// j's at off_[j] .. off_[j + 1] (T <= 64 kW slots).  cnt: LDS int[kW T],
+// bm: LDS uint64[kW T], zero on entry and on return; s_ws: LDS int[kW].
 // Ends with a workgroup barrier; k and f are not needed afterwards.
-template <int NC>
-__device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float (&f)[kSrtR][NC],
+template <int NC, int kW = kSrtW, int kR = kSrtR>
+__device__ __forceinline__ void sorted_place(const int (&k)[kR], const float (&f)[kR][NC],
                                              int len, int T, float* s_rows, int* cnt, int* off_,
                                              int* s_ws, unsigned long long* bm) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
-    const int R = srt_windows(len);
+    const int R = srt_windows<kW>(len);
     const int w0 = 64 * R * wave;  // this wave's first pulse
     // 1. counts per (wave, slot)
-    for (int q = tid; q < kSrtW * T; q += kSrtT) cnt[q] = 0;
+    for (int q = tid; q < kW * T; q += 64 * kW) cnt[q] = 0;
     lds_barrier();
     int* __restrict__ wc = cnt + wave * T;
 #pragma unroll
-    for (int r = 0; r < kSrtR; ++r) {
+    for (int r = 0; r < kR; ++r) {
         const int i = w0 + 64 * r + lane;
         if (r < R && i < len && (unsigned)k[r] < (unsigned)T) atomicAdd(&wc[k[r]], 1);
     }
@@ -2776,7 +2780,7 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
         int tot = 0;
         if (j < T)
 #pragma unroll
-            for (int w = 0; w < kSrtW; ++w) tot += cnt[w * T + j];
+            for (int w = 0; w < kW; ++w) tot += cnt[w * T + j];
         const int incl = wave_incl_scan(tot);
         if (lane == 63) s_ws[wave] = incl;
         lds_barrier();
@@ -2786,7 +2790,7 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
             off_[j] = run;
             int pos = run;
 #pragma unroll
-            for (int w = 0; w < kSrtW; ++w) {
+            for (int w = 0; w < kW; ++w) {
                 const int v = cnt[w * T + j];
                 cnt[w * T + j] = pos;
                 pos += v;
@@ -2794,7 +2798,7 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
         }
         if (j == 0) {
             int total = 0;
-            for (int w = 0; w < kSrtW; ++w) total += s_ws[w];
+            for (int w = 0; w < kW; ++w) total += s_ws[w];
             off_[T] = total;
         }
     }
@@ -2803,7 +2807,7 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
     unsigned long long* __restrict__ wm = bm + wave * T;
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int r = 0; r < kSrtR; ++r) {
+    for (int r = 0; r < kR; ++r) {
         if (r >= R) break;  // R is uniform: the whole workgroup leaves together
         const int i = w0 + 64 * r + lane;
         const bool ok = i < len && (unsigned)k[r] < (unsigned)T;
@@ -2832,8 +2836,9 @@ __device__ __forceinline__ void sorted_place(const int (&k)[kSrtR], const float 
 // float64 sums (which carry over from earlier sub-chunks).  Ends with a
 // barrier that orders LDS only.
 template <int NC>
-__device__ __forceinline__ void sorted_sums(int T, int wcol, const float* s_rows, const int* off_,
-                                            double& W, double (&S)[NC], int& count) {
+__device__ __forceinline__ void sorted_sums(int T, int wcol, const float* s_rows,
+                                            const float* zrow, const int* off_, double& W,
+                                            double (&S)[NC], int& count) {
     const int tid = threadIdx.x;
     if (tid < T) {
         const int mb = off_[tid], me = off_[tid + 1];
@@ -2848,7 +2853,6 @@ __device__ __forceinline__ void sorted_sums(int T, int wcol, const float* s_rows
         const int wc = weighted ? wcol : 0;
         const int wkeep = weighted ? -1 : 0;
         const int wone = weighted ? 0 : 0x3f800000;
-        const float* __restrict__ zrow = s_rows + kPoolChunk * NC;
         constexpr int U = 4;
         for (int m0 = mb; m0 < me; m0 += U) {
             float fv[U][NC], wv[U];
@@ -2893,6 +2897,7 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
     unsigned long long* bm = reinterpret_cast<unsigned long long*>(
         off_ + ((P + 2) & ~1));                                              // [kSrtW][P]
     for (int q = tid; q < kSrtW * P; q += kSrtT) bm[q] = 0ull;
+    const float* zrow = s_rows + kPoolChunk * NC;
     if (tid < kSrtZero) s_rows[kPoolChunk * NC + tid] = 0.0f;
     const int nchunks = a.header[6];
     const int G = gridDim.x;
@@ -3019,7 +3024,7 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
             // the rest of an event summed whole, sub-chunk after sub-chunk
             // (one ascending sum)
             for (int sb = kPoolChunk; sb < n; sb += kPoolChunk) {
-                sorted_sums<NC>(T, wcol, s_rows, off_, W, S, count);
+                sorted_sums<NC>(T, wcol, s_rows, zrow, off_, W, S, count);
                 const int sl = min(n - sb, kPoolChunk);
                 load(off, sb, sl);
                 sorted_place<NC>(k, f, sl, T, s_rows, cnt, off_, s_ws, bm);
@@ -3028,7 +3033,7 @@ __global__ __launch_bounds__(kSrtT) void pool_sorted_kernel(PoolArgs a) {
         // the rows are in LDS: the next chunk's loads go out now, behind the
         // sums and the outputs
         if (more) load_local(i + 1, m0);
-        sorted_sums<NC>(T, wcol, s_rows, off_, W, S, count);
+        sorted_sums<NC>(T, wcol, s_rows, zrow, off_, W, S, count);
         const int j = tid;
         if (part < 0) {
             if (j < P) {
@@ -3134,6 +3139,99 @@ __global__ __launch_bounds__(kSortT) void pool_knn_kernel(PoolArgs a) {
 }
 
 // ------------------------------------------- fused FPS + Voronoi pooling
+
+constexpr int kFusedR = 4;                        // 64-pulse windows per wave and sub-chunk
+constexpr int kFusedSub = 64 * kFpsW * kFusedR;  // pulses per sub-chunk (1024)
+static_assert(kFusedSub * kSrtMaxC <= kStage, "a sub-chunk's rows fit the staging area");
+static_assert((sizeof(unsigned long long) + sizeof(int)) * kFpsW * kSrtMaxP + 8 * sizeof(float) <=
+                  sizeof(int) * kFpsCap,
+              "masks, counts and the zero row fit s_perm");
+
+// Pooling of the cnt pulses one workgroup holds (an event, or a gang's
+// shard) for P <= 256 slots and NC <= 6 columns, without gathers: the pulses'
+// rows (global rows row0 + i, read whole and in order) and slots (slots[i],
+// LDS) go through sub-chunks of kFusedSub pulses, each counted and placed into
+// LDS sorted by slot (the standalone pooling's placement, on kFpsW waves) and
+// added by its slot's thread into float64 sums that carry over from one
+// sub-chunk to the next: every slot's sum is one chain in ascending pulse
+// order, the oracle's.  Thread j < T ends with slot j's weight W, sums S and
+// member count.  rows: LDS float[kFusedSub * NC]; bm: LDS uint64[kFpsW T] and
+// cw: LDS int[kFpsW T] (cleared here); zrow: LDS float[8] (zeroed here);
+// off_: LDS int[T + 1]; s_ws: LDS int[kFpsW].
+template <int NC>
+__device__ __forceinline__ void fused_sorted_sums(const PoolArgs& pa, int64_t row0,
+                                                  const int* slots, int cnt, int T, float* rows,
+                                                  unsigned long long* bm, int* cw, float* zrow,
+                                                  int* off_, int* s_ws, double& W,
+                                                  double (&S)[NC], int& count) {
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+    for (int q = tid; q < kFpsW * T; q += kFpsT) bm[q] = 0ull;  // ordered by the placement's barriers
+    if (tid < 8) zrow[tid] = 0.0f;
+    W = 0.0;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) S[q] = 0.0;
+    count = 0;
+    int k[kFusedR];
+    float f[kFusedR][NC];
+    // a sub-chunk's pulses of this thread (64 R wave + 64 r + lane, r < R),
+    // every load issued together (windows r >= R load the last pulse, which
+    // nothing reads)
+    auto load = [&](int sb) {
+        const int len = __builtin_amdgcn_readfirstlane(min(kFusedSub, cnt - sb));
+        const int R = srt_windows<kFpsW>(len);
+        const float* __restrict__ fg = pa.features + (row0 + sb) * (int64_t)NC;
+#pragma unroll
+        for (int r = 0; r < kFusedR; ++r) {
+            const int i = r < R ? min(64 * R * wave + 64 * r + lane, len - 1) : len - 1;
+            k[r] = slots[sb + i];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) f[r][q] = fg[(int64_t)i * NC + q];
+        }
+    };
+    if (cnt > 0) load(0);
+    for (int sb = 0; sb < cnt; sb += kFusedSub) {
+        const int len = __builtin_amdgcn_readfirstlane(min(kFusedSub, cnt - sb));
+        sorted_place<NC, kFpsW, kFusedR>(k, f, len, T, rows, cw, off_, s_ws, bm);
+        // the rows are in LDS: the next sub-chunk's loads go out behind the sums
+        if (sb + kFusedSub < cnt) load(sb + kFusedSub);
+        sorted_sums<NC>(T, pa.weight_col, rows, zrow, off_, W, S, count);
+    }
+}
+
+// fused_sorted_sums for one work item, then its outputs: a single-workgroup
+// event's means and member counts, or a gang shard's record of float64
+// partial sums (weight, then the columns) and member counts.
+template <int NC>
+__device__ __forceinline__ void fused_sorted_item(const SampleArgs& a, const PoolArgs& pa,
+                                                  const ItemInfo& it, int P, const int* slots,
+                                                  float* rows, int* s_perm, int* s_off,
+                                                  int* s_ws, bool gang) {
+    unsigned long long* bm = reinterpret_cast<unsigned long long*>(s_perm);
+    int* cw = s_perm + 2 * kFpsW * P;
+    float* zrow = reinterpret_cast<float*>(cw + kFpsW * P);
+    double W, S[NC];
+    int count;
+    fused_sorted_sums<NC>(pa, it.off + it.lo, slots, it.cnt, P, rows, bm, cw, zrow, s_off, s_ws,
+                          W, S, count);
+    const int j = threadIdx.x;
+    if (j >= P) return;
+    if (!gang) {
+        float* __restrict__ out = pa.pooled + (it.b * P + j) * (int64_t)NC;
+#pragma unroll
+        for (int q = 0; q < NC; ++q) out[q] = W != 0.0 ? (float)(S[q] / W) : 0.0f;
+        if (pa.cell_count) pa.cell_count[it.b * P + j] = count;
+    } else {
+        constexpr int C1 = NC + 1;
+        double* __restrict__ pj = a.gang_part + ((size_t)(it.item0 + it.g) * P + j) * C1;
+        pj[0] = W;
+#pragma unroll
+        for (int q = 0; q < NC; ++q) pj[1 + q] = S[q];
+        a.shard_cells[(size_t)(it.item0 + it.g) * (P + 1) + j] = count;
+    }
+}
 
 // Slot j's (weighted) mean of columns c0 .. c0+NC-1 from LDS rows, members
 // perm[beg .. end) in that order, kBatch at a time.  A batch is padded with
@@ -3288,35 +3386,53 @@ __global__ __launch_bounds__(kFpsT) void tokenize_kernel(SampleArgs a, PoolArgs 
         if (j1 < P) a.centroids[b * P + j1] = c1;
         return;
     }
-    // the shard's pulses sorted by slot: in s_asg itself when every slot is
-    // small, else in s_perm
-    const int* sorted = s_asg;
-    if (!block_sort_small(s_asg, it.cnt, P, s_perm, s_cnt, s_off)) {
-        block_sort_by_token(s_asg, it.cnt, P, s_perm, s_cnt, s_off);
-        sorted = s_perm;
-    }
-    if (kDirect || it.kind == 1) {
-        pool_slots_sorted(pa, b, off, P, sorted, s_off);
-        return;
-    }
-    // gang: this shard's float64 partial sums per slot (members in ascending
-    // order), published with a flag; then the G partials of each slot are
-    // added in shard order
     const int C1 = C + 1;
-    double* __restrict__ part = a.gang_part + (size_t)(it.item0 + it.g) * P * C1;
-    int32_t* __restrict__ cnts = a.shard_cells + (size_t)(it.item0 + it.g) * (P + 1);
-    for (int j = tid; j < P; j += kFpsT) {
-        const int beg = s_off[j], end = s_off[j + 1];
-        cnts[j] = end - beg;
-        double* __restrict__ pj = part + (size_t)j * C1;
-        for (int c0 = 0; c0 < C; c0 += kPoolCols) {
-            const int nc = min(kPoolCols, C - c0);
-            double W, Sx[kPoolCols];
-            pool_slot(pa, off, beg, end, c0, nc, [&](int m) { return it.lo + sorted[m]; }, W, Sx);
-            if (c0 == 0) pj[0] = W;
+    if (P <= kSrtMaxP && C <= kSrtMaxC && pa.stage_cap >= kFusedSub * C) {
+        // sub-chunks sorted into LDS: rows in the staging area, masks, counts
+        // and the zero row in s_perm (free after FPS), the per-wave totals in
+        // s_slots (used only by the streaming FPS)
+        int* sws = reinterpret_cast<int*>(s_slots);
+        const bool gang = !kDirect && it.kind == 2;
+        switch (C) {
+            case 1: fused_sorted_item<1>(a, pa, it, P, s_asg, s_feat, s_perm, s_off, sws, gang); break;
+            case 2: fused_sorted_item<2>(a, pa, it, P, s_asg, s_feat, s_perm, s_off, sws, gang); break;
+            case 3: fused_sorted_item<3>(a, pa, it, P, s_asg, s_feat, s_perm, s_off, sws, gang); break;
+            case 4: fused_sorted_item<4>(a, pa, it, P, s_asg, s_feat, s_perm, s_off, sws, gang); break;
+            case 5: fused_sorted_item<5>(a, pa, it, P, s_asg, s_feat, s_perm, s_off, sws, gang); break;
+            default: fused_sorted_item<6>(a, pa, it, P, s_asg, s_feat, s_perm, s_off, sws, gang); break;
+        }
+        if (kDirect || !gang) return;
+    } else {
+        // the shard's pulses sorted by slot: in s_asg itself when every slot
+        // is small, else in s_perm
+        const int* sorted = s_asg;
+        if (!block_sort_small(s_asg, it.cnt, P, s_perm, s_cnt, s_off)) {
+            block_sort_by_token(s_asg, it.cnt, P, s_perm, s_cnt, s_off);
+            sorted = s_perm;
+        }
+        if (kDirect || it.kind == 1) {
+            pool_slots_sorted(pa, b, off, P, sorted, s_off);
+            return;
+        }
+        // gang: this shard's float64 partial sums per slot (members in
+        // ascending order), published with a flag; then the G partials of
+        // each slot are added in shard order
+        double* __restrict__ part = a.gang_part + (size_t)(it.item0 + it.g) * P * C1;
+        int32_t* __restrict__ cnts = a.shard_cells + (size_t)(it.item0 + it.g) * (P + 1);
+        for (int j = tid; j < P; j += kFpsT) {
+            const int beg = s_off[j], end = s_off[j + 1];
+            cnts[j] = end - beg;
+            double* __restrict__ pj = part + (size_t)j * C1;
+            for (int c0 = 0; c0 < C; c0 += kPoolCols) {
+                const int nc = min(kPoolCols, C - c0);
+                double W, Sx[kPoolCols];
+                pool_slot(pa, off, beg, end, c0, nc, [&](int m) { return it.lo + sorted[m]; }, W,
+                          Sx);
+                if (c0 == 0) pj[0] = W;
 #pragma unroll
-            for (int q = 0; q < kPoolCols; ++q)
-                if (q < nc) pj[1 + c0 + q] = Sx[q];
+                for (int q = 0; q < kPoolCols; ++q)
+                    if (q < nc) pj[1 + c0 + q] = Sx[q];
+            }
         }
     }
     __threadfence();

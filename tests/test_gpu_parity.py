@@ -299,6 +299,22 @@ def test_pool_many_rounds(oracle_mod):
     _tokenize_vs_oracle(oracle_mod, b, 128, label="fused many rounds")
 
 
+def test_fused_sorted_pooling_widths(oracle_mod):
+    """The fused kernel's pooling of events and gang shards through 1024-pulse
+    sub-chunks sorted into LDS (P <= 256, rows of up to 6 columns), for every
+    row width, weighted by a column, by unit charge and as plain means, at
+    sub-chunk boundaries and with gangs; direct mode too (a bound of 4096)."""
+    ns = [1025, 2048, 3000, 4096, 9000, 600, 1024]
+    for C, cc in ((1, 0), (2, -1), (3, 1), (5, 4)):
+        b = synth.icecube_events(ns, 700 + C, C=C)
+        _tokenize_vs_oracle(oracle_mod, b, 256, charge_col=cc, label="fused sorted C=%d" % C)
+    b = synth.icecube_events(ns, 710, C=6)
+    _tokenize_vs_oracle(oracle_mod, b, 100, weighted=False, label="fused sorted plain P=100")
+    d = synth.icecube_events([1025, 2047, 4096, 300], 711, C=4)
+    _tokenize_vs_oracle(oracle_mod, d, 200, charge_col=2, label="fused sorted direct",
+                        max_event_points=4096)
+
+
 def test_tokenize_fused_edges(oracle_mod):
     """The fused Voronoi kernel on every path: pass-through, one workgroup,
     gangs (cooperative pooling across shards) and the streaming fallback."""

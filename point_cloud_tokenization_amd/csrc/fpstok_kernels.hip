@@ -1770,15 +1770,19 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
     const int valid = min(n, 64);
     uint64_t tau = ~0ull;
     if (k <= valid) {
-        int rank = 0;
-        for (int l = 0; l < 64; ++l) {
-            const uint64_t kl = ((uint64_t)(uint32_t)readlane_i((int)(mykey >> 32), l) << 32) |
-                                (uint32_t)readlane_i((int)(uint32_t)mykey, l);
-            rank += kl < mykey ? 1 : 0;
+        // the k-th smallest distance word (a key's high half) among the lane
+        // minima, bit by bit from the top: the smallest t with at least k
+        // lane minima at or below it.  Every key whose distance is at most t
+        // qualifies, so tau bounds the k-th smallest key from above (keys of
+        // equal distance only add candidates, which the exact ranking below
+        // orders).
+        const uint32_t hi = (uint32_t)(mykey >> 32);
+        uint32_t t = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t below = t | ((1u << bit) - 1u);  // this bit 0, the lower ones 1
+            if (__popcll(ballot(hi <= below)) < k) t |= 1u << bit;
         }
-        const int L = (int)__builtin_ctzll(ballot(rank == k - 1 && mykey != ~0ull));
-        tau = ((uint64_t)(uint32_t)readlane_i((int)(mykey >> 32), L) << 32) |
-              (uint32_t)readlane_i((int)(uint32_t)mykey, L);
+        tau = ((uint64_t)t << 32) | 0xFFFFFFFFull;
     }
     uint64_t* __restrict__ buf = s_buf[wave];
     int cnt = 0;

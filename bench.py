@@ -42,12 +42,12 @@ FPS_OPS_PER_POINT_ITER = 14
 # event size is under one workgroup's registers), from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE per dispatch, each scaled by its reading for a plain
 # device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
-# 2 * 378.4 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
+# 2 * 374.7 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
 # taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "0ec327471d41d2e61f3fa6e06453a1138e90bf1baeceaddf94985f720d865288",
-    "bytes": int(round((2 * 378.4 + 419.3) * 1024)),
+    "kernels_sha256": "443c5655f54156a539af6ed13bbdf76bf9eb15dfe8f16eeee67f27c62c7bcc04",
+    "bytes": int(round((2 * 374.7 + 419.3) * 1024)),
 }
 
 

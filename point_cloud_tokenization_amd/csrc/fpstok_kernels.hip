@@ -1736,7 +1736,8 @@ __global__ __launch_bounds__(kKnnT) void knn_kernel(KnnArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            knn_pool_list(a, b, off, n, j, j < T ? k : 0, lst);
+            // only the list's first entry can be a pulse
+            knn_pool_list(a, b, off, n, j, j < T && j < n ? 1 : 0, lst);
         }
         return;
     }

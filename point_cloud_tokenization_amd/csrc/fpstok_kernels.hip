@@ -473,6 +473,175 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
     return first_unselected(bm[lane]);
 }
 
+// ---------------------------------------- single-workgroup FPS: the list hit
+//
+// A run of list hits (see fps_single) as one hand-scheduled loop.  A wave on
+// its own issues one instruction every four cycles, but a vector result read
+// by the scalar unit (a compare's lane mask, a lane read feeding a scalar
+// compare), a DPP operand written by the instruction just before it, and
+// every branch each cost several issue slots when nothing independent sits
+// in between.  The compiler's schedule leaves those gaps open at the end of
+// the hit (lane maximum -> first lane -> winner's lane reads -> loop test);
+// here the pulses' distance updates, cut into two-instruction parts, fill
+// them.  Two hits per loop trip, the centroid alternating between two sets
+// of scalar registers, one conditional branch per hit.  Arithmetic and
+// operand order are those of sqd() and of the generic loop, so results are
+// bit-identical.
+//
+// Per hit j (slot j, centroid c = set I):
+//   selection s_j into lane j%64 of `sel` (lane select in m0);
+//   the list entry's distance to c, its running minimum, the wave maximum wm
+//   (six DPP steps, two independent instructions before each);
+//   the winner: first lane with lv == wm, its five values into set O;
+//   the pulses' update (distance, strict compare, slot and minimum selects);
+//   j += 1; leave when wm <= U, or when j reaches jend (set by the caller at
+//   the end of the 64-slot block of `sel`, or at P).
+// Hazard rules kept: two VALU instructions between a VGPR write and a DPP read
+// of it; at least one instruction between a VALU write of a scalar register
+// (compare mask, lane read) and any read of it.
+
+// one pulse's update in seven two-instruction parts; pulse k uses temporaries
+// T (e or f, alternating between pulses) and mask register K
+#define FH_A(k, C, T) "v_subrev_f32 %[" #T "0], %[" #C "x], %[px" #k "]\n v_subrev_f32 %[" #T "1], %[" #C "y], %[py" #k "]\n"
+#define FH_B(k, C, T) "v_subrev_f32 %[" #T "2], %[" #C "z], %[pz" #k "]\n v_subrev_f32 %[" #T "3], %[" #C "t], %[pt" #k "]\n"
+#define FH_C(k, C, T) "v_mul_f32 %[" #T "0], %[" #T "0], %[" #T "0]\n v_mul_f32 %[" #T "1], %[" #T "1], %[" #T "1]\n"
+#define FH_D(k, C, T) "v_mul_f32 %[" #T "2], %[" #T "2], %[" #T "2]\n v_mul_f32 %[" #T "3], %[" #T "3], %[" #T "3]\n"
+#define FH_E(k, C, T) "v_add_f32 %[" #T "0], %[" #T "0], %[" #T "1]\n v_add_f32 %[" #T "0], %[" #T "0], %[" #T "2]\n"
+#define FH_F(k, C, T) "v_add_f32 %[" #T "0], %[" #T "0], %[" #T "3]\n v_cmp_lt_f32_e64 %[m" #T "], %[" #T "0], %[md" #k "]\n"
+#define FH_G(k, C, T) "v_cndmask_b32_e64 %[nr" #k "], %[nr" #k "], %[vj], %[m" #T "]\n v_cndmask_b32_e64 %[md" #k "], %[md" #k "], %[" #T "0], %[m" #T "]\n"
+
+// the list entry's distance and minimum, then the copy the DPP steps reduce
+#define FH_LIST(C)                                                                       \
+    "v_subrev_f32 %[a0], %[" #C "x], %[lx]\n v_subrev_f32 %[a1], %[" #C "y], %[ly]\n"    \
+    "v_subrev_f32 %[a2], %[" #C "z], %[lz]\n v_subrev_f32 %[a3], %[" #C "t], %[lt]\n"    \
+    "v_mul_f32 %[a0], %[a0], %[a0]\n v_mul_f32 %[a1], %[a1], %[a1]\n"                    \
+    "v_mul_f32 %[a2], %[a2], %[a2]\n v_mul_f32 %[a3], %[a3], %[a3]\n"                    \
+    "v_add_f32 %[a0], %[a0], %[a1]\n v_add_f32 %[a0], %[a0], %[a2]\n"                    \
+    "v_add_f32 %[a0], %[a0], %[a3]\n v_min_i32 %[lv], %[a0], %[lv]\n"                    \
+    "v_mov_b32 %[dd], %[lv]\n"
+#define FH_DPP1 "v_max_i32_dpp %[dd], %[dd], %[dd] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+#define FH_DPP2 "v_max_i32_dpp %[dd], %[dd], %[dd] quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+#define FH_DPP3 "v_max_i32_dpp %[dd], %[dd], %[dd] row_half_mirror row_mask:0xf bank_mask:0xf\n"
+#define FH_DPP4 "v_max_i32_dpp %[dd], %[dd], %[dd] row_mirror row_mask:0xf bank_mask:0xf\n"
+#define FH_DPP5 "v_max_i32_dpp %[dd], %[dd], %[dd] row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+#define FH_DPP6 "v_max_i32_dpp %[dd], %[dd], %[dd] row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+// the winner of the hit into set O; the slot counter and the exit bound
+#define FH_WM "v_readlane_b32 %[wm], %[dd], 63\n"
+#define FH_CMP "v_cmp_eq_u32_e64 %[mw], %[wm], %[lv]\n"
+#define FH_FF1                                                                          \
+    "s_ff1_i32_b64 %[lw], %[mw]\n s_add_u32 %[j], %[j], 1\n s_add_u32 m0, m0, 1\n"      \
+    "s_cmp_eq_u32 %[j], %[jend]\n s_cselect_b32 %[ue], 0x7fffffff, %[U]\n"
+#define FH_READ(O)                                                                      \
+    "v_readlane_b32 %[" #O "x], %[lx], %[lw]\n v_readlane_b32 %[" #O "y], %[ly], %[lw]\n" \
+    "v_readlane_b32 %[" #O "z], %[lz], %[lw]\n v_readlane_b32 %[" #O "t], %[lt], %[lw]\n" \
+    "v_readlane_b32 %[" #O "s], %[li], %[lw]\n"
+#define FH_HEAD(I) "v_writelane_b32 %[sel], %[" #I "s], m0\n v_mov_b32 %[vj], %[j]\n"
+
+// One hit with the centroid in set I and the winner going to set O, for M
+// pulses per lane.  P0..P20 are the pulses' parts in issue order.
+#define FH_HIT(I, O, P0, P1, P2, P3, P4, P5, P6, P7, P8, P9, P10, TAIL)                     \
+    FH_HEAD(I) FH_LIST(I) P0 FH_DPP1 P1 FH_DPP2 P2 FH_DPP3 P3 FH_DPP4 P4 FH_DPP5 P5 FH_DPP6  \
+        P6 FH_WM P7 FH_CMP P8 P9 FH_FF1 P10 FH_READ(O) TAIL
+
+// pulse part streams: pulse k's parts A..F, then the previous pulse's G one
+// part later (so a compare's mask is never read by the next instruction)
+#define FH_HIT1(I, O)                                                                        \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
+           FH_F(0, I, e), "s_nop 1\n", "s_nop 0\n", "s_nop 0\n", "", "", "s_nop 0\n" FH_G(0, I, e))
+#define FH_HIT2(I, O)                                                                        \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
+           FH_F(0, I, e), FH_A(1, I, f), FH_G(0, I, e), FH_B(1, I, f), FH_C(1, I, f),       \
+           FH_D(1, I, f), FH_E(1, I, f) FH_F(1, I, f) "s_nop 0\n" FH_G(1, I, f))
+#define FH_HIT3(I, O)                                                                        \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
+           FH_F(0, I, e), FH_A(1, I, f), FH_G(0, I, e), FH_B(1, I, f), FH_C(1, I, f),       \
+           FH_D(1, I, f),                                                                    \
+           FH_E(1, I, f) FH_F(1, I, f) FH_A(2, I, e) FH_G(1, I, f) FH_B(2, I, e)             \
+           FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) "s_nop 0\n" FH_G(2, I, e))
+#define FH_HIT4(I, O)                                                                        \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
+           FH_F(0, I, e), FH_A(1, I, f), FH_G(0, I, e), FH_B(1, I, f), FH_C(1, I, f),       \
+           FH_D(1, I, f),                                                                    \
+           FH_E(1, I, f) FH_F(1, I, f) FH_A(2, I, e) FH_G(1, I, f) FH_B(2, I, e)             \
+           FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, f)              \
+           FH_G(2, I, e) FH_B(3, I, f) FH_C(3, I, f) FH_D(3, I, f) FH_E(3, I, f)              \
+           FH_F(3, I, f) "s_nop 0\n" FH_G(3, I, f))
+
+// the loop: two hits per trip; `which` says which set holds the last winner
+#define FH_LOOP(HIT)                                                                        \
+    "s_mov_b32 %[m0s], m0\n s_mov_b32 m0, %[jl]\n s_nop 0\n"                               \
+    "1:\n" HIT(c0, c1) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc1 2f\n"                    \
+    HIT(c1, c0) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc0 1b\n"                           \
+    "s_mov_b32 %[which], 0\n s_branch 3f\n"                                                 \
+    "2:\n s_mov_b32 %[which], 1\n"                                                          \
+    "3:\n s_mov_b32 m0, %[m0s]\n"
+
+#define FH_PULSE_IO(k) [md##k] "+v"(md[k]), [nr##k] "+v"(nr[k])
+#define FH_PULSE_IN(k) [px##k] "v"(px[k]), [py##k] "v"(py[k]), [pz##k] "v"(pz[k]), [pt##k] "v"(pt[k])
+#define FH_OUTS                                                                              \
+    [lv] "+v"(lvi), [sel] "+v"(sel), [c0x] "+s"(c0x), [c0y] "+s"(c0y), [c0z] "+s"(c0z),       \
+        [c0t] "+s"(c0t), [c0s] "+s"(c0s), [c1x] "=&s"(c1x), [c1y] "=&s"(c1y),                 \
+        [c1z] "=&s"(c1z), [c1t] "=&s"(c1t), [c1s] "=&s"(c1s), [j] "+s"(jj), [wm] "=&s"(wm),   \
+        [ue] "=&s"(ue), [lw] "=&s"(lw), [which] "=&s"(which), [me] "=&s"(me), [mf] "=&s"(mf), \
+        [mw] "=&s"(mw), [a0] "=&v"(t[0]), [a1] "=&v"(t[1]), [a2] "=&v"(t[2]),                 \
+        [a3] "=&v"(t[3]), [e0] "=&v"(t[4]), [e1] "=&v"(t[5]), [e2] "=&v"(t[6]),               \
+        [e3] "=&v"(t[7]), [f0] "=&v"(t[8]), [f1] "=&v"(t[9]), [f2] "=&v"(t[10]),              \
+        [f3] "=&v"(t[11]), [dd] "=&v"(t[12]), [vj] "=&v"(t[13]), [m0s] "=&s"(m0s)
+#define FH_INS                                                                               \
+    [lx] "v"(lx), [ly] "v"(ly), [lz] "v"(lz), [lt] "v"(lt), [li] "v"(li), [U] "s"(U),         \
+        [jend] "s"(jend), [jl] "s"(jl)
+
+// Runs list hits from slot j until the list no longer decides one (wm <= U)
+// or j + 1 reaches jend; returns with j = the last slot done, wm its list
+// maximum, and (s, c) the winner of that hit.  sel collects the selections
+// of the 64-slot block that holds j (lane q: slot 64*(j/64) + q).
+template <int M>
+__device__ __forceinline__ void fps_hit_run(const float (&px)[M], const float (&py)[M],
+                                            const float (&pz)[M], const float (&pt)[M],
+                                            float (&md)[M], int (&nr)[M], float& lv, float lx,
+                                            float ly, float lz, float lt, int li, int U, int jend,
+                                            int& j, int& wm_out, int& s, float& cx, float& cy,
+                                            float& cz, float& ct, int& sel) {
+    // every scalar operand is uniform; readfirstlane says so to the compiler
+    const auto u = [](float v) {
+        return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+    };
+    int lvi = __float_as_int(lv);
+    float c0x = u(cx), c0y = u(cy), c0z = u(cz), c0t = u(ct), c1x, c1y, c1z, c1t;
+    int c0s = __builtin_amdgcn_readfirstlane(s), c1s, wm, ue, lw, which;
+    int jj = __builtin_amdgcn_readfirstlane(j);
+    U = __builtin_amdgcn_readfirstlane(U);
+    jend = __builtin_amdgcn_readfirstlane(jend);
+    const int jl = jj & 63;
+    uint64_t me, mf, mw;
+    float t[14];
+    int m0s;  // m0 (the lane select of v_writelane) is saved and restored
+    if constexpr (M == 1) {
+        asm volatile(FH_LOOP(FH_HIT1) : FH_PULSE_IO(0), FH_OUTS : FH_PULSE_IN(0), FH_INS
+                     : "scc");
+    } else if constexpr (M == 2) {
+        asm volatile(FH_LOOP(FH_HIT2) : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_OUTS
+                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_INS : "scc");
+    } else if constexpr (M == 3) {
+        asm volatile(FH_LOOP(FH_HIT3) : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_OUTS
+                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_INS : "scc");
+    } else {
+        static_assert(M == 4, "hand-scheduled hits for 1 to 4 pulses per lane");
+        asm volatile(FH_LOOP(FH_HIT4)
+                     : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_PULSE_IO(3), FH_OUTS
+                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_PULSE_IN(3), FH_INS
+                     : "scc");
+    }
+    lv = __int_as_float(lvi);
+    j = jj - 1;
+    wm_out = wm;
+    s = which ? c1s : c0s;
+    cx = which ? c1x : c0x;
+    cy = which ? c1y : c0y;
+    cz = which ? c1z : c0z;
+    ct = which ? c1t : c0t;
+}
+
 // FPS of one event of at most 256*M pulses by one workgroup, every pulse in
 // registers (lane-blocked: thread t owns pulses t*M .. t*M+M-1).
 //
@@ -560,7 +729,15 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
     for (;;) {
         // ---- a run of iterations decided by the list
         int wm;
-        for (;;) {
+        if constexpr (M <= 4) {
+            const int j0 = j;
+            const int jb = j & ~63;
+            int sel = 0;
+            fps_hit_run<M>(px, py, pz, pt, md, nr, lv, lx, ly, lz, lt, li, U, min(P, jb + 64), j,
+                           wm, s, cx, cy, cz, ct, sel);
+            // the selections of slots j0..j (one 64-slot block)
+            if (lane >= (j0 & 63) && lane <= (j & 63)) s_sel[jb + lane] = sel;
+        } else for (;;) {
             s_sel[j] = s;
             // distances are >= +0, so their bit patterns order as signed
             // integers, and an empty entry (-1.0, negative) stays empty
@@ -588,6 +765,12 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             ++j;
         }
         if (j + 1 == P) break;
+        if (wm > U) {
+            // the run stopped at the end of a block of selections: the list
+            // still decides the next slot
+            ++j;
+            continue;
+        }
 
         // ---- exchange
         const int par = ex & 1;

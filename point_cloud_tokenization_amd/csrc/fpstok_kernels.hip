@@ -501,14 +501,16 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
 // (compare mask, lane read) and any read of it.
 
 // one pulse's update in seven two-instruction parts; pulse k uses temporaries
-// T (e or f, alternating between pulses) and mask register K
+// T0..T3, T alternating between e and a (the list's temporaries, free once
+// the list distance is done); every pulse's compare mask goes to mk, read by
+// its selects before the next pulse's compare writes it
 #define FH_A(k, C, T) "v_subrev_f32 %[" #T "0], %[" #C "x], %[px" #k "]\n v_subrev_f32 %[" #T "1], %[" #C "y], %[py" #k "]\n"
 #define FH_B(k, C, T) "v_subrev_f32 %[" #T "2], %[" #C "z], %[pz" #k "]\n v_subrev_f32 %[" #T "3], %[" #C "t], %[pt" #k "]\n"
 #define FH_C(k, C, T) "v_mul_f32 %[" #T "0], %[" #T "0], %[" #T "0]\n v_mul_f32 %[" #T "1], %[" #T "1], %[" #T "1]\n"
 #define FH_D(k, C, T) "v_mul_f32 %[" #T "2], %[" #T "2], %[" #T "2]\n v_mul_f32 %[" #T "3], %[" #T "3], %[" #T "3]\n"
 #define FH_E(k, C, T) "v_add_f32 %[" #T "0], %[" #T "0], %[" #T "1]\n v_add_f32 %[" #T "0], %[" #T "0], %[" #T "2]\n"
-#define FH_F(k, C, T) "v_add_f32 %[" #T "0], %[" #T "0], %[" #T "3]\n v_cmp_lt_f32_e64 %[m" #T "], %[" #T "0], %[md" #k "]\n"
-#define FH_G(k, C, T) "v_cndmask_b32_e64 %[nr" #k "], %[nr" #k "], %[vj], %[m" #T "]\n v_cndmask_b32_e64 %[md" #k "], %[md" #k "], %[" #T "0], %[m" #T "]\n"
+#define FH_F(k, C, T) "v_add_f32 %[" #T "0], %[" #T "0], %[" #T "3]\n v_cmp_lt_f32_e64 %[mk], %[" #T "0], %[md" #k "]\n"
+#define FH_G(k, C, T) "v_cndmask_b32_e64 %[nr" #k "], %[nr" #k "], %[vj], %[mk]\n v_cndmask_b32_e64 %[md" #k "], %[md" #k "], %[" #T "0], %[mk]\n"
 
 // the list entry's distance and minimum, then the copy the DPP steps reduce
 #define FH_LIST(C)                                                                       \
@@ -550,30 +552,30 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
            FH_F(0, I, e), "s_nop 1\n", "s_nop 0\n", "s_nop 0\n", "", "", "s_nop 0\n" FH_G(0, I, e))
 #define FH_HIT2(I, O)                                                                        \
     FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
-           FH_F(0, I, e), FH_A(1, I, f), FH_G(0, I, e), FH_B(1, I, f), FH_C(1, I, f),       \
-           FH_D(1, I, f), FH_E(1, I, f) FH_F(1, I, f) "s_nop 0\n" FH_G(1, I, f))
+           FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a),       \
+           FH_D(1, I, a), FH_E(1, I, a) FH_F(1, I, a) "s_nop 0\n" FH_G(1, I, a))
 #define FH_HIT3(I, O)                                                                        \
     FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
-           FH_F(0, I, e), FH_A(1, I, f), FH_G(0, I, e), FH_B(1, I, f), FH_C(1, I, f),       \
-           FH_D(1, I, f),                                                                    \
-           FH_E(1, I, f) FH_F(1, I, f) FH_A(2, I, e) FH_G(1, I, f) FH_B(2, I, e)             \
+           FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a),       \
+           FH_D(1, I, a),                                                                    \
+           FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e)             \
            FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) "s_nop 0\n" FH_G(2, I, e))
 #define FH_HIT4(I, O)                                                                        \
     FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
-           FH_F(0, I, e), FH_A(1, I, f), FH_G(0, I, e), FH_B(1, I, f), FH_C(1, I, f),       \
-           FH_D(1, I, f),                                                                    \
-           FH_E(1, I, f) FH_F(1, I, f) FH_A(2, I, e) FH_G(1, I, f) FH_B(2, I, e)             \
-           FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, f)              \
-           FH_G(2, I, e) FH_B(3, I, f) FH_C(3, I, f) FH_D(3, I, f) FH_E(3, I, f)              \
-           FH_F(3, I, f) "s_nop 0\n" FH_G(3, I, f))
+           FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a),       \
+           FH_D(1, I, a),                                                                    \
+           FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e)             \
+           FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a)              \
+           FH_G(2, I, e) FH_B(3, I, a) FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a)              \
+           FH_F(3, I, a) "s_nop 0\n" FH_G(3, I, a))
 
-// the loop: two hits per trip; `which` says which set holds the last winner
+// the loop: two hits per trip; the last winner is left in set 0
 #define FH_LOOP(HIT)                                                                        \
-    "s_mov_b32 %[m0s], m0\n s_mov_b32 m0, %[jl]\n s_nop 0\n"                               \
+    "s_mov_b32 %[m0s], m0\n s_and_b32 m0, %[j], 63\n s_nop 0\n"                            \
     "1:\n" HIT(c0, c1) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc1 2f\n"                    \
-    HIT(c1, c0) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc0 1b\n"                           \
-    "s_mov_b32 %[which], 0\n s_branch 3f\n"                                                 \
-    "2:\n s_mov_b32 %[which], 1\n"                                                          \
+    HIT(c1, c0) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc0 1b\n s_branch 3f\n"              \
+    "2:\n s_mov_b32 %[c0x], %[c1x]\n s_mov_b32 %[c0y], %[c1y]\n s_mov_b32 %[c0z], %[c1z]\n" \
+    " s_mov_b32 %[c0t], %[c1t]\n s_mov_b32 %[c0s], %[c1s]\n"                               \
     "3:\n s_mov_b32 m0, %[m0s]\n"
 
 #define FH_PULSE_IO(k) [md##k] "+v"(md[k]), [nr##k] "+v"(nr[k])
@@ -582,14 +584,13 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
     [lv] "+v"(lvi), [sel] "+v"(sel), [c0x] "+s"(c0x), [c0y] "+s"(c0y), [c0z] "+s"(c0z),       \
         [c0t] "+s"(c0t), [c0s] "+s"(c0s), [c1x] "=&s"(c1x), [c1y] "=&s"(c1y),                 \
         [c1z] "=&s"(c1z), [c1t] "=&s"(c1t), [c1s] "=&s"(c1s), [j] "+s"(jj), [wm] "=&s"(wm),   \
-        [ue] "=&s"(ue), [lw] "=&s"(lw), [which] "=&s"(which), [me] "=&s"(me), [mf] "=&s"(mf), \
-        [mw] "=&s"(mw), [a0] "=&v"(t[0]), [a1] "=&v"(t[1]), [a2] "=&v"(t[2]),                 \
-        [a3] "=&v"(t[3]), [e0] "=&v"(t[4]), [e1] "=&v"(t[5]), [e2] "=&v"(t[6]),               \
-        [e3] "=&v"(t[7]), [f0] "=&v"(t[8]), [f1] "=&v"(t[9]), [f2] "=&v"(t[10]),              \
-        [f3] "=&v"(t[11]), [dd] "=&v"(t[12]), [vj] "=&v"(t[13]), [m0s] "=&s"(m0s)
+        [ue] "=&s"(ue), [lw] "=&s"(lw), [mk] "=&s"(mk), [mw] "=&s"(mw),                      \
+        [a0] "=&v"(t0), [a1] "=&v"(t1), [a2] "=&v"(t2), [a3] "=&v"(t3),       \
+        [e0] "=&v"(t4), [e1] "=&v"(t5), [e2] "=&v"(t6), [e3] "=&v"(t7), [dd] "=&v"(t8),       \
+        [vj] "=&v"(t9), [m0s] "=&s"(m0s)
 #define FH_INS                                                                               \
     [lx] "v"(lx), [ly] "v"(ly), [lz] "v"(lz), [lt] "v"(lt), [li] "v"(li), [U] "s"(U),         \
-        [jend] "s"(jend), [jl] "s"(jl)
+        [jend] "s"(jend)
 
 // Runs list hits from slot j until the list no longer decides one (wm <= U)
 // or j + 1 reaches jend; returns with j = the last slot done, wm its list
@@ -608,13 +609,12 @@ __device__ __forceinline__ void fps_hit_run(const float (&px)[M], const float (&
     };
     int lvi = __float_as_int(lv);
     float c0x = u(cx), c0y = u(cy), c0z = u(cz), c0t = u(ct), c1x, c1y, c1z, c1t;
-    int c0s = __builtin_amdgcn_readfirstlane(s), c1s, wm, ue, lw, which;
+    int c0s = __builtin_amdgcn_readfirstlane(s), c1s, wm, ue, lw;
     int jj = __builtin_amdgcn_readfirstlane(j);
     U = __builtin_amdgcn_readfirstlane(U);
     jend = __builtin_amdgcn_readfirstlane(jend);
-    const int jl = jj & 63;
-    uint64_t me, mf, mw;
-    float t[14];
+    uint64_t mk, mw;
+    float t0, t1, t2, t3, t4, t5, t6, t7, t8, t9;  // temporaries
     int m0s;  // m0 (the lane select of v_writelane) is saved and restored
     if constexpr (M == 1) {
         asm volatile(FH_LOOP(FH_HIT1) : FH_PULSE_IO(0), FH_OUTS : FH_PULSE_IN(0), FH_INS
@@ -635,11 +635,11 @@ __device__ __forceinline__ void fps_hit_run(const float (&px)[M], const float (&
     lv = __int_as_float(lvi);
     j = jj - 1;
     wm_out = wm;
-    s = which ? c1s : c0s;
-    cx = which ? c1x : c0x;
-    cy = which ? c1y : c0y;
-    cz = which ? c1z : c0z;
-    ct = which ? c1t : c0t;
+    s = c0s;
+    cx = c0x;
+    cy = c0y;
+    cz = c0z;
+    ct = c0t;
 }
 
 // FPS of one event of at most 256*M pulses by one workgroup, every pulse in

@@ -423,6 +423,11 @@ struct SingleLds {
     uint32_t bm[kFpsW][64];    // per-wave selection bitmap (degenerate case only)
 };
 
+static_assert(offsetof(SingleLds, ov) == 0 && offsetof(SingleLds, oi) == 2048 &&
+                  offsetof(SingleLds, oc) == 4096 && offsetof(SingleLds, wc) == 12288 &&
+                  offsetof(SingleLds, wb) == 12320,
+              "the hand-scheduled exchange addresses this layout");
+
 // LDS of a shard's own exchange in the gang FPS.
 struct FpsLds {
     FpsSlot wl[kFpsW][64];    // each wave's contribution to an exchange
@@ -560,28 +565,126 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
            FH_D(1, I, a),                                                                    \
            FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e)             \
            FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) "s_nop 0\n" FH_G(2, I, e))
-#define FH_HIT4(I, O)                                                                        \
-    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),  \
-           FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a),       \
-           FH_D(1, I, a),                                                                    \
-           FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e)             \
-           FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a)              \
-           FH_G(2, I, e) FH_B(3, I, a) FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a)              \
-           FH_F(3, I, a) "s_nop 0\n" FH_G(3, I, a))
+// The exchange of the usual case, for 2 or 3 pulses per lane, in the same
+// loop (label 5): the steps of the exchange in fps_single with the same
+// LDS layout (SingleLds, parity ex & 1).  Each lane's farthest pulse and
+// second distance; the wave's largest second distance by DPP; the offers
+// (farthest >= that bound, and >= 0) written under an exec mask, their rank
+// from mbcnt of exec; lane 0 writes the wave's count and bound; a barrier;
+// every lane reads the four counts and bounds (U = the largest bound, >= 0);
+// when the offers fit the list, lane l loads offer l of the waves'
+// concatenation (lanes past the total: empty) and the list's maximum and
+// first lane give the next centroid, into set 0; then the hits go on.
+// Leaves the loop with code 1 (the list overflows: the caller's exchange
+// redoes it with the next parity) or code 2 (every distance is 0: the list
+// and U are new, the caller picks the lowest unselected pulse).
+#define FH_BEST(k)                                                                         \
+    "v_cmp_gt_i32_e64 %[mk], %[md" #k "], %[e0]\n v_max_i32 %[e3], %[e1], %[md" #k "]\n"      \
+    "s_nop 0\n v_cndmask_b32_e64 %[e1], %[e3], %[e0], %[mk]\n"                              \
+    "v_cndmask_b32_e64 %[e0], %[e0], %[md" #k "], %[mk]\n"                                  \
+    "v_cndmask_b32_e64 %[e2], %[e2], " #k ", %[mk]\n"                                       \
+    "v_cndmask_b32_e64 %[a0], %[a0], %[px" #k "], %[mk]\n"                                  \
+    "v_cndmask_b32_e64 %[a1], %[a1], %[py" #k "], %[mk]\n"                                  \
+    "v_cndmask_b32_e64 %[a2], %[a2], %[pz" #k "], %[mk]\n"                                  \
+    "v_cndmask_b32_e64 %[a3], %[a3], %[pt" #k "], %[mk]\n"
+#define FH_BEST0                                                                           \
+    "v_mov_b32 %[e0], %[md0]\n v_bfrev_b32 %[e1], 1\n v_mov_b32 %[e2], 0\n"                 \
+    "v_mov_b32 %[a0], %[px0]\n v_mov_b32 %[a1], %[py0]\n v_mov_b32 %[a2], %[pz0]\n"         \
+    "v_mov_b32 %[a3], %[pt0]\n"
+// The second centroid set (c1) is free during an exchange and serves as its
+// scalar temporaries.  LDS layout the exchange addresses directly (SingleLds):
+// ov at 0, oi at 2048, oc at 4096, wc at 12288, wb at 12320; parity p of
+// ov/oi at +1024p, of oc at +4096p, of wc/wb at +16p; wave w at +256w
+// (ov, oi), +1024w (oc), +4w (wc, wb).
+#define FH_EXCH(BEST)                                                                      \
+    "5:\n" FH_BEST0 BEST                                                                   \
+    "v_mov_b32 %[dd], %[e1]\n v_add_u32 %[e2], %[e2], %[lb]\n s_nop 0\n"                    \
+    FH_DPP1 "s_nop 1\n" FH_DPP2 "s_nop 1\n" FH_DPP3 "s_nop 1\n" FH_DPP4 "s_nop 1\n"          \
+    FH_DPP5 "s_nop 1\n" FH_DPP6 "s_nop 1\n"                                                 \
+    "v_readlane_b32 %[wm], %[dd], 63\n"                                                    \
+    "s_and_b32 %[c1y], %[ex], 1\n s_lshl_b32 %[c1y], %[c1y], 10\n s_add_u32 %[c1y], %[c1y], %[lds]\n" \
+    "v_cmp_le_i32_e64 %[mw], 0, %[e0]\n"                                                    \
+    "v_cmp_ge_i32_e64 %[mk], %[e0], %[wm]\n"                                                \
+    "s_lshl_b32 %[ue], %[wave], 8\n s_add_u32 %[ue], %[ue], %[c1y]\n"                         \
+    "s_lshl_b32 %[lw], %[wave], 10\n s_add_u32 %[lw], %[lw], %[lds]\n"                       \
+    "s_add_u32 %[lw], %[lw], 0x1000\n s_and_b32 %[c1x], %[ex], 1\n"                          \
+    "s_lshl_b32 %[c1x], %[c1x], 12\n s_add_u32 %[lw], %[lw], %[c1x]\n"                          \
+    "s_and_b64 %[mk], %[mk], %[mw]\n s_mov_b64 %[mw], exec\n s_mov_b64 exec, %[mk]\n"        \
+    "s_nop 1\n"                                                                            \
+    "v_mbcnt_lo_u32_b32 %[vj], exec_lo, 0\n v_mbcnt_hi_u32_b32 %[vj], exec_hi, %[vj]\n"     \
+    "v_lshl_add_u32 %[dd], %[vj], 2, %[ue]\n v_lshl_add_u32 %[vj], %[vj], 4, %[lw]\n"        \
+    "ds_write2st64_b32 %[dd], %[e0], %[e2] offset1:8\n"                                     \
+    "ds_write2_b32 %[vj], %[a0], %[a1] offset1:1\n"                                         \
+    "ds_write2_b32 %[vj], %[a2], %[a3] offset0:2 offset1:3\n"                               \
+    "s_bcnt1_i32_b64 %[lw], %[mk]\n s_mov_b64 exec, 1\n"                                    \
+    "s_and_b32 %[ue], %[ex], 1\n s_lshl_b32 %[ue], %[ue], 4\n s_add_u32 %[ue], %[ue], %[lds]\n" \
+    "s_add_u32 %[ue], %[ue], 0x3000\n s_nop 0\n"                                            \
+    "v_mov_b32 %[e1], %[lw]\n v_mov_b32 %[e3], %[wm]\n v_mov_b32 %[dd], %[wave]\n"          \
+    "v_lshl_add_u32 %[dd], %[dd], 2, %[ue]\n"                                               \
+    "ds_write2_b32 %[dd], %[e1], %[e3] offset1:8\n"                                         \
+    "s_mov_b64 exec, %[mw]\n"                                                              \
+    "s_waitcnt lgkmcnt(0)\n s_barrier\n"                                                   \
+    "v_mov_b32 %[dd], %[ue]\n s_add_u32 %[c1x], %[c1x], %[lds]\n s_add_u32 %[c1x], %[c1x], 0x1000\n" \
+    "ds_read_b32 %[e0], %[dd]\n ds_read_b32 %[e1], %[dd] offset:4\n"                        \
+    "ds_read_b32 %[e2], %[dd] offset:8\n ds_read_b32 %[e3], %[dd] offset:12\n"              \
+    "ds_read_b32 %[a0], %[dd] offset:32\n ds_read_b32 %[a1], %[dd] offset:36\n"             \
+    "ds_read_b32 %[a2], %[dd] offset:40\n ds_read_b32 %[a3], %[dd] offset:44\n"             \
+    "s_add_u32 %[ex], %[ex], 1\n"                                                          \
+    "s_waitcnt lgkmcnt(0)\n"                                                               \
+    "v_max3_i32 %[a0], %[a0], %[a1], %[a2]\n v_max3_i32 %[a0], %[a0], %[a3], 0\n"           \
+    "v_add_u32 %[a1], %[e0], %[e1]\n v_add3_u32 %[a2], %[e0], %[e1], %[e2]\n"               \
+    "v_add_u32 %[a3], %[a2], %[e3]\n"                                                      \
+    "v_readfirstlane_b32 %[ue], %[a0]\n v_readfirstlane_b32 %[lw], %[a3]\n"                 \
+    "v_cmp_ge_u32_e64 %[mk], %[lane], %[e0]\n v_mov_b32 %[dd], 0\n"                        \
+    "v_cndmask_b32_e64 %[vj], 0, 1, %[mk]\n v_cndmask_b32_e64 %[dd], %[dd], %[e0], %[mk]\n" \
+    "v_cmp_ge_u32_e64 %[mk], %[lane], %[a1]\n s_nop 0\n"                                   \
+    "v_cndmask_b32_e64 %[vj], %[vj], 2, %[mk]\n v_cndmask_b32_e64 %[dd], %[dd], %[a1], %[mk]\n" \
+    "v_cmp_ge_u32_e64 %[mk], %[lane], %[a2]\n s_nop 0\n"                                   \
+    "v_cndmask_b32_e64 %[vj], %[vj], 3, %[mk]\n v_cndmask_b32_e64 %[dd], %[dd], %[a2], %[mk]\n" \
+    "v_sub_u32 %[dd], %[lane], %[dd]\n"                                                    \
+    "s_cmp_gt_i32 %[lw], 64\n s_cbranch_scc1 6f\n"                                          \
+    "v_lshlrev_b32 %[e1], 8, %[vj]\n v_lshl_add_u32 %[e1], %[dd], 2, %[e1]\n"               \
+    "v_add_u32 %[e1], %[c1y], %[e1]\n"                                                      \
+    "v_lshlrev_b32 %[e2], 10, %[vj]\n v_lshl_add_u32 %[e2], %[dd], 4, %[e2]\n"              \
+    "v_add_u32 %[e2], %[c1x], %[e2]\n"                                                      \
+    "v_cmp_gt_u32_e64 %[mk], %[a3], %[lane]\n v_mov_b32 %[lv], 0xbf800000\n"               \
+    "s_mov_b32 %[U], %[ue]\n s_mov_b64 %[mw], exec\n s_mov_b64 exec, %[mk]\n"               \
+    "ds_read_b32 %[lv], %[e1]\n ds_read_b32 %[li], %[e1] offset:2048\n"                     \
+    "ds_read_b32 %[lx], %[e2]\n ds_read_b32 %[ly], %[e2] offset:4\n"                        \
+    "ds_read_b32 %[lz], %[e2] offset:8\n ds_read_b32 %[lt], %[e2] offset:12\n"              \
+    "s_mov_b64 exec, %[mw]\n s_waitcnt lgkmcnt(0)\n"                                        \
+    "v_mov_b32 %[dd], %[lv]\n s_nop 1\n"                                                   \
+    FH_DPP1 "s_nop 1\n" FH_DPP2 "s_nop 1\n" FH_DPP3 "s_nop 1\n" FH_DPP4 "s_nop 1\n"          \
+    FH_DPP5 "s_nop 1\n" FH_DPP6 "s_nop 1\n"                                                 \
+    "v_readlane_b32 %[wm], %[dd], 63\n s_nop 0\n"                                          \
+    "v_cmp_eq_u32_e64 %[mk], %[wm], %[lv]\n"                                                \
+    "s_cmp_lt_i32 %[wm], 1\n s_cbranch_scc1 7f\n"                                           \
+    "s_ff1_i32_b64 %[lw], %[mk]\n s_nop 0\n"                                               \
+    FH_READ(c0) "s_branch 1b\n"                                                            \
+    "6:\n s_mov_b32 %[code], 1\n s_branch 4f\n"                                             \
+    "7:\n s_mov_b32 %[code], 2\n s_branch 4f\n"
 
-// the loop: two hits per trip; the last winner is left in set 0
-#define FH_LOOP(HIT)                                                                        \
-    "s_mov_b32 %[m0s], m0\n s_and_b32 m0, %[j], 63\n s_nop 0\n"                            \
+// the loop: two hits per trip; a hit whose list no longer decides goes to the
+// exchange (or, for one pulse per lane, back to the caller); the last winner
+// is left in set 0
+#define FH_LOOP(HIT, EXCH)                                                                  \
+    "s_mov_b32 %[m0s], m0\n s_and_b32 m0, %[j], 63\n s_mov_b32 %[code], 0\n"                 \
     "1:\n" HIT(c0, c1) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc1 2f\n"                    \
-    HIT(c1, c0) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc0 1b\n s_branch 3f\n"              \
-    "2:\n s_mov_b32 %[c0x], %[c1x]\n s_mov_b32 %[c0y], %[c1y]\n s_mov_b32 %[c0z], %[c1z]\n" \
-    " s_mov_b32 %[c0t], %[c1t]\n s_mov_b32 %[c0s], %[c1s]\n"                               \
-    "3:\n s_mov_b32 m0, %[m0s]\n"
+    HIT(c1, c0) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc0 1b\n"                           \
+    "s_cmp_eq_u32 %[j], %[jend]\n s_cbranch_scc0 5f\n s_branch 4f\n"                        \
+    "2:\n s_cmp_eq_u32 %[j], %[jend]\n s_cbranch_scc0 5f\n"                                 \
+    "s_mov_b32 %[c0x], %[c1x]\n s_mov_b32 %[c0y], %[c1y]\n s_mov_b32 %[c0z], %[c1z]\n"        \
+    " s_mov_b32 %[c0t], %[c1t]\n s_mov_b32 %[c0s], %[c1s]\n s_branch 4f\n"                   \
+    EXCH                                                                                   \
+    "4:\n s_mov_b32 m0, %[m0s]\n"
+#define FH_EXCH1 "5:\n s_mov_b32 %[code], 1\n"
 
 #define FH_PULSE_IO(k) [md##k] "+v"(md[k]), [nr##k] "+v"(nr[k])
 #define FH_PULSE_IN(k) [px##k] "v"(px[k]), [py##k] "v"(py[k]), [pz##k] "v"(pz[k]), [pt##k] "v"(pt[k])
 #define FH_OUTS                                                                              \
-    [lv] "+v"(lvi), [sel] "+v"(sel), [c0x] "+s"(c0x), [c0y] "+s"(c0y), [c0z] "+s"(c0z),       \
+    [lv] "+v"(lvi), [sel] "+v"(sel), [lx] "+v"(lx), [ly] "+v"(ly), [lz] "+v"(lz),             \
+        [lt] "+v"(lt), [li] "+v"(li), [U] "+s"(U), [ex] "+s"(ex), [code] "=&s"(code),          \
+        [c0x] "+s"(c0x), [c0y] "+s"(c0y), [c0z] "+s"(c0z),       \
         [c0t] "+s"(c0t), [c0s] "+s"(c0s), [c1x] "=&s"(c1x), [c1y] "=&s"(c1y),                 \
         [c1z] "=&s"(c1z), [c1t] "=&s"(c1t), [c1s] "=&s"(c1s), [j] "+s"(jj), [wm] "=&s"(wm),   \
         [ue] "=&s"(ue), [lw] "=&s"(lw), [mk] "=&s"(mk), [mw] "=&s"(mw),                      \
@@ -589,48 +692,53 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
         [e0] "=&v"(t4), [e1] "=&v"(t5), [e2] "=&v"(t6), [e3] "=&v"(t7), [dd] "=&v"(t8),       \
         [vj] "=&v"(t9), [m0s] "=&s"(m0s)
 #define FH_INS                                                                               \
-    [lx] "v"(lx), [ly] "v"(ly), [lz] "v"(lz), [lt] "v"(lt), [li] "v"(li), [U] "s"(U),         \
-        [jend] "s"(jend)
+    [jend] "s"(jend), [lds] "s"(lds), [wave] "s"(wave), [lane] "v"(lane), [lb] "v"(lbase)
 
-// Runs list hits from slot j until the list no longer decides one (wm <= U)
-// or j + 1 reaches jend; returns with j = the last slot done, wm its list
-// maximum, and (s, c) the winner of that hit.  sel collects the selections
-// of the 64-slot block that holds j (lane q: slot 64*(j/64) + q).
+// Runs list hits from slot j, with the exchanges of the usual case in
+// between, until j + 1 reaches jend (the end of the 64-slot block of `sel`,
+// or P; code 0), an exchange overflows the list (code 1: the caller's
+// exchange redoes it) or finds every distance 0 (code 2: the list and U are
+// new, the caller picks the lowest unselected pulse).  Returns with j = the
+// last slot done, wm its list maximum, (s, c) the winner of that hit, and
+// the list, U and the exchange count ex as they stand.  sel collects the
+// selections of the block (lane q: slot 64*(j/64) + q).
 template <int M>
-__device__ __forceinline__ void fps_hit_run(const float (&px)[M], const float (&py)[M],
-                                            const float (&pz)[M], const float (&pt)[M],
-                                            float (&md)[M], int (&nr)[M], float& lv, float lx,
-                                            float ly, float lz, float lt, int li, int U, int jend,
-                                            int& j, int& wm_out, int& s, float& cx, float& cy,
-                                            float& cz, float& ct, int& sel) {
+__device__ __forceinline__ int fps_hit_run(const float (&px)[M], const float (&py)[M],
+                                           const float (&pz)[M], const float (&pt)[M],
+                                           float (&md)[M], int (&nr)[M], float& lv, float& lx,
+                                           float& ly, float& lz, float& lt, int& li, int& U,
+                                           int& ex, int jend, int& j, int& wm_out, int& s,
+                                           float& cx, float& cy, float& cz, float& ct, int& sel,
+                                           SingleLds& L, int wave, int lane, int lbase) {
     // every scalar operand is uniform; readfirstlane says so to the compiler
     const auto u = [](float v) {
         return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
     };
     int lvi = __float_as_int(lv);
     float c0x = u(cx), c0y = u(cy), c0z = u(cz), c0t = u(ct), c1x, c1y, c1z, c1t;
-    int c0s = __builtin_amdgcn_readfirstlane(s), c1s, wm, ue, lw;
+    int c0s = __builtin_amdgcn_readfirstlane(s), c1s, wm, ue, lw, code;
     int jj = __builtin_amdgcn_readfirstlane(j);
     U = __builtin_amdgcn_readfirstlane(U);
+    ex = __builtin_amdgcn_readfirstlane(ex);
     jend = __builtin_amdgcn_readfirstlane(jend);
+    wave = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(&L));
     uint64_t mk, mw;
     float t0, t1, t2, t3, t4, t5, t6, t7, t8, t9;  // temporaries
     int m0s;  // m0 (the lane select of v_writelane) is saved and restored
     if constexpr (M == 1) {
-        asm volatile(FH_LOOP(FH_HIT1) : FH_PULSE_IO(0), FH_OUTS : FH_PULSE_IN(0), FH_INS
-                     : "scc");
+        asm volatile(FH_LOOP(FH_HIT1, FH_EXCH1) : FH_PULSE_IO(0), FH_OUTS : FH_PULSE_IN(0), FH_INS
+                     : "scc", "memory");
     } else if constexpr (M == 2) {
-        asm volatile(FH_LOOP(FH_HIT2) : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_OUTS
-                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_INS : "scc");
-    } else if constexpr (M == 3) {
-        asm volatile(FH_LOOP(FH_HIT3) : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_OUTS
-                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_INS : "scc");
+        asm volatile(FH_LOOP(FH_HIT2, FH_EXCH(FH_BEST(1)))
+                     : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_OUTS
+                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_INS : "scc", "memory");
     } else {
-        static_assert(M == 4, "hand-scheduled hits for 1 to 4 pulses per lane");
-        asm volatile(FH_LOOP(FH_HIT4)
-                     : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_PULSE_IO(3), FH_OUTS
-                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_PULSE_IN(3), FH_INS
-                     : "scc");
+        static_assert(M == 3, "hand-scheduled hits for 1 to 3 pulses per lane");
+        asm volatile(FH_LOOP(FH_HIT3, FH_EXCH(FH_BEST(1) FH_BEST(2)))
+                     : FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_OUTS
+                     : FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_INS : "scc", "memory");
     }
     lv = __int_as_float(lvi);
     j = jj - 1;
@@ -640,6 +748,7 @@ __device__ __forceinline__ void fps_hit_run(const float (&px)[M], const float (&
     cy = c0y;
     cz = c0z;
     ct = c0t;
+    return code;
 }
 
 // FPS of one event of at most 256*M pulses by one workgroup, every pulse in
@@ -729,14 +838,27 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
     for (;;) {
         // ---- a run of iterations decided by the list
         int wm;
-        if constexpr (M <= 4) {
+        if constexpr (M <= 3) {
             const int j0 = j;
             const int jb = j & ~63;
             int sel = 0;
-            fps_hit_run<M>(px, py, pz, pt, md, nr, lv, lx, ly, lz, lt, li, U, min(P, jb + 64), j,
-                           wm, s, cx, cy, cz, ct, sel);
+            const int code = fps_hit_run<M>(px, py, pz, pt, md, nr, lv, lx, ly, lz, lt, li, U, ex,
+                                            min(P, jb + 64), j, wm, s, cx, cy, cz, ct, sel, L,
+                                            wave, lane, lbase);
             // the selections of slots j0..j (one 64-slot block)
             if (lane >= (j0 & 63) && lane <= (j & 63)) s_sel[jb + lane] = sel;
+            if (code == 2) {
+                // the exchange found every distance 0: the lowest unselected pulse
+                s = min(first_unselected_sel(L.bm[wave], s_sel, j), n - 1);
+                const float4 q = p[s];
+                cx = readlane_f(q.x, 0);
+                cy = readlane_f(q.y, 0);
+                cz = readlane_f(q.z, 0);
+                ct = readlane_f(q.w, 0);
+                ++j;
+                continue;
+            }
+            if (code == 1) wm = INT32_MIN;  // the exchange below redoes it
         } else for (;;) {
             s_sel[j] = s;
             // distances are >= +0, so their bit patterns order as signed

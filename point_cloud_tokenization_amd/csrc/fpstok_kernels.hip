@@ -517,16 +517,18 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
 #define FH_F(k, C, T) "v_add_f32 %[" #T "0], %[" #T "0], %[" #T "3]\n v_cmp_lt_f32_e64 %[mk], %[" #T "0], %[md" #k "]\n"
 #define FH_G(k, C, T) "v_cndmask_b32_e64 %[nr" #k "], %[nr" #k "], %[vj], %[mk]\n v_cndmask_b32_e64 %[md" #k "], %[md" #k "], %[" #T "0], %[mk]\n"
 
-// the list entry's distance and minimum, then the copy the DPP steps reduce
+// the list entry's distance and its running minimum
 #define FH_LIST(C)                                                                       \
     "v_subrev_f32 %[a0], %[" #C "x], %[lx]\n v_subrev_f32 %[a1], %[" #C "y], %[ly]\n"    \
     "v_subrev_f32 %[a2], %[" #C "z], %[lz]\n v_subrev_f32 %[a3], %[" #C "t], %[lt]\n"    \
     "v_mul_f32 %[a0], %[a0], %[a0]\n v_mul_f32 %[a1], %[a1], %[a1]\n"                    \
     "v_mul_f32 %[a2], %[a2], %[a2]\n v_mul_f32 %[a3], %[a3], %[a3]\n"                    \
     "v_add_f32 %[a0], %[a0], %[a1]\n v_add_f32 %[a0], %[a0], %[a2]\n"                    \
-    "v_add_f32 %[a0], %[a0], %[a3]\n v_min_i32 %[lv], %[a0], %[lv]\n"                    \
-    "v_mov_b32 %[dd], %[lv]\n"
+    "v_add_f32 %[a0], %[a0], %[a3]\n v_min_i32 %[lv], %[a0], %[lv]\n"
 #define FH_DPP1 "v_max_i32_dpp %[dd], %[dd], %[dd] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+// the first step of a hit's reduction reads the list values themselves: a
+// quad permute has a source in every lane, so every lane of dd is written
+#define FH_DPP1L "v_max_i32_dpp %[dd], %[lv], %[lv] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
 #define FH_DPP2 "v_max_i32_dpp %[dd], %[dd], %[dd] quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
 #define FH_DPP3 "v_max_i32_dpp %[dd], %[dd], %[dd] row_half_mirror row_mask:0xf bank_mask:0xf\n"
 #define FH_DPP4 "v_max_i32_dpp %[dd], %[dd], %[dd] row_mirror row_mask:0xf bank_mask:0xf\n"
@@ -547,7 +549,7 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
 // One hit with the centroid in set I and the winner going to set O, for M
 // pulses per lane.  P0..P20 are the pulses' parts in issue order.
 #define FH_HIT(I, O, P0, P1, P2, P3, P4, P5, P6, P7, P8, P9, P10, TAIL)                     \
-    FH_HEAD(I) FH_LIST(I) P0 FH_DPP1 P1 FH_DPP2 P2 FH_DPP3 P3 FH_DPP4 P4 FH_DPP5 P5 FH_DPP6  \
+    FH_HEAD(I) FH_LIST(I) P0 FH_DPP1L P1 FH_DPP2 P2 FH_DPP3 P3 FH_DPP4 P4 FH_DPP5 P5 FH_DPP6  \
         P6 FH_WM P7 FH_CMP P8 P9 FH_FF1 P10 FH_READ(O) TAIL
 
 // pulse part streams: pulse k's parts A..F, then the previous pulse's G one
@@ -599,16 +601,14 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
 #define FH_EXCH(BEST)                                                                      \
     "5:\n" FH_BEST0 BEST                                                                   \
     "v_mov_b32 %[dd], %[e1]\n v_add_u32 %[e2], %[e2], %[lb]\n s_nop 0\n"                    \
-    FH_DPP1 "s_nop 1\n" FH_DPP2 "s_nop 1\n" FH_DPP3 "s_nop 1\n" FH_DPP4 "s_nop 1\n"          \
-    FH_DPP5 "s_nop 1\n" FH_DPP6 "s_nop 1\n"                                                 \
-    "v_readlane_b32 %[wm], %[dd], 63\n"                                                    \
-    "s_and_b32 %[c1y], %[ex], 1\n s_lshl_b32 %[c1y], %[c1y], 10\n s_add_u32 %[c1y], %[c1y], %[lds]\n" \
-    "v_cmp_le_i32_e64 %[mw], 0, %[e0]\n"                                                    \
-    "v_cmp_ge_i32_e64 %[mk], %[e0], %[wm]\n"                                                \
-    "s_lshl_b32 %[ue], %[wave], 8\n s_add_u32 %[ue], %[ue], %[c1y]\n"                         \
-    "s_lshl_b32 %[lw], %[wave], 10\n s_add_u32 %[lw], %[lw], %[lds]\n"                       \
-    "s_add_u32 %[lw], %[lw], 0x1000\n s_and_b32 %[c1x], %[ex], 1\n"                          \
-    "s_lshl_b32 %[c1x], %[c1x], 12\n s_add_u32 %[lw], %[lw], %[c1x]\n"                          \
+    FH_DPP1 "s_and_b32 %[c1y], %[ex], 1\n s_lshl_b32 %[c1y], %[c1y], 10\n"                   \
+    FH_DPP2 "s_add_u32 %[c1y], %[c1y], %[lds]\n s_lshl_b32 %[ue], %[wave], 8\n"               \
+    FH_DPP3 "s_add_u32 %[ue], %[ue], %[c1y]\n s_lshl_b32 %[lw], %[wave], 10\n"                \
+    FH_DPP4 "s_add_u32 %[lw], %[lw], %[lds]\n s_add_u32 %[lw], %[lw], 0x1000\n"               \
+    FH_DPP5 "s_and_b32 %[c1x], %[ex], 1\n s_lshl_b32 %[c1x], %[c1x], 12\n"                   \
+    FH_DPP6 "s_add_u32 %[lw], %[lw], %[c1x]\n v_cmp_le_i32_e64 %[mw], 0, %[e0]\n"             \
+    "v_readlane_b32 %[wm], %[dd], 63\n s_nop 0\n"                                          \
+    "v_cmp_ge_i32_e64 %[mk], %[e0], %[wm]\n s_nop 0\n"                                      \
     "s_and_b64 %[mk], %[mk], %[mw]\n s_mov_b64 %[mw], exec\n s_mov_b64 exec, %[mk]\n"        \
     "s_nop 1\n"                                                                            \
     "v_mbcnt_lo_u32_b32 %[vj], exec_lo, 0\n v_mbcnt_hi_u32_b32 %[vj], exec_hi, %[vj]\n"     \
@@ -653,8 +653,7 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
     "ds_read_b32 %[lx], %[e2]\n ds_read_b32 %[ly], %[e2] offset:4\n"                        \
     "ds_read_b32 %[lz], %[e2] offset:8\n ds_read_b32 %[lt], %[e2] offset:12\n"              \
     "s_mov_b64 exec, %[mw]\n s_waitcnt lgkmcnt(0)\n"                                        \
-    "v_mov_b32 %[dd], %[lv]\n s_nop 1\n"                                                   \
-    FH_DPP1 "s_nop 1\n" FH_DPP2 "s_nop 1\n" FH_DPP3 "s_nop 1\n" FH_DPP4 "s_nop 1\n"          \
+    "s_nop 1\n" FH_DPP1L "s_nop 1\n" FH_DPP2 "s_nop 1\n" FH_DPP3 "s_nop 1\n" FH_DPP4 "s_nop 1\n"          \
     FH_DPP5 "s_nop 1\n" FH_DPP6 "s_nop 1\n"                                                 \
     "v_readlane_b32 %[wm], %[dd], 63\n s_nop 0\n"                                          \
     "v_cmp_eq_u32_e64 %[mk], %[wm], %[lv]\n"                                                \
@@ -887,11 +886,13 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             ++j;
         }
         if (j + 1 == P) break;
-        if (wm > U) {
-            // the run stopped at the end of a block of selections: the list
-            // still decides the next slot
-            ++j;
-            continue;
+        if constexpr (M <= 3) {
+            if (wm > U) {
+                // the run stopped at the end of a block of selections: the
+                // list still decides the next slot
+                ++j;
+                continue;
+            }
         }
 
         // ---- exchange

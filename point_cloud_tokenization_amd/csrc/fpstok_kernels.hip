@@ -567,6 +567,53 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
            FH_D(1, I, a),                                                                    \
            FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e)             \
            FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) "s_nop 0\n" FH_G(2, I, e))
+// 4 to 8 pulses per lane: the same stream, the hits only (the exchange is
+// the caller's)
+#define FH_HIT4(I, O)                                                                         \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
+    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
+    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
+    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
+    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) "s_nop 0\n" FH_G(3, I, a))
+#define FH_HIT5(I, O)                                                                         \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
+    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
+    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
+    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
+    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
+    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) "s_nop 0\n"          \
+    FH_G(4, I, e))
+#define FH_HIT6(I, O)                                                                         \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
+    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
+    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
+    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
+    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
+    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
+    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
+    "s_nop 0\n" FH_G(5, I, a))
+#define FH_HIT7(I, O)                                                                         \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
+    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
+    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
+    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
+    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
+    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
+    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
+    FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
+    FH_F(6, I, e) "s_nop 0\n" FH_G(6, I, e))
+#define FH_HIT8(I, O)                                                                         \
+    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
+    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
+    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
+    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
+    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
+    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
+    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
+    FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
+    FH_F(6, I, e) FH_A(7, I, a) FH_G(6, I, e) FH_B(7, I, a) FH_C(7, I, a) FH_D(7, I, a)        \
+    FH_E(7, I, a) FH_F(7, I, a) "s_nop 0\n" FH_G(7, I, a))
+
 // The exchange of the usual case, for 2 or 3 pulses per lane, in the same
 // loop (label 5): the steps of the exchange in fps_single with the same
 // LDS layout (SingleLds, parity ex & 1).  Each lane's farthest pulse and
@@ -678,6 +725,26 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
     "4:\n s_mov_b32 m0, %[m0s]\n"
 #define FH_EXCH1 "5:\n s_mov_b32 %[code], 1\n"
 
+// the loop of hits only: leaves when a hit's list no longer decides or at
+// jend; the last winner is left in set 0
+#define FH_LOOPH(HIT)                                                                      \
+    "s_mov_b32 %[m0s], m0\n s_and_b32 m0, %[j], 63\n s_nop 0\n"                            \
+    "1:\n" HIT(c0, c1) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc1 2f\n"                    \
+    HIT(c1, c0) "s_cmp_le_i32 %[wm], %[ue]\n s_cbranch_scc0 1b\n s_branch 3f\n"              \
+    "2:\n s_mov_b32 %[c0x], %[c1x]\n s_mov_b32 %[c0y], %[c1y]\n s_mov_b32 %[c0z], %[c1z]\n" \
+    " s_mov_b32 %[c0t], %[c1t]\n s_mov_b32 %[c0s], %[c1s]\n"                               \
+    "3:\n s_mov_b32 m0, %[m0s]\n"
+#define FH_OUTSH                                                                             \
+    [lv] "+v"(lvi), [sel] "+v"(sel), [c0x] "+s"(c0x), [c0y] "+s"(c0y), [c0z] "+s"(c0z),       \
+        [c0t] "+s"(c0t), [c0s] "+s"(c0s), [c1x] "=&s"(c1x), [c1y] "=&s"(c1y),                 \
+        [c1z] "=&s"(c1z), [c1t] "=&s"(c1t), [c1s] "=&s"(c1s), [j] "+s"(jj), [wm] "=&s"(wm),   \
+        [ue] "=&s"(ue), [lw] "=&s"(lw), [mk] "=&s"(mk), [mw] "=&s"(mw), [a0] "=&v"(t0),       \
+        [a1] "=&v"(t1), [a2] "=&v"(t2), [a3] "=&v"(t3), [e0] "=&v"(t4), [e1] "=&v"(t5),       \
+        [e2] "=&v"(t6), [e3] "=&v"(t7), [dd] "=&v"(t8), [vj] "=&v"(t9), [m0s] "=&s"(m0s)
+#define FH_INSH                                                                              \
+    [lx] "v"(lx), [ly] "v"(ly), [lz] "v"(lz), [lt] "v"(lt), [li] "v"(li), [U] "s"(U),         \
+        [jend] "s"(jend)
+
 #define FH_PULSE_IO(k) [md##k] "+v"(md[k]), [nr##k] "+v"(nr[k])
 #define FH_PULSE_IN(k) [px##k] "v"(px[k]), [py##k] "v"(py[k]), [pz##k] "v"(pz[k]), [pt##k] "v"(pt[k])
 #define FH_OUTS                                                                              \
@@ -748,6 +815,63 @@ __device__ __forceinline__ int fps_hit_run(const float (&px)[M], const float (&p
     cz = c0z;
     ct = c0t;
     return code;
+}
+
+// Runs list hits only (4 to 8 pulses per lane) from slot j until a hit's
+// list no longer decides (wm <= U) or j + 1 reaches jend; returns with j =
+// the last slot done, wm its list maximum and (s, c) the winner of that hit.
+template <int M>
+__device__ __forceinline__ void fps_hit_run_h(const float (&px)[M], const float (&py)[M],
+                                              const float (&pz)[M], const float (&pt)[M],
+                                              float (&md)[M], int (&nr)[M], float& lv, float lx,
+                                              float ly, float lz, float lt, int li, int U,
+                                              int jend, int& j, int& wm_out, int& s, float& cx,
+                                              float& cy, float& cz, float& ct, int& sel) {
+    const auto u = [](float v) {
+        return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+    };
+    int lvi = __float_as_int(lv);
+    float c0x = u(cx), c0y = u(cy), c0z = u(cz), c0t = u(ct), c1x, c1y, c1z, c1t;
+    int c0s = __builtin_amdgcn_readfirstlane(s), c1s, wm, ue, lw;
+    int jj = __builtin_amdgcn_readfirstlane(j);
+    U = __builtin_amdgcn_readfirstlane(U);
+    jend = __builtin_amdgcn_readfirstlane(jend);
+    uint64_t mk, mw;
+    float t0, t1, t2, t3, t4, t5, t6, t7, t8, t9;  // temporaries
+    int m0s;
+#define FH_IO4 FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_PULSE_IO(3)
+#define FH_IN4 FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_PULSE_IN(3)
+    if constexpr (M == 4) {
+        asm volatile(FH_LOOPH(FH_HIT4) : FH_IO4, FH_OUTSH : FH_IN4, FH_INSH : "scc");
+    } else if constexpr (M == 5) {
+        asm volatile(FH_LOOPH(FH_HIT5) : FH_IO4, FH_PULSE_IO(4), FH_OUTSH
+                     : FH_IN4, FH_PULSE_IN(4), FH_INSH : "scc");
+    } else if constexpr (M == 6) {
+        asm volatile(FH_LOOPH(FH_HIT6) : FH_IO4, FH_PULSE_IO(4), FH_PULSE_IO(5), FH_OUTSH
+                     : FH_IN4, FH_PULSE_IN(4), FH_PULSE_IN(5), FH_INSH : "scc");
+    } else if constexpr (M == 7) {
+        asm volatile(FH_LOOPH(FH_HIT7)
+                     : FH_IO4, FH_PULSE_IO(4), FH_PULSE_IO(5), FH_PULSE_IO(6), FH_OUTSH
+                     : FH_IN4, FH_PULSE_IN(4), FH_PULSE_IN(5), FH_PULSE_IN(6), FH_INSH : "scc");
+    } else {
+        static_assert(M == 8, "hand-scheduled hits only for 4 to 8 pulses per lane");
+        asm volatile(FH_LOOPH(FH_HIT8)
+                     : FH_IO4, FH_PULSE_IO(4), FH_PULSE_IO(5), FH_PULSE_IO(6), FH_PULSE_IO(7),
+                       FH_OUTSH
+                     : FH_IN4, FH_PULSE_IN(4), FH_PULSE_IN(5), FH_PULSE_IN(6), FH_PULSE_IN(7),
+                       FH_INSH
+                     : "scc");
+    }
+#undef FH_IO4
+#undef FH_IN4
+    lv = __int_as_float(lvi);
+    j = jj - 1;
+    wm_out = wm;
+    s = c0s;
+    cx = c0x;
+    cy = c0y;
+    cz = c0z;
+    ct = c0t;
 }
 
 // FPS of one event of at most 256*M pulses by one workgroup, every pulse in
@@ -858,6 +982,13 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
                 continue;
             }
             if (code == 1) wm = INT32_MIN;  // the exchange below redoes it
+        } else if constexpr (M <= 8) {
+            const int j0 = j;
+            const int jb = j & ~63;
+            int sel = 0;
+            fps_hit_run_h<M>(px, py, pz, pt, md, nr, lv, lx, ly, lz, lt, li, U, min(P, jb + 64), j,
+                             wm, s, cx, cy, cz, ct, sel);
+            if (lane >= (j0 & 63) && lane <= (j & 63)) s_sel[jb + lane] = sel;
         } else for (;;) {
             s_sel[j] = s;
             // distances are >= +0, so their bit patterns order as signed
@@ -886,7 +1017,7 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
             ++j;
         }
         if (j + 1 == P) break;
-        if constexpr (M <= 3) {
+        if constexpr (M <= 8) {
             if (wm > U) {
                 // the run stopped at the end of a block of selections: the
                 // list still decides the next slot

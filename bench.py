@@ -42,12 +42,12 @@ FPS_OPS_PER_POINT_ITER = 14
 # event size is under one workgroup's registers), from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE per dispatch, each scaled by its reading for a plain
 # device-to-device copy of known size (FETCH x2.000, WRITE x1.000): reads
-# 2 * 397.9 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
+# 2 * 394.0 KiB, writes 419.3 KiB.  Valid only for the kernel source it was
 # taken on; reported as null for any other.
 MEASURED_TRAFFIC = {
     "workload": HEADLINE,
-    "kernels_sha256": "cadaafe3a3664536b6566ee8ae3ef81f8ee1d46478b7aadf50f7f8627149317e",
-    "bytes": int(round((2 * 397.9 + 419.3) * 1024)),
+    "kernels_sha256": "c94222e657a0d8c24a431f48e9c099b6edc4d3641f5641c3397dcf771b1126bb",
+    "bytes": int(round((2 * 394.0 + 419.3) * 1024)),
 }
 
 

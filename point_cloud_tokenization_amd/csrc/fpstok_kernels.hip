@@ -567,7 +567,7 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
            FH_D(1, I, a),                                                                    \
            FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e)             \
            FH_C(2, I, e) FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) "s_nop 0\n" FH_G(2, I, e))
-// 4 to 16 pulses per lane: the same stream, the hits only (the exchange is
+// 4 to 8 pulses per lane: the same stream, the hits only (the exchange is
 // the caller's)
 #define FH_HIT4(I, O)                                                                         \
     FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
@@ -613,73 +613,6 @@ __device__ __forceinline__ int first_unselected_sel(uint32_t* bm, const int* s_s
     FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
     FH_F(6, I, e) FH_A(7, I, a) FH_G(6, I, e) FH_B(7, I, a) FH_C(7, I, a) FH_D(7, I, a)        \
     FH_E(7, I, a) FH_F(7, I, a) "s_nop 0\n" FH_G(7, I, a))
-#define FH_HIT10(I, O)                                                                         \
-    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
-    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
-    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
-    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
-    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
-    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
-    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
-    FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
-    FH_F(6, I, e) FH_A(7, I, a) FH_G(6, I, e) FH_B(7, I, a) FH_C(7, I, a) FH_D(7, I, a)        \
-    FH_E(7, I, a) FH_F(7, I, a) FH_A(8, I, e) FH_G(7, I, a) FH_B(8, I, e) FH_C(8, I, e)        \
-    FH_D(8, I, e) FH_E(8, I, e) FH_F(8, I, e) FH_A(9, I, a) FH_G(8, I, e) FH_B(9, I, a)        \
-    FH_C(9, I, a) FH_D(9, I, a) FH_E(9, I, a) FH_F(9, I, a) "s_nop 0\n" FH_G(9, I, a))
-#define FH_HIT12(I, O)                                                                         \
-    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
-    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
-    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
-    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
-    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
-    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
-    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
-    FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
-    FH_F(6, I, e) FH_A(7, I, a) FH_G(6, I, e) FH_B(7, I, a) FH_C(7, I, a) FH_D(7, I, a)        \
-    FH_E(7, I, a) FH_F(7, I, a) FH_A(8, I, e) FH_G(7, I, a) FH_B(8, I, e) FH_C(8, I, e)        \
-    FH_D(8, I, e) FH_E(8, I, e) FH_F(8, I, e) FH_A(9, I, a) FH_G(8, I, e) FH_B(9, I, a)        \
-    FH_C(9, I, a) FH_D(9, I, a) FH_E(9, I, a) FH_F(9, I, a) FH_A(10, I, e) FH_G(9, I, a)       \
-    FH_B(10, I, e) FH_C(10, I, e) FH_D(10, I, e) FH_E(10, I, e) FH_F(10, I, e) FH_A(11, I, a)  \
-    FH_G(10, I, e) FH_B(11, I, a) FH_C(11, I, a) FH_D(11, I, a) FH_E(11, I, a) FH_F(11, I, a)  \
-    "s_nop 0\n" FH_G(11, I, a))
-#define FH_HIT14(I, O)                                                                         \
-    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
-    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
-    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
-    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
-    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
-    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
-    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
-    FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
-    FH_F(6, I, e) FH_A(7, I, a) FH_G(6, I, e) FH_B(7, I, a) FH_C(7, I, a) FH_D(7, I, a)        \
-    FH_E(7, I, a) FH_F(7, I, a) FH_A(8, I, e) FH_G(7, I, a) FH_B(8, I, e) FH_C(8, I, e)        \
-    FH_D(8, I, e) FH_E(8, I, e) FH_F(8, I, e) FH_A(9, I, a) FH_G(8, I, e) FH_B(9, I, a)        \
-    FH_C(9, I, a) FH_D(9, I, a) FH_E(9, I, a) FH_F(9, I, a) FH_A(10, I, e) FH_G(9, I, a)       \
-    FH_B(10, I, e) FH_C(10, I, e) FH_D(10, I, e) FH_E(10, I, e) FH_F(10, I, e) FH_A(11, I, a)  \
-    FH_G(10, I, e) FH_B(11, I, a) FH_C(11, I, a) FH_D(11, I, a) FH_E(11, I, a) FH_F(11, I, a)  \
-    FH_A(12, I, e) FH_G(11, I, a) FH_B(12, I, e) FH_C(12, I, e) FH_D(12, I, e) FH_E(12, I, e)  \
-    FH_F(12, I, e) FH_A(13, I, a) FH_G(12, I, e) FH_B(13, I, a) FH_C(13, I, a) FH_D(13, I, a)  \
-    FH_E(13, I, a) FH_F(13, I, a) "s_nop 0\n" FH_G(13, I, a))
-#define FH_HIT16(I, O)                                                                         \
-    FH_HIT(I, O, FH_A(0, I, e), FH_B(0, I, e), FH_C(0, I, e), FH_D(0, I, e), FH_E(0, I, e),    \
-    FH_F(0, I, e), FH_A(1, I, a), FH_G(0, I, e), FH_B(1, I, a), FH_C(1, I, a), FH_D(1, I, a),  \
-    FH_E(1, I, a) FH_F(1, I, a) FH_A(2, I, e) FH_G(1, I, a) FH_B(2, I, e) FH_C(2, I, e)        \
-    FH_D(2, I, e) FH_E(2, I, e) FH_F(2, I, e) FH_A(3, I, a) FH_G(2, I, e) FH_B(3, I, a)        \
-    FH_C(3, I, a) FH_D(3, I, a) FH_E(3, I, a) FH_F(3, I, a) FH_A(4, I, e) FH_G(3, I, a)        \
-    FH_B(4, I, e) FH_C(4, I, e) FH_D(4, I, e) FH_E(4, I, e) FH_F(4, I, e) FH_A(5, I, a)        \
-    FH_G(4, I, e) FH_B(5, I, a) FH_C(5, I, a) FH_D(5, I, a) FH_E(5, I, a) FH_F(5, I, a)        \
-    FH_A(6, I, e) FH_G(5, I, a) FH_B(6, I, e) FH_C(6, I, e) FH_D(6, I, e) FH_E(6, I, e)        \
-    FH_F(6, I, e) FH_A(7, I, a) FH_G(6, I, e) FH_B(7, I, a) FH_C(7, I, a) FH_D(7, I, a)        \
-    FH_E(7, I, a) FH_F(7, I, a) FH_A(8, I, e) FH_G(7, I, a) FH_B(8, I, e) FH_C(8, I, e)        \
-    FH_D(8, I, e) FH_E(8, I, e) FH_F(8, I, e) FH_A(9, I, a) FH_G(8, I, e) FH_B(9, I, a)        \
-    FH_C(9, I, a) FH_D(9, I, a) FH_E(9, I, a) FH_F(9, I, a) FH_A(10, I, e) FH_G(9, I, a)       \
-    FH_B(10, I, e) FH_C(10, I, e) FH_D(10, I, e) FH_E(10, I, e) FH_F(10, I, e) FH_A(11, I, a)  \
-    FH_G(10, I, e) FH_B(11, I, a) FH_C(11, I, a) FH_D(11, I, a) FH_E(11, I, a) FH_F(11, I, a)  \
-    FH_A(12, I, e) FH_G(11, I, a) FH_B(12, I, e) FH_C(12, I, e) FH_D(12, I, e) FH_E(12, I, e)  \
-    FH_F(12, I, e) FH_A(13, I, a) FH_G(12, I, e) FH_B(13, I, a) FH_C(13, I, a) FH_D(13, I, a)  \
-    FH_E(13, I, a) FH_F(13, I, a) FH_A(14, I, e) FH_G(13, I, a) FH_B(14, I, e) FH_C(14, I, e)  \
-    FH_D(14, I, e) FH_E(14, I, e) FH_F(14, I, e) FH_A(15, I, a) FH_G(14, I, e) FH_B(15, I, a)  \
-    FH_C(15, I, a) FH_D(15, I, a) FH_E(15, I, a) FH_F(15, I, a) "s_nop 0\n" FH_G(15, I, a))
 
 // The exchange of the usual case, for 2 or 3 pulses per lane, in the same
 // loop (label 5): the steps of the exchange in fps_single with the same
@@ -884,7 +817,7 @@ __device__ __forceinline__ int fps_hit_run(const float (&px)[M], const float (&p
     return code;
 }
 
-// Runs list hits only (4 to 16 pulses per lane) from slot j until a hit's
+// Runs list hits only (4 to 8 pulses per lane) from slot j until a hit's
 // list no longer decides (wm <= U) or j + 1 reaches jend; returns with j =
 // the last slot done, wm its list maximum and (s, c) the winner of that hit.
 template <int M>
@@ -908,10 +841,6 @@ __device__ __forceinline__ void fps_hit_run_h(const float (&px)[M], const float 
     int m0s;
 #define FH_IO4 FH_PULSE_IO(0), FH_PULSE_IO(1), FH_PULSE_IO(2), FH_PULSE_IO(3)
 #define FH_IN4 FH_PULSE_IN(0), FH_PULSE_IN(1), FH_PULSE_IN(2), FH_PULSE_IN(3)
-#define FH_IO8 FH_IO4, FH_PULSE_IO(4), FH_PULSE_IO(5), FH_PULSE_IO(6), FH_PULSE_IO(7)
-#define FH_IN8 FH_IN4, FH_PULSE_IN(4), FH_PULSE_IN(5), FH_PULSE_IN(6), FH_PULSE_IN(7)
-#define FH_IO12 FH_IO8, FH_PULSE_IO(8), FH_PULSE_IO(9), FH_PULSE_IO(10), FH_PULSE_IO(11)
-#define FH_IN12 FH_IN8, FH_PULSE_IN(8), FH_PULSE_IN(9), FH_PULSE_IN(10), FH_PULSE_IN(11)
     if constexpr (M == 4) {
         asm volatile(FH_LOOPH(FH_HIT4) : FH_IO4, FH_OUTSH : FH_IN4, FH_INSH : "scc");
     } else if constexpr (M == 5) {
@@ -924,31 +853,17 @@ __device__ __forceinline__ void fps_hit_run_h(const float (&px)[M], const float 
         asm volatile(FH_LOOPH(FH_HIT7)
                      : FH_IO4, FH_PULSE_IO(4), FH_PULSE_IO(5), FH_PULSE_IO(6), FH_OUTSH
                      : FH_IN4, FH_PULSE_IN(4), FH_PULSE_IN(5), FH_PULSE_IN(6), FH_INSH : "scc");
-    } else if constexpr (M == 8) {
-        asm volatile(FH_LOOPH(FH_HIT8) : FH_IO8, FH_OUTSH : FH_IN8, FH_INSH : "scc");
-    } else if constexpr (M == 10) {
-        asm volatile(FH_LOOPH(FH_HIT10) : FH_IO8, FH_PULSE_IO(8), FH_PULSE_IO(9), FH_OUTSH
-                     : FH_IN8, FH_PULSE_IN(8), FH_PULSE_IN(9), FH_INSH : "scc");
-    } else if constexpr (M == 12) {
-        asm volatile(FH_LOOPH(FH_HIT12) : FH_IO12, FH_OUTSH : FH_IN12, FH_INSH : "scc");
-    } else if constexpr (M == 14) {
-        asm volatile(FH_LOOPH(FH_HIT14) : FH_IO12, FH_PULSE_IO(12), FH_PULSE_IO(13), FH_OUTSH
-                     : FH_IN12, FH_PULSE_IN(12), FH_PULSE_IN(13), FH_INSH : "scc");
     } else {
-        static_assert(M == 16, "hand-scheduled hits only for 4 to 16 pulses per lane");
-        asm volatile(FH_LOOPH(FH_HIT16)
-                     : FH_IO12, FH_PULSE_IO(12), FH_PULSE_IO(13), FH_PULSE_IO(14),
-                       FH_PULSE_IO(15), FH_OUTSH
-                     : FH_IN12, FH_PULSE_IN(12), FH_PULSE_IN(13), FH_PULSE_IN(14),
-                       FH_PULSE_IN(15), FH_INSH
+        static_assert(M == 8, "hand-scheduled hits only for 4 to 8 pulses per lane");
+        asm volatile(FH_LOOPH(FH_HIT8)
+                     : FH_IO4, FH_PULSE_IO(4), FH_PULSE_IO(5), FH_PULSE_IO(6), FH_PULSE_IO(7),
+                       FH_OUTSH
+                     : FH_IN4, FH_PULSE_IN(4), FH_PULSE_IN(5), FH_PULSE_IN(6), FH_PULSE_IN(7),
+                       FH_INSH
                      : "scc");
     }
 #undef FH_IO4
 #undef FH_IN4
-#undef FH_IO8
-#undef FH_IN8
-#undef FH_IO12
-#undef FH_IN12
     lv = __int_as_float(lvi);
     j = jj - 1;
     wm_out = wm;
@@ -988,16 +903,15 @@ __device__ __forceinline__ void fps_hit_run_h(const float (&px)[M], const float 
 //    barrier; beyond 64 the first 64 are kept and U is raised to the
 //    largest of the others.
 // Every wave holds the same list (lane l: entry l) and takes the same
-// decisions; between exchanges the waves never synchronise.  A run of list
-// hits (the list's distances and their wave maximum, the pulses' update,
-// the first lane holding the maximum and five lane reads for the winner;
-// the centroid in scalar registers) is the hand-scheduled loop above
-// (fps_hit_run, fps_hit_run_h), which also runs the exchange's usual case
-// for 2 or 3 pulses per lane; the exchange below handles the rest.  U is
-// kept >= 0, so a maximum of 0 (every pulse selected or duplicate) always
-// goes through an exchange, where the "lowest unselected index" rule is
-// applied.  The selections of a 64-slot block go to LDS (s_sel) when a run
-// of the loop ends.
+// decisions; between exchanges the waves never synchronise.  One wave on a
+// SIMD issues a vector instruction only every few cycles, so a run of list
+// hits is kept to one short straight loop: the list's distances and their
+// wave maximum, the pulses' update, a ballot and five lane reads for the
+// winner; the centroid stays in scalar registers.  U is kept >= 0, so a
+// maximum of 0 (every pulse selected or duplicate) always goes through an
+// exchange, where the "lowest unselected index" rule is applied.  Every
+// wave writes iteration j's selection to s_sel[j] (the same value from
+// all: one LDS store, no branch).
 template <int M>
 __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64_t off, int n,
                                            int s0, SingleLds& L, int* s_sel, int* s_asg,
@@ -1068,20 +982,48 @@ __device__ __forceinline__ void fps_single(const SampleArgs& a, int64_t b, int64
                 continue;
             }
             if (code == 1) wm = INT32_MIN;  // the exchange below redoes it
-        } else {
+        } else if constexpr (M <= 8) {
             const int j0 = j;
             const int jb = j & ~63;
             int sel = 0;
             fps_hit_run_h<M>(px, py, pz, pt, md, nr, lv, lx, ly, lz, lt, li, U, min(P, jb + 64), j,
                              wm, s, cx, cy, cz, ct, sel);
             if (lane >= (j0 & 63) && lane <= (j & 63)) s_sel[jb + lane] = sel;
+        } else for (;;) {
+            s_sel[j] = s;
+            // distances are >= +0, so their bit patterns order as signed
+            // integers, and an empty entry (-1.0, negative) stays empty
+            lv = __int_as_float(min(__float_as_int(sqd(lx, ly, lz, lt, cx, cy, cz, ct)),
+                                    __float_as_int(lv)));
+            wm = wave_max_i(__float_as_int(lv));
+#pragma unroll
+            for (int k = 0; k < M; ++k) {
+                const float d = sqd(px[k], py[k], pz[k], pt[k], cx, cy, cz, ct);
+                const bool u = d < md[k];
+                nr[k] = u ? j : nr[k];
+                md[k] = u ? d : md[k];
+            }
+            // the best listed pulse (lanes hold the list in pulse order),
+            // read before the test: when the run ends here the exchange
+            // replaces it
+            const int Lw = (int)__builtin_ctzll(ballot(__float_as_int(lv) == wm));
+            s = readlane_i(li, Lw);
+            cx = readlane_f(lx, Lw);
+            cy = readlane_f(ly, Lw);
+            cz = readlane_f(lz, Lw);
+            ct = readlane_f(lt, Lw);
+            if (__builtin_expect(wm <= U, 0)) break;
+            if (__builtin_expect(j + 1 == P, 0)) break;
+            ++j;
         }
         if (j + 1 == P) break;
-        if (wm > U) {
-            // the run stopped at the end of a block of selections: the list
-            // still decides the next slot
-            ++j;
-            continue;
+        if constexpr (M <= 8) {
+            if (wm > U) {
+                // the run stopped at the end of a block of selections: the
+                // list still decides the next slot
+                ++j;
+                continue;
+            }
         }
 
         // ---- exchange

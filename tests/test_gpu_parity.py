@@ -72,7 +72,9 @@ def test_tie_rich_grids(oracle_mod, side):
 
 
 def test_identical_clouds(oracle_mod):
-    b = synth.identical_events([5, 129, 1000, 4500], 9, C=6)
+    # 400 and 700 pulses: 2 and 3 per lane, the all-zero maximum inside the
+    # hand-scheduled loop's exchange
+    b = synth.identical_events([5, 129, 400, 700, 1000, 4500], 9, C=6)
     check_pipeline(oracle_mod, b, P=128, mode=0, L=2, label="identical")
     check_pipeline(oracle_mod, b, P=128, mode=1, k=64, label="identical knn")
 
@@ -159,10 +161,11 @@ def test_candidate_list_overflow(oracle_mod, P):
     """More candidates above the bound than the lists hold: a workgroup's
     64-entry list, a shard's 63 published entries, the gang's 256 entries.
     Every lane holds one far pulse and copies of the seed (stride = pulses
-    per lane).  With P = 300 the far pulses run out and the all-zero rule
-    takes over, in single workgroups and in gangs."""
-    ns = [200, 256, 512, 1024, 2048, 4096, 8192, 20000]
-    strides = [2, 2, 2, 4, 8, 16, 16, 16]
+    per lane; 400-768 pulses: the exchange inside the hand-scheduled loop,
+    2 and 3 per lane).  With P = 300 the far pulses run out and the all-zero
+    rule takes over, in single workgroups and in gangs."""
+    ns = [200, 256, 400, 512, 700, 768, 1024, 2048, 4096, 8192, 20000]
+    strides = [2, 2, 2, 2, 3, 3, 4, 8, 16, 16, 16]
     b = synth.seed_copies_events(ns, 31 + P, C=6, strides=strides)
     check_pipeline(oracle_mod, b, P=P, mode=0, label="overflow P=%d" % P)
     _tokenize_vs_oracle(oracle_mod, b, P, label="overflow fused P=%d" % P)
